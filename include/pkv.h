@@ -1,0 +1,148 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: decode-phase paged attention and the one-token
+ * KV append, hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute is defined by these pages:
+ *   - "Decode Phase Attention Forward Pass" (sections 2-5 and the closing
+ *     padding caveat): one query token per sequence, q of shape
+ *     (batch, heads, dim), attends with no causal mask over the whole history
+ *     of its sequence, which is found by walking the sequence's list of
+ *     physical blocks; context_lens counts the history including the token
+ *     stored this step; query head h reads KV head h / (Hq / Hkv); positions
+ *     past the context length take no part in the softmax.
+ *   - "tiny-vllm part 5", section on scattering a new token's K/V into
+ *     16-token blocks: the new token's rows are written at
+ *     (slot / block_size, slot % block_size) before attention runs.
+ *   - the "Decode Phase" glossary (memory-bound decode; KV-cache quantisation
+ *     to FP8): the fp8 variant stores OCP e4m3fn codes with an fp32 scale per
+ *     (block, kv head).
+ *
+ * Conventions for every call:
+ *   - Tensors are caller-owned, contiguous, row-major device memory.  The
+ *     library keeps no pointer after a call returns and allocates nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *     No call synchronises the host with the device.
+ *   - bf16 means IEEE binary32 truncated to its upper 16 bits (stored as
+ *     uint16); e4m3fn is the OCP 8-bit format (bias 7, no infinities, max 448).
+ *   - Arguments the host can check (null pointers, unsupported shapes or
+ *     dtypes, misaligned pointers, a too-small workspace) are checked before
+ *     any launch; the call then returns a negative status and enqueues
+ *     nothing.  Device-resident data is the caller's contract and is not read
+ *     by the host: block ids must lie in [0, NB), 1 <= context_lens[b] <=
+ *     MBS * BS, slots must be unique.  The kernels clamp out-of-range ids and
+ *     lengths so that a broken contract gives wrong numbers, never an
+ *     out-of-bounds access.
+ *   - Supported: D in {64, 128}; BS in {16, 32}; Hq / Hkv in {1, 2, 4, 8}.
+ *
+ * Layouts:
+ *   q, out            [B, Hq, D]           bf16
+ *   k_cache, v_cache  [NB, BS, Hkv, D]     bf16 or e4m3fn (one token's heads
+ *                                          form one contiguous row, blocks
+ *                                          are token-major, as in the pages)
+ *   k_scale, v_scale  [NB, Hkv]            fp32 (fp8 only, else NULL)
+ *   block_tables      [B, MBS]             int32; entries past the history
+ *                                          are never read
+ *   context_lens      [B]                  int32
+ *   k_new, v_new      [N, Hkv, D]          bf16
+ *   slot_mapping      [N]                  int32; slot = block * BS + offset,
+ *                                          negative = no token
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PKV_OK 0
+#define PKV_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PKV_ERR_SHAPE (-2)       /* inconsistent or out-of-range sizes */
+#define PKV_ERR_UNSUPPORTED (-3) /* D, BS, G or dtype outside the supported set */
+#define PKV_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required */
+#define PKV_ERR_HIP (-5)         /* a HIP runtime call failed; see pkv_last_error() */
+#define PKV_ERR_ALIGN (-6)       /* a tensor pointer is not 16-byte aligned */
+
+/* KV cache element types */
+#define PKV_KV_BF16 0
+#define PKV_KV_FP8_E4M3FN 1
+
+/* Store the step's new token of each of N sequences into the paged cache
+ * ("tiny-vllm part 5", scattering into blocks; the first page's note that
+ * the K/V of the token generated this step is already in the cache when
+ * attention runs).
+ *
+ * For i < N with s = slot_mapping[i] >= 0: block = s / BS, off = s % BS, and
+ * k_cache[block, off, :, :] = k_new[i] (same for V).
+ *   bf16: an exact copy of the bits.
+ *   fp8:  for each kv head g, if off == 0 the token opens the block and sets
+ *         k_scale[block, g] = amax_d |k_new[i, g, d]| / 448 in fp32 (1.0 if
+ *         the amax is 0); otherwise the block's existing scale is kept.  Each
+ *         element is stored as e4m3fn(x / scale), x / scale a correctly
+ *         rounded fp32 division, rounded to nearest even and saturated to
+ *         +-448.  Same for V with v_scale.
+ * Slots outside [0, NB * BS) are skipped.  k_scale and v_scale must be NULL
+ * for bf16 and non-NULL for fp8.  N == 0 is a no-op. */
+int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                  void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                  int N, int Hkv, int D, int BS, int NB, int kv_dtype, void* stream);
+
+/* Bytes of device workspace pkv_paged_decode_attention needs for these
+ * sizes on the current device (it depends on the device's compute-unit
+ * count).  Returns 0 for sizes the library does not support. */
+size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                        int kv_dtype);
+
+/* Decode-phase paged attention ("Decode Phase Attention Forward Pass",
+ * sections 2-5):
+ *   out[b, h, :] = sum_{t < L_b} softmax_t(scale * <q[b, h], K_t>) * V_t,
+ *   L_b = context_lens[b], K_t = k_cache[block_tables[b][t / BS], t % BS,
+ *   h / (Hq / Hkv), :] (times k_scale of that block and head for fp8),
+ *   likewise V_t.  No causal mask; nothing past L_b is read.  A sequence with
+ *   L_b <= 0 gets out = 0.
+ * Accumulation is fp32; out is rounded to bf16 (round to nearest even).
+ * The context is split across the whole GPU (a partition kernel writes
+ * fp32 partial results into `workspace`, a merge kernel combines them by
+ * log-sum-exp); the workspace contents are scratch and need no clearing.
+ * Calls that share a workspace must not overlap in time. */
+int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                               int NB, int MBS, int kv_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* The two halves of pkv_paged_decode_attention, with the same arguments:
+ * calling partition then merge on one stream is exactly the full call.
+ * Exposed so that each kernel can be timed on its own. */
+int pkv_paged_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                               int NB, int MBS, int kv_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                           int NB, int MBS, int kv_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* pkv_status_string(int status);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Number of persistent waves the attention grid uses on the current device
+ * (0 if the device cannot be queried).  Informational. */
+int pkv_attention_waves(int D, int BS, int G, int kv_dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

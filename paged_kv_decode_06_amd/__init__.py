@@ -1,0 +1,28 @@
+"""MI355X-native decode-phase paged attention.
+
+Two operations sit behind a C-ABI shared library (``libpkv.so``, declared in
+``include/pkv.h``) built from hand-written HIP for gfx950:
+
+* ``kv_append``: store the step's new K/V token of each sequence into its slot
+  of the block-paged cache (bf16 copy, or e4m3fn quantisation with a
+  per-(block, kv head) scale);
+* ``paged_decode_attention``: one query token per sequence attends over its
+  whole paged history (GQA grouping, no causal mask, exact masking of
+  everything past ``context_lens``), split over the context with a
+  log-sum-exp merge.
+
+The Python functions in :mod:`paged_kv_decode_06_amd.ops` only marshal
+torch tensors into the C calls; every step runs in the HIP kernels.  There is
+no fallback: if the library is missing the call raises.
+"""
+from .ops import (  # noqa: F401
+    KV_BF16,
+    KV_FP8,
+    PkvError,
+    kv_append,
+    paged_decode_attention,
+    paged_decode_merge,
+    paged_decode_partition,
+    workspace_bytes,
+    library_path,
+)

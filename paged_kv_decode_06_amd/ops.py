@@ -1,0 +1,194 @@
+"""Thin ctypes binding of libpkv.so (declared in include/pkv.h).
+
+Argument marshalling only: shape/dtype checks on the torch tensors, raw
+device pointers and the current HIP stream go into the C calls, and every
+step of the computation runs in the library's kernels.  The library is
+loaded on first use; if it is missing or fails to load, the call raises --
+there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+KV_BF16 = 0
+KV_FP8 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpkv.so"
+_lib = None
+_lock = threading.Lock()
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, text: str, detail: str):
+        super().__init__(f"{fn} failed with status {status} ({text}){': ' + detail if detail else ''}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()'). "
+                "There is no fallback implementation.")
+        lib = ctypes.CDLL(path)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.pkv_kv_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.pkv_kv_append.restype = I
+        lib.pkv_paged_decode_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.pkv_paged_decode_workspace_bytes.restype = S
+        attn_args = [P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
+        for name in ("pkv_paged_decode_attention", "pkv_paged_decode_partition",
+                     "pkv_paged_decode_merge"):
+            fn = getattr(lib, name)
+            fn.argtypes = attn_args
+            fn.restype = I
+        lib.pkv_status_string.argtypes = [I]
+        lib.pkv_status_string.restype = ctypes.c_char_p
+        lib.pkv_last_error.argtypes = []
+        lib.pkv_last_error.restype = ctypes.c_char_p
+        lib.pkv_attention_waves.argtypes = [I, I, I, I]
+        lib.pkv_attention_waves.restype = I
+        _lib = lib
+    return _lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        L = _load()
+        raise PkvError(fn, status, L.pkv_status_string(status).decode(),
+                       L.pkv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _kv_dtype(k_cache: torch.Tensor) -> int:
+    if k_cache.dtype == torch.bfloat16:
+        return KV_BF16
+    if k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return KV_FP8
+    raise TypeError(f"cache dtype must be bfloat16 or uint8/float8_e4m3fn, got {k_cache.dtype}")
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+              stream=None) -> None:
+    """pkv_kv_append: store each sequence's new K/V token into its slot."""
+    kvd = _kv_dtype(k_cache)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    _need(k_cache, "k_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    if kvd == KV_FP8:
+        _need(k_scale, "k_scale", torch.float32, 2)
+        _need(v_scale, "v_scale", torch.float32, 2)
+    N, Hkv, D = k_new.shape
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v_new.shape) != (N, Hkv, D) or slot_mapping.shape[0] != N:
+        raise ValueError("k_new, v_new and slot_mapping disagree on N/Hkv/D")
+    if tuple(k_cache.shape) != (NB, BS, Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape must be [NB, BS, Hkv, D] and match k_new")
+    st = _load().pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB,
+                               kvd, _stream(stream))
+    _check("pkv_kv_append", st)
+
+
+def workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:
+    return int(_load().pkv_paged_decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype))
+
+
+def _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
+               workspace, stream):
+    kvd = _kv_dtype(k_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if kvd == KV_FP8:
+        _need(k_scale, "k_scale", torch.float32, 2)
+        _need(v_scale, "v_scale", torch.float32, 2)
+    B, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    MBS = block_tables.shape[1]
+    if D2 != D or v_cache.shape != k_cache.shape or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("q/out/cache shapes disagree")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables/context_lens must have B rows")
+    if workspace is None:
+        raise ValueError("workspace is required (see workspace_bytes)")
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    return (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+            _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
+            B, Hq, Hkv, D, BS, NB, MBS, kvd, _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(stream))
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           k_scale=None, v_scale=None, workspace=None, stream=None) -> None:
+    """pkv_paged_decode_attention: out[b, h] = softmax(scale q K^T) V over the paged history."""
+    args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
+                      v_scale, workspace, stream)
+    _check("pkv_paged_decode_attention", _load().pkv_paged_decode_attention(*args))
+
+
+def paged_decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           k_scale=None, v_scale=None, workspace=None, stream=None) -> None:
+    """First half of paged_decode_attention (the partition kernel)."""
+    args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
+                      v_scale, workspace, stream)
+    _check("pkv_paged_decode_partition", _load().pkv_paged_decode_partition(*args))
+
+
+def paged_decode_merge(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                       k_scale=None, v_scale=None, workspace=None, stream=None) -> None:
+    """Second half of paged_decode_attention (the log-sum-exp merge kernel)."""
+    args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
+                      v_scale, workspace, stream)
+    _check("pkv_paged_decode_merge", _load().pkv_paged_decode_merge(*args))
