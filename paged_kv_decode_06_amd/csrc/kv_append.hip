@@ -1,0 +1,103 @@
+// One-token KV append into the block-paged cache.
+//
+// The new token of each sequence goes to (block, offset) = (slot / BS,
+// slot % BS), as in the decode-time K/V write of "tiny-vllm part 5"
+// (section on scattering into blocks); here the caller resolves the slot and
+// one launch writes every sequence's K and V rows.  fp8: the token that
+// opens a block (offset 0) sets that block's per-head scale to amax/448.
+
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+namespace {
+
+// bf16: one workgroup per token; each lane copies 16-byte pieces of the
+// token's K row (Hkv*D values) or V row.  A bit copy, so trivially exact.
+__global__ __launch_bounds__(256) void kv_append_bf16_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int32_t* __restrict__ slots, uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    int row_vecs, int64_t num_slots) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  for (int c = threadIdx.x; c < 2 * row_vecs; c += blockDim.x) {
+    if (c < row_vecs)
+      k_cache[slot * row_vecs + c] = k_new[(int64_t)i * row_vecs + c];
+    else
+      v_cache[slot * row_vecs + (c - row_vecs)] = v_new[(int64_t)i * row_vecs + (c - row_vecs)];
+  }
+}
+
+// fp8: one wave per (token, kv head, K or V).  Lane l holds elements
+// l, l + 64, ... of the head's D values.
+template <int D>
+__global__ __launch_bounds__(64) void kv_append_fp8_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ slots, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, float* __restrict__ k_scale, float* __restrict__ v_scale,
+    int Hkv, int BS, int64_t num_slots) {
+  constexpr int PER = D / kWave;
+  const int lane = threadIdx.x;
+  const int which = blockIdx.x & 1;          // 0 = K, 1 = V
+  const int g = (blockIdx.x >> 1) % Hkv;
+  const int i = (blockIdx.x >> 1) / Hkv;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  const uint16_t* src = (which ? v_new : k_new) + ((int64_t)i * Hkv + g) * D;
+  uint8_t* dst = (which ? v_cache : k_cache) + (slot * Hkv + g) * D;
+  float* scale_slot = (which ? v_scale : k_scale) + blk * Hkv + g;
+
+  float x[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) x[k] = __uint_as_float((uint32_t)src[lane + k * kWave] << 16);
+
+  float sc;
+  if (off == 0) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) amax = fmaxf(amax, __builtin_fabsf(x[k]));
+    amax = wave_max(amax);
+    sc = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+    if (lane == 0) *scale_slot = sc;
+  } else {
+    sc = *scale_slot;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k)
+    dst[lane + k * kWave] = (uint8_t)f32_to_e4m3fn_rne_sat(__fdiv_rn(x[k], sc));
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slots,
+                            void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                            int N, int Hkv, int D, int BS, int NB, bool fp8, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  const int64_t num_slots = (int64_t)NB * BS;
+  if (!fp8) {
+    const int row_vecs = Hkv * D / 8;
+    hipLaunchKernelGGL(kv_append_bf16_kernel, dim3(N), dim3(256), 0, stream,
+                       (const uint4*)k_new, (const uint4*)v_new, slots, (uint4*)k_cache,
+                       (uint4*)v_cache, row_vecs, num_slots);
+  } else {
+    const dim3 grid((unsigned)N * Hkv * 2);
+    if (D == 128)
+      hipLaunchKernelGGL(kv_append_fp8_kernel<128>, grid, dim3(64), 0, stream,
+                         (const uint16_t*)k_new, (const uint16_t*)v_new, slots,
+                         (uint8_t*)k_cache, (uint8_t*)v_cache, k_scale, v_scale, Hkv, BS,
+                         num_slots);
+    else if (D == 64)
+      hipLaunchKernelGGL(kv_append_fp8_kernel<64>, grid, dim3(64), 0, stream,
+                         (const uint16_t*)k_new, (const uint16_t*)v_new, slots,
+                         (uint8_t*)k_cache, (uint8_t*)v_cache, k_scale, v_scale, Hkv, BS,
+                         num_slots);
+    else
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

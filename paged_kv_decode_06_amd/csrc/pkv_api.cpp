@@ -1,0 +1,272 @@
+// C ABI of libpkv.so (declared in include/pkv.h): argument checks, grid
+// sizing and dispatch.  No call allocates device memory or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device facts, queried once per (device, kernel variant, LDS size).
+struct DeviceCache {
+  std::mutex mu;
+  std::unordered_map<int, int> cu_count;                 // device -> CUs
+  std::unordered_map<unsigned long long, int> blocks;    // key -> blocks per CU
+};
+DeviceCache& cache() {
+  static DeviceCache c;
+  return c;
+}
+
+int current_device(int* dev) { return hipGetDevice(dev) == hipSuccess ? 0 : -1; }
+
+int cu_count(int dev) {
+  auto& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  auto it = c.cu_count.find(dev);
+  if (it != c.cu_count.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  c.cu_count[dev] = n;
+  return n;
+}
+
+// LDS of the partition kernel grows with B; occupancy is looked up for B
+// rounded up to a multiple of 1024 so that the cache stays small.
+int blocks_per_cu(int dev, int D, int BS, int G, bool fp8, int B) {
+  const int Bq = ((B + 1023) / 1024) * 1024;
+  const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)D << 28) |
+                                 ((unsigned long long)BS << 20) | ((unsigned long long)G << 16) |
+                                 ((unsigned long long)fp8 << 15) | (unsigned long long)(Bq / 1024);
+  auto& c = cache();
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    auto it = c.blocks.find(key);
+    if (it != c.blocks.end()) return it->second;
+  }
+  const int n = pkv::partition_blocks_per_cu(D, BS, G, fp8, pkv::partition_lds_bytes(Bq));
+  std::lock_guard<std::mutex> lk(c.mu);
+  c.blocks[key] = n;
+  return n;
+}
+
+bool supported(int D, int BS, int G, int kv_dtype) {
+  return (D == 64 || D == 128) && (BS == 16 || BS == 32) &&
+         (G == 1 || G == 2 || G == 4 || G == 8) &&
+         (kv_dtype == PKV_KV_BF16 || kv_dtype == PKV_KV_FP8_E4M3FN);
+}
+
+// Persistent grid: every workgroup that fits at once on every CU.
+int attention_blocks(int D, int BS, int G, int kv_dtype, int B) {
+  int dev;
+  if (current_device(&dev) != 0) return 0;
+  const int ncu = cu_count(dev);
+  const int per_cu = blocks_per_cu(dev, D, BS, G, kv_dtype == PKV_KV_FP8_E4M3FN, B);
+  return ncu * per_cu;
+}
+
+struct AttnCall {
+  pkv::AttnParams p;
+  int D, BS, G, blocks;
+  bool fp8;
+};
+
+int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
+                      const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
+                      int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                      size_t workspace_bytes, AttnCall* call) {
+  g_last_error.clear();
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0 || MBS <= 0)
+    return fail(PKV_ERR_SHAPE, "sizes must be positive (B may be 0): B=%d Hq=%d Hkv=%d D=%d BS=%d NB=%d MBS=%d",
+                B, Hq, Hkv, D, BS, NB, MBS);
+  if (Hq % Hkv != 0) return fail(PKV_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (!supported(D, BS, G, kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d G=%d kv_dtype=%d", D, BS, G, kv_dtype);
+  if (B > pkv::kMaxBatch) return fail(PKV_ERR_UNSUPPORTED, "B=%d exceeds %d", B, pkv::kMaxBatch);
+  if ((long long)MBS * BS > (1LL << 30))
+    return fail(PKV_ERR_SHAPE, "MBS*BS=%lld is too large", (long long)MBS * BS);
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
+  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
+  if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
+    return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
+  const int blocks = attention_blocks(D, BS, G, kv_dtype, B);
+  if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
+  const int waves = blocks * pkv::kAttnWavesPerBlock;
+  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv, G, D, waves);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace_bytes, lay.total);
+  if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+
+  pkv::AttnParams& p = call->p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = out;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.NB = NB;
+  p.MBS = MBS;
+  p.total_waves = waves;
+  char* ws = static_cast<char*>(workspace);
+  p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  p.ws_o = reinterpret_cast<float*>(ws + lay.o_off);
+  call->D = D;
+  call->BS = BS;
+  call->G = G;
+  call->fp8 = fp8;
+  call->blocks = blocks;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer";
+    case PKV_ERR_SHAPE: return "bad shape";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_attention_waves(int D, int BS, int G, int kv_dtype) {
+  if (!supported(D, BS, G, kv_dtype)) return 0;
+  return attention_blocks(D, BS, G, kv_dtype, 1) * pkv::kAttnWavesPerBlock;
+}
+
+size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                        int kv_dtype) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || MBS <= 0 || Hq % Hkv != 0) return 0;
+  const int G = Hq / Hkv;
+  if (!supported(D, BS, G, kv_dtype) || B > pkv::kMaxBatch) return 0;
+  const int blocks = attention_blocks(D, BS, G, kv_dtype, B);
+  if (blocks <= 0) return 0;
+  const int waves = blocks * pkv::kAttnWavesPerBlock;
+  return pkv::workspace_layout(B, Hkv, G, D, waves).total;
+}
+
+int pkv_paged_decode_partition(const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                               int NB, int MBS, int kv_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipError_t e = pkv::launch_partition(call.p, call.D, call.BS, call.G, call.fp8, call.blocks,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "partition kernel launch");
+}
+
+int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           void* out, int B, int Hq, int Hkv, int D, int BS, int NB, int MBS,
+                           int kv_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipError_t e = pkv::launch_merge(call.p, call.D, call.G, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+}
+
+int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                               int NB, int MBS, int kv_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_partition(call.p, call.D, call.BS, call.G, call.fp8, call.blocks, s);
+  if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  e = pkv::launch_merge(call.p, call.D, call.G, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+}
+
+int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, int N, int Hkv,
+                  int D, int BS, int NB, int kv_dtype, void* stream) {
+  g_last_error.clear();
+  if (N < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0)
+    return fail(PKV_ERR_SHAPE, "sizes must be positive (N may be 0): N=%d Hkv=%d D=%d BS=%d NB=%d",
+                N, Hkv, D, BS, NB);
+  if ((D != 64 && D != 128) || (BS != 16 && BS != 32) ||
+      (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3FN))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d kv_dtype=%d", D, BS, kv_dtype);
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
+  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
+  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
+  if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
+  if (!fp8 && (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)))
+    return fail(PKV_ERR_ALIGN, "k_new, v_new and the caches must be 16-byte aligned");
+  if (N == 0) return PKV_OK;
+  hipError_t e = pkv::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
+                                       v_scale, N, Hkv, D, BS, NB, fp8,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_append kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Device-side helpers shared by the libpkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+
+// ---- bf16 -------------------------------------------------------------------
+
+// A 32-bit word holds two bf16 values; bf16 is the top half of a binary32, so
+// widening is a shift or a mask.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// ---- OCP e4m3fn -------------------------------------------------------------
+
+// Eight e4m3fn bytes -> eight floats with the gfx950 converter, which reads
+// the OCP encoding (exact: every e4m3fn value is a binary32 value).
+__device__ __forceinline__ void unpack8(const uint2 v, float (&f)[8]) {
+  auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false);
+  auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+  auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false);
+  auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+  f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+  f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+}
+
+// binary32 -> e4m3fn, round to nearest (ties to even), saturating at +-448.
+// Bit-level: below 2^-6 the format is fixed point with step 2^-9, so the
+// code is rint(|y| * 2^9) (8 lands exactly on the smallest normal, 0x08);
+// above, the binary32 significand is rounded to 3 bits at bit 20 and the
+// exponent is re-biased from 127 to 7 (a carry out of the significand bumps
+// the exponent, which the addition does by itself).  The sign bit is
+// copied, so negative values that round to zero give 0x80.  NaN gives 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn_rne_sat(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(y);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                              // 2^-6
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7ffffu + ((ua >> 20) & 1u);
+  const uint32_t exp8 = (ua >> 23) - 127u + 7u;     // 1..15
+  const uint32_t man3 = (ua >> 20) & 7u;
+  return sign | (exp8 << 3) | man3;
+}
+
+// ---- cross-lane reductions (DPP within a 16-lane row) -----------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N in 1, 2, 4, 8, 16); every lane of the
+// group gets the group's total.  After the two quad steps each quad holds its
+// sum; the half-row mirror pairs quad 0 with quad 1 (lane i with 7 - i) and
+// the row mirror pairs the two halves (lane i with 15 - i).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group size");
+  if constexpr (N >= 2) x += dpp_mov<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp_mov<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_mov<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_mov<kDppRowMirror>(x));
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

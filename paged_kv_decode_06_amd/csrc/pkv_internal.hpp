@@ -1,0 +1,66 @@
+// Host-side interface between the C ABI (pkv_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Arguments of the attention kernels.  Pointers are device pointers.
+struct AttnParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float scale_log2;     // softmax scale * log2(e): scores live in the exp2 domain
+  int B, Hq, Hkv, NB, MBS;
+  int total_waves;      // persistent waves of the partition grid
+  // workspace (see workspace_layout)
+  int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
+  float* ws_ml;         // [rows, G, 2] running max (log2 domain) and sum
+  float* ws_o;          // [rows, G, D] unnormalised partial outputs
+};
+
+struct WorkspaceLayout {
+  size_t pre_off, ml_off, o_off, total;
+  int rows;
+};
+
+// rows = total_waves + B * Hkv: each (wave, (sequence, kv head)) pair that
+// shares work gets row wave + segment, a unique index (both grow together
+// along the work axis).
+inline WorkspaceLayout workspace_layout(int B, int Hkv, int G, int D, int total_waves) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  WorkspaceLayout w;
+  w.rows = total_waves + B * Hkv;
+  w.pre_off = 0;
+  w.ml_off = up(sizeof(int32_t) * (size_t)(B + 1));
+  w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * G);
+  w.total = w.o_off + up(sizeof(float) * (size_t)w.rows * G * D);
+  return w;
+}
+
+constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
+constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
+constexpr int kMaxBatch = 8192;          // sequence prefix sums live in LDS
+
+// Partition kernel (VALU).  Returns hipErrorInvalidValue for an unsupported
+// (D, BS, G, fp8) combination.
+hipError_t launch_partition(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+                            hipStream_t stream);
+// Workgroups of the partition kernel that fit on one compute unit (0 if unsupported).
+int partition_blocks_per_cu(int D, int BS, int G, bool fp8, size_t lds_bytes);
+size_t partition_lds_bytes(int B);
+
+hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slots,
+                            void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                            int N, int Hkv, int D, int BS, int NB, bool fp8, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,110 @@
+"""Helpers for the GPU parity tests: run a decode step through the C ABI and
+the same step through the oracle, on the same seeded inputs.
+
+The oracle only ever sees generator output (the pre-append cache, q and the
+new token), never anything the HIP path produced.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_decode_06_amd import ops
+from paged_kv_decode_06_amd import workloads as W
+
+BF16_ATOL = 4e-3
+BF16_RTOL = 8e-3
+FP8_ATOL = 3e-2
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def workspace_for(wl: W.Workload) -> torch.Tensor:
+    kvd = ops.KV_FP8 if wl.kv_dtype == "fp8" else ops.KV_BF16
+    n = ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd)
+    assert n > 0
+    return torch.empty(n, dtype=torch.uint8, device=wl.q.device)
+
+
+def gpu_step(wl: W.Workload, out=None, workspace=None, append=True) -> torch.Tensor:
+    """kv_append of this step's token, then attention; returns out (bf16)."""
+    if append:
+        ops.kv_append(wl.k_new, wl.v_new, wl.slot_mapping, wl.k_cache, wl.v_cache,
+                      wl.k_scale, wl.v_scale)
+    if out is None:
+        out = torch.empty_like(wl.q)
+    if workspace is None:
+        workspace = workspace_for(wl)
+    ops.paged_decode_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens,
+                               wl.scale, out, wl.k_scale, wl.v_scale, workspace)
+    return out
+
+
+class HostProblem:
+    """Host (numpy) copy of a workload, or of a subset of its sequences with
+    their pages renumbered into a compact pool, taken before the GPU runs."""
+
+    def __init__(self, wl: W.Workload, seqs=None):
+        BS = wl.BS
+        seqs = list(range(wl.B)) if seqs is None else list(seqs)
+        self.seqs = seqs
+        pages = [wl.block_tables_np[b, : (int(wl.lengths[b]) + BS - 1) // BS] for b in seqs]
+        old = np.concatenate(pages).astype(np.int64)
+        self.old_blocks = old
+        remap = {int(p): i for i, p in enumerate(old)}
+        idx = torch.from_numpy(old).to(wl.k_cache.device)
+        self.k = W.cache_host(wl.k_cache.index_select(0, idx)).copy()
+        self.v = W.cache_host(wl.v_cache.index_select(0, idx)).copy()
+        if wl.k_scale is not None:
+            self.ks = wl.k_scale.index_select(0, idx).cpu().numpy().copy()
+            self.vs = wl.v_scale.index_select(0, idx).cpu().numpy().copy()
+        else:
+            self.ks = self.vs = None
+        mbs = max(len(p) for p in pages)
+        self.bt = np.full((len(seqs), mbs), -1, np.int32)
+        for i, p in enumerate(pages):
+            self.bt[i, : len(p)] = [remap[int(x)] for x in p]
+        self.cl = wl.lengths[seqs].astype(np.int32)
+        sel = torch.tensor(seqs, device=wl.q.device)
+        self.q = W.bf16_bits(wl.q.index_select(0, sel))
+        self.k_new = W.bf16_bits(wl.k_new.index_select(0, sel))
+        self.v_new = W.bf16_bits(wl.v_new.index_select(0, sel))
+        slots = []
+        for i, b in enumerate(seqs):
+            blk, off = divmod(int(wl.slot_mapping_np[b]), BS)
+            slots.append(remap[blk] * BS + off)
+        self.slots = np.array(slots, np.int32)
+        self.scale = wl.scale
+        self.BS = BS
+
+    def append(self):
+        oracle.kv_append(self.k_new, self.v_new, self.slots, self.k, self.v, self.ks, self.vs)
+
+    def attention(self, nthreads=0):
+        return oracle.paged_decode_attention(self.q, self.k, self.v, self.bt, self.cl, self.scale,
+                                             k_scale=self.ks, v_scale=self.vs,
+                                             nthreads=nthreads)
+
+
+def error_report(gpu: np.ndarray, ref: np.ndarray) -> dict:
+    err = np.abs(gpu - ref)
+    return dict(max_abs=float(err.max()), rms=float(np.sqrt((err ** 2).mean())),
+                max_rel=float((err / np.maximum(np.abs(ref), 1e-30)).max()))
+
+
+def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""):
+    assert gpu.shape == ref.shape
+    assert np.isfinite(gpu).all(), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    if kv_dtype == "fp8":
+        bad = err > FP8_ATOL
+    else:
+        bad = err > BF16_ATOL + BF16_RTOL * np.abs(ref)
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(
+            f"{what}: {bad.sum()} elements out of tolerance, first at {tuple(i)}: "
+            f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}; {error_report(gpu, ref)}")

@@ -1,0 +1,96 @@
+"""The C ABI library loads and exports every symbol include/pkv.h declares,
+and rejects bad host-side arguments before touching a GPU (CPU only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_decode_06_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.library_path()):
+        pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
+    return ops.lib()
+
+
+def test_header_declares_the_two_calls():
+    names = declared_functions()
+    assert "pkv_paged_decode_attention" in names and "pkv_kv_append" in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st, text in [(0, "ok"), (-1, "null pointer"), (-4, "workspace too small")]:
+        assert lib.pkv_status_string(st).decode() == text
+
+
+NULL = None
+
+
+def attn(lib, **over):
+    args = dict(q=8, k=16, v=32, ks=NULL, vs=NULL, bt=48, cl=64, scale=0.125, out=80,
+                B=2, Hq=8, Hkv=2, D=64, BS=16, NB=4, MBS=2, kv=0, ws=96, wsb=1 << 20, stream=NULL)
+    args.update(over)
+    P = ctypes.c_void_p
+    a = args
+    return lib.pkv_paged_decode_attention(
+        P(a["q"]) if a["q"] else None, P(a["k"]) if a["k"] else None,
+        P(a["v"]) if a["v"] else None, P(a["ks"]) if a["ks"] else None,
+        P(a["vs"]) if a["vs"] else None, P(a["bt"]) if a["bt"] else None,
+        P(a["cl"]) if a["cl"] else None, ctypes.c_float(a["scale"]),
+        P(a["out"]) if a["out"] else None, a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+        a["NB"], a["MBS"], a["kv"], P(a["ws"]) if a["ws"] else None,
+        ctypes.c_size_t(a["wsb"]), None)
+
+
+def test_attention_argument_checks_fail_before_launch(lib):
+    # these are checked before any HIP call, so they work without a GPU
+    assert attn(lib, q=0) == -1
+    assert attn(lib, out=0) == -1
+    assert attn(lib, Hq=6, Hkv=4) == -2            # Hq % Hkv != 0
+    assert attn(lib, D=96) == -3                   # unsupported head dim
+    assert attn(lib, BS=8) == -3                   # unsupported block size
+    assert attn(lib, Hq=32, Hkv=2) == -3           # G = 16
+    assert attn(lib, kv=7) == -3
+    assert attn(lib, kv=1) == -1                   # fp8 without scales
+    assert attn(lib, ks=128, vs=144) == -2         # bf16 with scales
+    assert attn(lib, B=-1) == -2
+    assert attn(lib, B=100000) == -3
+    assert attn(lib, q=9) == -6                    # misaligned
+    assert "Hq" in lib.pkv_last_error().decode() or lib.pkv_last_error().decode()
+
+
+def test_kv_append_argument_checks(lib):
+    P = ctypes.c_void_p
+    f = lib.pkv_kv_append
+    ok = [P(16), P(32), P(48), P(64), P(80), None, None, 2, 2, 64, 16, 4, 0, None]
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == -1
+    bad = list(ok); bad[9] = 80
+    assert f(*bad) == -3
+    bad = list(ok); bad[12] = 1                     # fp8 without scales
+    assert f(*bad) == -1
+    bad = list(ok); bad[7] = -1
+    assert f(*bad) == -2
+    bad = list(ok); bad[0] = P(17)
+    assert f(*bad) == -6
+    zero = list(ok); zero[7] = 0                    # N = 0: nothing to do
+    assert f(*zero) == 0
