@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step = kv_append of the step's token + paged decode
+attention (partition + merge kernels), on one MI355X.
+
+Default workload: the Llama-3-8B-shaped layer (B=64, Hq=32, Hkv=8, D=128,
+block 16, context lengths uniform in [512, 4096], bf16 KV).  Prints ONE JSON
+line.  `value` is KV bytes read per step (sum over sequences of
+L * 2 * Hkv * D * bytes per element) divided by the measured step time.
+
+Inputs are resident in HBM before timing starts.  R copies of the KV cache
+(same contents, different addresses) are cycled so that no step finds the
+previous step's pages in the 256 MB memory-side cache.  The partition
+kernel's own duration is taken with HIP events recorded on the stream it is
+launched on, and gives the roofline entry; the oracle timed on the host
+cores gives the CPU baseline.
+
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+
+def kv_bytes(wl) -> int:
+    elem = 1 if wl.kv_dtype == "fp8" else 2
+    tot = int(wl.lengths.sum()) * 2 * wl.Hkv * wl.D * elem
+    if wl.kv_dtype == "fp8":
+        pages = ((wl.lengths + wl.BS - 1) // wl.BS).sum()
+        tot += int(pages) * wl.Hkv * 2 * 4
+    return tot
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle, as it stands, on the host cores: one full decode step's
+    attention over the same batch (after the oracle's own append), repeated
+    until about `budget_s` of wall time has passed."""
+    import numpy as np
+    import oracle
+    from paged_kv_decode_06_amd import workloads as W
+
+    k = W.cache_host(wl.k_cache).copy()
+    v = W.cache_host(wl.v_cache).copy()
+    ks = None if wl.k_scale is None else wl.k_scale.cpu().numpy().copy()
+    vs = None if wl.v_scale is None else wl.v_scale.cpu().numpy().copy()
+    oracle.kv_append(W.bf16_bits(wl.k_new), W.bf16_bits(wl.v_new), wl.slot_mapping_np, k, v, ks, vs)
+    q = W.bf16_bits(wl.q)
+    cl = wl.lengths.astype(np.int32)
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = min(threads, int(os.environ.get("OMP_NUM_THREADS", threads) or threads))
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.paged_decode_attention(q, k, v, wl.block_tables_np, cl, wl.scale, k_scale=ks,
+                                      v_scale=vs, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all > budget_s or len(times) >= 5:
+            break
+    t = sum(times) / len(times)
+    return {"value": round(kv_bytes(wl) / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full {wl.name} batch (B={wl.B}), fp64 attention of one step, "
+                      f"{len(times)} run(s), mean {t:.3f} s per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="llama3_8b")
+    ap.add_argument("--copies", type=int, default=0, help="KV cache copies cycled (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma",
+                    help="partition-kernel variant")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_decode_06_amd import ops
+    from paged_kv_decode_06_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ops.select_partition_kernel(ops.PARTITION_MFMA if args.kernel == "mfma" else ops.PARTITION_VALU)
+    cfg = W.CONFIGS[args.config]
+    wl = W.make_config_workload(args.config, device=dev, poison=False)
+    nbytes = kv_bytes(wl)
+    pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
+    copies = args.copies or max(2, int(np.ceil(2.0e9 / pool_bytes)))
+
+    stream = torch.cuda.Stream(device=dev)
+    kvd = ops.KV_FP8 if wl.kv_dtype == "fp8" else ops.KV_BF16
+    ws = torch.empty(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(wl.q)
+    caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
+    for _ in range(copies - 1):
+        caches.append(tuple(None if t is None else t.clone() for t in caches[0]))
+    steps = []
+    for kc, vc, ks, vs in caches:
+        app = ops.PreparedAppend(wl.k_new, wl.v_new, wl.slot_mapping, kc, vc, ks, vs, stream=stream)
+        att = ops.PreparedAttention(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, out,
+                                    ks, vs, ws, stream=stream)
+        steps.append((app, att))
+    torch.cuda.synchronize()
+
+    K, Wm = args.steps, args.warmup
+    with torch.cuda.stream(stream):
+        for i in range(Wm):
+            app, att = steps[i % copies]
+            app()
+            att()
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            app, att = steps[(Wm + i) % copies]
+            app()
+            ev0[i].record(stream)
+            att.partition()
+            ev1[i].record(stream)
+            att.merge()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    part_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+    part_avg_ms = float(np.mean(part_ms))
+
+    # breakdown of one step, each kernel between its own pair of events
+    nb = min(K, 50)
+    e = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    with torch.cuda.stream(stream):
+        for i in range(nb):
+            app, att = steps[i % copies]
+            e[i][0].record(stream)
+            app()
+            e[i][1].record(stream)
+            att.partition()
+            e[i][2].record(stream)
+            att.merge()
+            e[i][3].record(stream)
+    torch.cuda.synchronize()
+    app_us = float(np.median([x[0].elapsed_time(x[1]) for x in e])) * 1e3
+    part_med_us = float(np.median([x[1].elapsed_time(x[2]) for x in e])) * 1e3
+    merge_us = float(np.median([x[2].elapsed_time(x[3]) for x in e])) * 1e3
+
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (part_avg_ms * 1e-3) / 1e9
+    waves = ops.lib().pkv_attention_waves(wl.D, wl.BS, wl.G, kvd)
+    result = {
+        "metric": "KV-read GB/s per decode-attention step (1 MI355X)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "kv_dtype": wl.kv_dtype,
+            "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.BS,
+            "sum_context": int(wl.lengths.sum()), "num_blocks": wl.NB,
+            "kv_bytes_per_step": nbytes, "kv_cache_copies_cycled": copies,
+            "step": "kv_append + partition + merge",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{args.kernel}_partition_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "detail": {
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+            "partition_us_mean": round(part_avg_ms * 1e3, 2),
+            "partition_us_median": round(part_med_us, 2),
+            "merge_us_median": round(merge_us, 2),
+            "kv_append_us_median": round(app_us, 2),
+            "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
+            "persistent_waves": waves,
+        },
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

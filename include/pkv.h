@@ -141,6 +141,18 @@ const char* pkv_last_error(void);
  * (0 if the device cannot be queried).  Informational. */
 int pkv_attention_waves(int D, int BS, int G, int kv_dtype);
 
+/* Partition-kernel variants.  Both compute the same attention; MFMA (the
+ * default) puts the GQA group on the matrix cores, VALU uses fp32 vector
+ * FMAs.  The choice is process-wide and is read at the start of every
+ * attention call, workspace query included, so switch only between calls
+ * (never while another thread is inside one) and size the workspace after
+ * switching.  The environment variable PKV_ATTN_KERNEL=valu selects VALU
+ * when the library loads.  Returns PKV_ERR_UNSUPPORTED for another value. */
+#define PKV_PARTITION_VALU 0
+#define PKV_PARTITION_MFMA 1
+int pkv_select_partition_kernel(int variant);
+int pkv_partition_kernel(void);
+
 #ifdef __cplusplus
 }
 #endif

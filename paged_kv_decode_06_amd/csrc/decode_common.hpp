@@ -1,0 +1,116 @@
+// Pieces shared by the partition kernels (VALU and MFMA variants).
+//
+// Semantics ("Decode Phase Attention Forward Pass", sections 2-5): one query
+// token per sequence attends, with no causal mask, over positions
+// t < context_lens[b] of its history; position t lives at
+// (block_tables[b][t / BS], t % BS); query head h reads kv head h / G.
+// The pages' route gathers the history into a zero-padded dense tensor and
+// calls a dense kernel; here nothing is gathered: each wave reads the pages
+// in place through the block table, and positions past the context length
+// are selected away (never weighted by zero, so stale or NaN bytes in a
+// block's tail cannot leak in).
+//
+// Work split (flash-decoding style split of the context).  The work axis is
+// every (sequence b, kv head g, page j) triple in that order: position
+// Hkv*pre[b] + g*n_b + j, where n_b = ceil(L_b / BS) and pre is the prefix
+// sum of n_b.  A persistent grid of W waves cuts this axis into equal pieces
+// of Q = ceil(Hkv*pre[B] / W) pages, so every wave streams the same number of
+// KV bytes whatever the length mix.  A (b, g) run that one wave covers
+// completely is finished in place (out written as bf16); otherwise each wave
+// that touches it leaves (m, l, o) for its share in workspace row
+// wave + segment (segment = b*Hkv + g), and the merge kernel combines the
+// rows of a segment, which are consecutive.  m is kept in the exp2 domain
+// (scores times scale*log2(e)).
+#pragma once
+
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+// Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]).
+// Called by every thread of the workgroup.
+__device__ inline void build_prefix(const int32_t* __restrict__ context_lens, int B, int BS,
+                                    int MBS, int32_t* s_pre, int32_t* s_tmp) {
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int per = (B + nt - 1) / nt;
+  const int b0 = tid * per;
+  const int b1 = min(B, b0 + per);
+  const int max_len = MBS * BS;
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int L = min(max(context_lens[b], 0), max_len);
+    sum += (L + BS - 1) / BS;
+  }
+  s_tmp[tid] = sum;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the per-thread sums
+  for (int off = 1; off < nt; off <<= 1) {
+    const int v = tid >= off ? s_tmp[tid - off] : 0;
+    __syncthreads();
+    s_tmp[tid] += v;
+    __syncthreads();
+  }
+  int run = tid == 0 ? 0 : s_tmp[tid - 1];
+  for (int b = b0; b < b1; ++b) {
+    s_pre[b] = run;
+    const int L = min(max(context_lens[b], 0), max_len);
+    run += (L + BS - 1) / BS;
+  }
+  if (tid == nt - 1) s_pre[B] = s_tmp[nt - 1];
+  __syncthreads();
+}
+
+// Last b in [0, B) with Hkv * pre[b] <= x (x < Hkv * pre[B]).
+__device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int Hkv, int x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (Hkv * s_pre[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// One wave's share of a (sequence, kv head) run: pages [j0, j1) of run
+// (b, g), whose first page sits at `run_start` on the work axis.
+struct Piece {
+  int b, g, n_b, run_start, j0, j1;
+};
+
+__device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int Hkv, int x,
+                                              int x_end) {
+  Piece pc;
+  pc.b = find_sequence(s_pre, B, Hkv, x);
+  pc.n_b = s_pre[pc.b + 1] - s_pre[pc.b];
+  const int seg_start = Hkv * s_pre[pc.b];
+  pc.g = (x - seg_start) / pc.n_b;
+  pc.run_start = seg_start + pc.g * pc.n_b;
+  pc.j0 = x - pc.run_start;
+  pc.j1 = min(pc.n_b, x_end - pc.run_start);
+  return pc;
+}
+
+// Calls f(Sh<D, BS, G, fp8>{}) for the supported combination given at run
+// time; false if it is not supported.
+template <template <int, int, int, bool> class Sh, class F>
+bool dispatch_shapes(int D, int BS, int G, bool fp8, F&& f) {
+#define PKV_CASE(d, bs, gg, f8)                     \
+  if (D == d && BS == bs && G == gg && fp8 == f8) { \
+    f(Sh<d, bs, gg, f8>{});                         \
+    return true;                                    \
+  }
+#define PKV_G(d, bs, f8) \
+  PKV_CASE(d, bs, 1, f8) PKV_CASE(d, bs, 2, f8) PKV_CASE(d, bs, 4, f8) PKV_CASE(d, bs, 8, f8)
+#define PKV_BS(d, f8) PKV_G(d, 16, f8) PKV_G(d, 32, f8)
+  PKV_BS(64, false) PKV_BS(128, false) PKV_BS(64, true) PKV_BS(128, true)
+#undef PKV_BS
+#undef PKV_G
+#undef PKV_CASE
+  return false;
+}
+
+}  // namespace pkv

@@ -1,46 +1,25 @@
-// Decode-phase paged attention: partition kernel + log-sum-exp merge kernel.
+// Partition kernel, VALU variant.
 //
-// Semantics ("Decode Phase Attention Forward Pass", sections 2-5): one query
-// token per sequence attends, with no causal mask, over positions
-// t < context_lens[b] of its history; position t lives at
-// (block_tables[b][t / BS], t % BS); query head h reads kv head h / G.
-// The pages' route gathers the history into a zero-padded dense tensor and
-// calls a dense kernel; here nothing is gathered: each wave reads the pages
-// in place through the block table and positions past the context length
-// are selected away (never weighted by zero, so stale or NaN bytes in a
-// block's tail cannot leak in).
-//
-// Work decomposition (flash-decoding style split of the context).  The work
-// axis is every (sequence b, kv head g, page j) triple in that order:
-// position Hkv*pre[b] + g*n_b + j, where n_b = ceil(L_b / BS) and pre is the
-// prefix sum of n_b.  A persistent grid of W waves cuts this axis into equal
-// pieces of Q = ceil(Hkv*pre[B] / W) pages, so every wave streams the same
-// number of KV bytes whatever the length mix.  A (b, g) run that one wave
-// covers completely is finished in place (out written as bf16); otherwise
-// each wave that touches it leaves (m, l, o) for its share in workspace row
-// wave + segment, and the merge kernel combines the rows of a segment,
-// which are consecutive.
-//
-// Inside a wave (VALU path): lanes are laid out as TPW token rows of LPT
-// lanes; a lane holds 8 consecutive head-dim elements of one token (one
-// 16-byte load for bf16, 8 bytes for fp8).  q for the G heads of the group
-// sits in registers, so each K/V byte is loaded once for the whole GQA group.
-// Per page: partial dot products, a DPP reduction over the LPT lanes of a
-// row, online softmax per row in the exp2 domain, PV accumulation.  The TPW
-// rows are merged with cross-lane shuffles at the end of a piece.
+// Inside a wave, lanes are laid out as TPW token rows of LPT lanes; a lane
+// holds 8 consecutive head-dim elements of one token (one 16-byte load for
+// bf16, 8 bytes for fp8).  q for the G heads of the group sits in registers
+// as fp32, so each K/V byte is loaded once for the whole GQA group.  Per
+// page: partial dot products, a DPP reduction over the LPT lanes of a row,
+// online softmax per row in the exp2 domain, PV accumulation with fp32 FMAs.
+// The TPW rows are merged with cross-lane shuffles at the end of a piece.
+// The work split over waves is described in decode_common.hpp.
 
 #include <float.h>
 
 #include <type_traits>
 
-#include "pkv_device.hpp"
-#include "pkv_internal.hpp"
+#include "decode_common.hpp"
 
 namespace pkv {
 namespace {
 
 template <int D_, int BS_, int G_, bool FP8_>
-struct Shape {
+struct ValuShape {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr int G = G_;
@@ -54,59 +33,13 @@ struct Shape {
   static_assert(LPP >= 1 && BS % TPW == 0, "page must hold whole token rows");
 };
 
-// Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]).
-__device__ void build_prefix(const int32_t* __restrict__ context_lens, int B, int BS, int MBS,
-                             int32_t* s_pre, int32_t* s_tmp) {
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
-  const int per = (B + nt - 1) / nt;
-  const int b0 = tid * per;
-  const int b1 = min(B, b0 + per);
-  const int max_len = MBS * BS;
-  int sum = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int L = min(max(context_lens[b], 0), max_len);
-    sum += (L + BS - 1) / BS;
-  }
-  s_tmp[tid] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums
-  for (int off = 1; off < nt; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
-  }
-  int run = tid == 0 ? 0 : s_tmp[tid - 1];
-  for (int b = b0; b < b1; ++b) {
-    s_pre[b] = run;
-    const int L = min(max(context_lens[b], 0), max_len);
-    run += (L + BS - 1) / BS;
-  }
-  if (tid == nt - 1) s_pre[B] = s_tmp[nt - 1];
-  __syncthreads();
-}
-
-// Last b in [0, B) with Hkv * pre[b] <= x (x < Hkv * pre[B]).
-__device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int Hkv, int x) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (Hkv * s_pre[mid] <= x)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 template <class S>
 __device__ __forceinline__ typename S::Vec load_row(const uint8_t* __restrict__ base) {
   return *reinterpret_cast<const typename S::Vec*>(base);
 }
 
 template <class S>
-__global__ __launch_bounds__(kAttnBlockThreads) void partition_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const AttnParams p) {
   constexpr int D = S::D, BS = S::BS, G = S::G, LPT = S::LPT, TPW = S::TPW, LPP = S::LPP;
   constexpr int EB = S::EB;
   using Vec = typename S::Vec;
@@ -315,130 +248,28 @@ __global__ __launch_bounds__(kAttnBlockThreads) void partition_kernel(const Attn
   }
 }
 
-// Merge: one wave per (sequence, query head).  The rows of a (b, g) run are
-// wave + segment for the consecutive waves w0..w1 whose pieces cover it.
-template <int D>
-__global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnParams p, int G) {
-  constexpr int PER = D / kWave;               // head-dim elements per lane
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t bh = (int64_t)blockIdx.x * (kAttnBlockThreads / kWave) + (threadIdx.x >> 6);
-  if (bh >= (int64_t)p.B * p.Hq) return;
-  const int b = (int)(bh / p.Hq);
-  const int h = (int)(bh % p.Hq);
-  const int g = h / G;
-  const int jj = h % G;
-  const int Hkv = p.Hkv;
-  const int total = Hkv * p.ws_pre[p.B];
-  const int n_b = p.ws_pre[b + 1] - p.ws_pre[b];
-  uint16_t* op = static_cast<uint16_t*>(p.out) + bh * D;
-  if (n_b == 0) {                              // empty history: defined as 0
-#pragma unroll
-    for (int k = 0; k < PER; ++k) op[lane * PER + k] = 0;
-    return;
-  }
-  const int W = p.total_waves;
-  const int Q = (total + W - 1) / W;
-  const int start = Hkv * p.ws_pre[b] + g * n_b;
-  const int w0 = start / Q;
-  const int w1 = (start + n_b - 1) / Q;
-  if (w0 == w1) return;                        // finished by the partition kernel
-  const int seg = b * Hkv + g;
-  const int P = w1 - w0 + 1;
-  const int64_t row0 = (int64_t)w0 + seg;
-
-  float M = -FLT_MAX;
-  for (int i = lane; i < P; i += kWave) M = fmaxf(M, p.ws_ml[((row0 + i) * G + jj) * 2]);
-  M = wave_max(M);
-
-  float num[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) num[k] = 0.0f;
-  float den = 0.0f;
-  for (int i0 = 0; i0 < P; i0 += kWave) {
-    const int n = min(kWave, P - i0);
-    float wgt = 0.0f;
-    if (lane < n) {
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + ((row0 + i0 + lane) * G + jj) * 2);
-      wgt = fast_exp2(ml.x - M);
-      den += wgt * ml.y;
-    }
-    for (int i = 0; i < n; ++i) {
-      const float wi = __shfl(wgt, i);
-      const float* src = p.ws_o + ((row0 + i0 + i) * G + jj) * D + lane * PER;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) num[k] = fmaf(wi, src[k], num[k]);
-    }
-  }
-  den = wave_sum(den);
-  const float inv = 1.0f / den;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(op + lane * 2) = pack_bf16x2(num[0] * inv, num[1] * inv);
-  } else {
-    op[lane] = (uint16_t)f32_to_bf16_rne(num[0] * inv);
-  }
-}
-
-template <class S>
-void* partition_fn() {
-  return reinterpret_cast<void*>(&partition_kernel<S>);
-}
-
-// Dispatch over the supported (D, BS, G, fp8) set.
-template <class F>
-bool dispatch(int D, int BS, int G, bool fp8, F&& f) {
-#define PKV_CASE(d, bs, gg, f8)                                    \
-  if (D == d && BS == bs && G == gg && fp8 == f8) {                \
-    f(Shape<d, bs, gg, f8>{});                                     \
-    return true;                                                   \
-  }
-#define PKV_G(d, bs, f8) PKV_CASE(d, bs, 1, f8) PKV_CASE(d, bs, 2, f8) PKV_CASE(d, bs, 4, f8) PKV_CASE(d, bs, 8, f8)
-#define PKV_BS(d, f8) PKV_G(d, 16, f8) PKV_G(d, 32, f8)
-  PKV_BS(64, false) PKV_BS(128, false) PKV_BS(64, true) PKV_BS(128, true)
-#undef PKV_BS
-#undef PKV_G
-#undef PKV_CASE
-  return false;
-}
-
 }  // namespace
 
-size_t partition_lds_bytes(int B) {
-  return sizeof(int32_t) * ((size_t)B + 1 + kAttnBlockThreads);
-}
-
-int partition_blocks_per_cu(int D, int BS, int G, bool fp8, size_t lds_bytes) {
+int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
   int blocks = 0;
-  const bool ok = dispatch(D, BS, G, fp8, [&](auto s) {
+  const size_t lds_bytes = prefix_lds_bytes(B);
+  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, fp8, [&](auto s) {
     using S = decltype(s);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, partition_kernel<S>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, valu_partition_kernel<S>,
                                                      kAttnBlockThreads, lds_bytes) != hipSuccess)
       blocks = 0;
   });
   return ok ? blocks : 0;
 }
 
-hipError_t launch_partition(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
-                            hipStream_t stream) {
-  const size_t lds = partition_lds_bytes(p.B);
-  const bool ok = dispatch(D, BS, G, fp8, [&](auto s) {
+hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+                                 hipStream_t stream) {
+  const size_t lds = prefix_lds_bytes(p.B);
+  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, fp8, [&](auto s) {
     using S = decltype(s);
-    hipLaunchKernelGGL(partition_kernel<S>, dim3(blocks), dim3(kAttnBlockThreads), lds, stream, p);
+    hipLaunchKernelGGL(valu_partition_kernel<S>, dim3(blocks), dim3(kAttnBlockThreads), lds, stream, p);
   });
   if (!ok) return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.Hq;
-  const int waves_per_block = kAttnBlockThreads / kWave;
-  const dim3 grid((unsigned)((rows + waves_per_block - 1) / waves_per_block));
-  if (rows == 0) return hipSuccess;
-  if (D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kAttnBlockThreads), 0, stream, p, G);
-  else if (D == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kAttnBlockThreads), 0, stream, p, G);
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

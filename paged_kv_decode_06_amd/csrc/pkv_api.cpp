@@ -3,9 +3,11 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 #include <unordered_map>
@@ -61,16 +63,19 @@ int cu_count(int dev) {
 // rounded up to a multiple of 1024 so that the cache stays small.
 int blocks_per_cu(int dev, int D, int BS, int G, bool fp8, int B) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)D << 28) |
-                                 ((unsigned long long)BS << 20) | ((unsigned long long)G << 16) |
-                                 ((unsigned long long)fp8 << 15) | (unsigned long long)(Bq / 1024);
+  const pkv::AttnPath path = pkv::attn_path();
+  const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)path << 36) |
+                                 ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
+                                 ((unsigned long long)G << 16) | ((unsigned long long)fp8 << 15) |
+                                 (unsigned long long)(Bq / 1024);
   auto& c = cache();
   {
     std::lock_guard<std::mutex> lk(c.mu);
     auto it = c.blocks.find(key);
     if (it != c.blocks.end()) return it->second;
   }
-  const int n = pkv::partition_blocks_per_cu(D, BS, G, fp8, pkv::partition_lds_bytes(Bq));
+  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, fp8, Bq)
+                                             : pkv::valu_blocks_per_cu(D, BS, G, fp8, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
   return n;
@@ -159,7 +164,24 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   return PKV_OK;
 }
 
+hipError_t launch_partition(const AttnCall& c, hipStream_t s) {
+  return pkv::attn_path() == pkv::AttnPath::kMfma
+             ? pkv::launch_partition_mfma(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s)
+             : pkv::launch_partition_valu(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s);
+}
+
 }  // namespace
+
+namespace pkv {
+std::atomic<int>& path_flag() {
+  static std::atomic<int> flag([] {
+    const char* e = std::getenv("PKV_ATTN_KERNEL");
+    return (e && std::string(e) == "valu") ? (int)AttnPath::kValu : (int)AttnPath::kMfma;
+  }());
+  return flag;
+}
+AttnPath attn_path() { return static_cast<AttnPath>(path_flag().load(std::memory_order_relaxed)); }
+}  // namespace pkv
 
 extern "C" {
 
@@ -177,6 +199,15 @@ const char* pkv_status_string(int status) {
 }
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_select_partition_kernel(int variant) {
+  if (variant != PKV_PARTITION_VALU && variant != PKV_PARTITION_MFMA)
+    return fail(PKV_ERR_UNSUPPORTED, "unknown partition kernel variant %d", variant);
+  pkv::path_flag().store(variant, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int pkv_partition_kernel(void) { return (int)pkv::attn_path(); }
 
 int pkv_attention_waves(int D, int BS, int G, int kv_dtype) {
   if (!supported(D, BS, G, kv_dtype)) return 0;
@@ -206,8 +237,7 @@ int pkv_paged_decode_partition(const void* q, const void* k_cache, const void* v
                              workspace_bytes, &call);
   if (st != PKV_OK) return st;
   if (B == 0) return PKV_OK;
-  hipError_t e = pkv::launch_partition(call.p, call.D, call.BS, call.G, call.fp8, call.blocks,
-                                       static_cast<hipStream_t>(stream));
+  hipError_t e = launch_partition(call, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_fail(e, "partition kernel launch");
 }
 
@@ -239,7 +269,7 @@ int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v
   if (st != PKV_OK) return st;
   if (B == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = pkv::launch_partition(call.p, call.D, call.BS, call.G, call.fp8, call.blocks, s);
+  hipError_t e = launch_partition(call, s);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   e = pkv::launch_merge(call.p, call.D, call.G, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace pkv {
 
 // Arguments of the attention kernels.  Pointers are device pointers.
@@ -49,13 +51,28 @@ constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
 constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
 constexpr int kMaxBatch = 8192;          // sequence prefix sums live in LDS
 
-// Partition kernel (VALU).  Returns hipErrorInvalidValue for an unsupported
-// (D, BS, G, fp8) combination.
-hipError_t launch_partition(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
-                            hipStream_t stream);
-// Workgroups of the partition kernel that fit on one compute unit (0 if unsupported).
-int partition_blocks_per_cu(int D, int BS, int G, bool fp8, size_t lds_bytes);
-size_t partition_lds_bytes(int B);
+// LDS of the sequence prefix sums (plus the scan scratch) for B sequences.
+inline size_t prefix_lds_bytes(int B) {
+  return sizeof(int32_t) * ((size_t)B + 1 + kAttnBlockThreads);
+}
+
+// The two partition-kernel variants.  Launchers return hipErrorInvalidValue
+// for an unsupported (D, BS, G, fp8) combination; *_blocks_per_cu give the
+// workgroups that fit on one compute unit (0 if unsupported).
+enum class AttnPath { kValu = 0, kMfma = 1 };
+hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+                                 hipStream_t stream);
+int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B);
+hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+                                 hipStream_t stream);
+int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B);
+// LDS a workgroup of the MFMA variant needs on top of the prefix sums.
+size_t mfma_stage_lds_bytes(int D);
+
+// Variant used by the attention calls: MFMA unless PKV_ATTN_KERNEL=valu is
+// set when the library loads, or pkv_select_partition_kernel changes it.
+AttnPath attn_path();
+std::atomic<int>& path_flag();
 
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
 

@@ -66,6 +66,10 @@ def _load():
         lib.pkv_last_error.restype = ctypes.c_char_p
         lib.pkv_attention_waves.argtypes = [I, I, I, I]
         lib.pkv_attention_waves.restype = I
+        lib.pkv_select_partition_kernel.argtypes = [I]
+        lib.pkv_select_partition_kernel.restype = I
+        lib.pkv_partition_kernel.argtypes = []
+        lib.pkv_partition_kernel.restype = I
         _lib = lib
     return _lib
 
@@ -137,6 +141,20 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scal
     _check("pkv_kv_append", st)
 
 
+PARTITION_VALU = 0
+PARTITION_MFMA = 1
+
+
+def select_partition_kernel(variant: int) -> None:
+    """pkv_select_partition_kernel: 0 = VALU, 1 = MFMA (process-wide; resize
+    workspaces afterwards)."""
+    _check("pkv_select_partition_kernel", _load().pkv_select_partition_kernel(int(variant)))
+
+
+def partition_kernel() -> int:
+    return int(_load().pkv_partition_kernel())
+
+
 def workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:
     return int(_load().pkv_paged_decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype))
 
@@ -192,3 +210,43 @@ def paged_decode_merge(q, k_cache, v_cache, block_tables, context_lens, scale, o
     args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
                       v_scale, workspace, stream)
     _check("pkv_paged_decode_merge", _load().pkv_paged_decode_merge(*args))
+
+
+class PreparedAttention:
+    """The attention call with its arguments marshalled once, for loops that
+    launch the same shapes repeatedly (benchmarks, serving loops).  The
+    tensors must stay alive and in place for as long as this object is used."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                 k_scale=None, v_scale=None, workspace=None, stream=None):
+        self._args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                k_scale, v_scale, workspace, stream)
+        self._lib = _load()
+
+    def __call__(self):
+        _check("pkv_paged_decode_attention", self._lib.pkv_paged_decode_attention(*self._args))
+
+    def partition(self):
+        _check("pkv_paged_decode_partition", self._lib.pkv_paged_decode_partition(*self._args))
+
+    def merge(self):
+        _check("pkv_paged_decode_merge", self._lib.pkv_paged_decode_merge(*self._args))
+
+
+class PreparedAppend:
+    """kv_append with its arguments marshalled once (see PreparedAttention)."""
+
+    def __init__(self, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+                 stream=None):
+        kvd = _kv_dtype(k_cache)
+        N, Hkv, D = k_new.shape
+        NB, BS = k_cache.shape[0], k_cache.shape[1]
+        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+            _need(t, name, torch.bfloat16, 3)
+        _need(slot_mapping, "slot_mapping", torch.int32, 1)
+        self._args = (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+                      _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB, kvd, _stream(stream))
+        self._lib = _load()
+
+    def __call__(self):
+        _check("pkv_kv_append", self._lib.pkv_kv_append(*self._args))

@@ -27,6 +27,18 @@ def say(*a):
     print(*a, flush=True)
 
 
+KERNELS = {"mfma": ops.PARTITION_MFMA, "valu": ops.PARTITION_VALU}
+
+
+@pytest.fixture(params=list(KERNELS))
+def kernel(request):
+    """Run the test with each partition-kernel variant (the default, MFMA, last)."""
+    ops.select_partition_kernel(KERNELS[request.param])
+    say(f"partition kernel: {request.param}")
+    yield request.param
+    ops.select_partition_kernel(ops.PARTITION_MFMA)
+
+
 def build(B, Hq, Hkv, D, BS, lengths, kv="bf16", seed=0, poison=True, NB=None, scale=None):
     say(f"case B={B} Hq={Hq} Hkv={Hkv} D={D} BS={BS} kv={kv} seed={seed} L={list(lengths)[:8]}")
     return W.build_workload("t", B, Hq, Hkv, D, BS, list(lengths), kv_dtype=kv, seed=seed,
@@ -79,13 +91,13 @@ SMALL = [
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"B{s[0]}Hq{s[1]}Hkv{s[2]}D{s[3]}BS{s[4]}{s[6]}")
-def test_step_matches_oracle_small(shape):
+def test_step_matches_oracle_small(shape, kernel):
     B, Hq, Hkv, D, BS, lengths, kv = shape
     wl = build(B, Hq, Hkv, D, BS, lengths, kv=kv, seed=B * 10 + D + BS)
     check_step(wl, f"{shape}")
 
 
-def test_all_supported_variants_run():
+def test_all_supported_variants_run(kernel):
     """Every (D, BS, G, dtype) instantiation against the oracle."""
     for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8), ("bf16", "fp8")):
         Hkv = 2
@@ -93,7 +105,7 @@ def test_all_supported_variants_run():
         check_step(wl, f"D{D} BS{BS} G{G} {kv}")
 
 
-def test_tiny_configuration():
+def test_tiny_configuration(kernel):
     say("config tiny")
     wl = W.make_config_workload("tiny", device=DEV, poison=True)
     out, ref = check_step(wl, "tiny")
@@ -104,7 +116,7 @@ def test_tiny_configuration():
         assert np.array_equal(o[0, h], v_new[0, h // wl.G])
 
 
-def test_poison_does_not_change_bits():
+def test_poison_does_not_change_bits(kernel):
     """NaN in free blocks, block tails and unused table entries (-1) never
     reaches the math: the poisoned run is bitwise the clean run."""
     outs = []
@@ -114,7 +126,7 @@ def test_poison_does_not_change_bits():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_block_permutation_is_bitwise_invariant():
+def test_block_permutation_is_bitwise_invariant(kernel):
     wl = build(3, 32, 8, 128, 16, (100, 700, 1500), seed=8, poison=False)
     out1 = GS.gpu_step(wl).clone()
     perm = torch.from_numpy(np.random.default_rng(1).permutation(wl.NB)).to(DEV)
@@ -130,7 +142,7 @@ def test_block_permutation_is_bitwise_invariant():
 
 
 @pytest.mark.parametrize("t_star", [0, 15, 16, 511, 512, 1999])
-def test_needle(t_star):
+def test_needle(t_star, kernel):
     wl = build(1, 8, 2, 128, 16, (2000,), seed=3, poison=False)
     ops.kv_append(wl.k_new, wl.v_new, wl.slot_mapping, wl.k_cache, wl.v_cache)
     blk = int(wl.block_tables_np[0, t_star // 16])
@@ -142,7 +154,7 @@ def test_needle(t_star):
 
 
 @pytest.mark.parametrize("page", [0, 1, 31, 62])
-def test_page_marker(page):
+def test_page_marker(page, kernel):
     L = 1000
     wl = build(1, 4, 1, 128, 16, (L,), seed=4, poison=False, scale=0.0)
     ops.kv_append(wl.k_new, wl.v_new, wl.slot_mapping, wl.k_cache, wl.v_cache)
@@ -153,7 +165,7 @@ def test_page_marker(page):
     assert np.allclose(out, expect, rtol=2 ** -8, atol=0)
 
 
-def test_zero_length_sequence_gives_zero():
+def test_zero_length_sequence_gives_zero(kernel):
     wl = build(3, 8, 2, 64, 16, (5, 1, 40), seed=2, poison=False)
     out = GS.gpu_step(wl).clone()
     wl.context_lens[1] = 0
@@ -185,7 +197,7 @@ def pick_sequences(wl: W.Workload, n=6):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b", "long_context", "mixed_70b", "fp8"])
-def test_full_configuration_sampled(name):
+def test_full_configuration_sampled(name, kernel):
     """The full-size configurations, in the launch configuration the benchmark
     times, checked on sampled sequences (first, last, longest, shortest and
     random ones) against the oracle on those sequences' pages."""
