@@ -4,33 +4,40 @@
 // serves all G <= 16 query heads of a kv head with the matrix cores and
 // each K/V byte is read once per group:
 //
-//   scores  S^T[t][h] = sum_d K[t][d] q[h][d]       16x16x32 bf16 MFMA:
-//           A = 16 tokens x 32 dims of K (straight from the page, one
-//           16-byte load per lane), B = the group's q (heads past G are 0)
-//   output  O[h][d] += sum_t P[h][t] V[t][d]          16x16x16 bf16 MFMA:
+//   scores  S^T[t][h] = sum_d K[t][d] q[h][d]       16x16x32 bf16 MFMA,
+//           A = a 16-token x 32-dim slice of the K tile, B = the group's q
+//           (columns past G are zero)
+//   output  O[h][d] += sum_t P[h][t] V[t][d]          16x16x16 bf16 MFMA,
 //           A = P in exactly the register layout S^T came out in,
-//           B = V read back transposed from an LDS copy of the tile
+//           B = four tokens of one head dim of the V tile
 //
-// Lane l (n = l % 16, r = l / 16) ends a score step holding S^T for
-// tokens 4r..4r+3 of the 16-token block and head n; that is the A-operand
-// layout of the 16x16x16 product, so P never leaves its registers.  V is
-// the only operand that needs a transpose (it is contiguous along the head
-// dim, the product contracts over tokens), so each 16-token V tile is
-// staged in LDS (rows padded to avoid bank conflicts) and read back four
-// tokens at a time.
+// Lane l (n = l % 16, r = l / 16) ends a score step holding S^T for tokens
+// 4r..4r+3 of the tile and head n, which is the A-operand layout of the
+// 16x16x16 product, so P never leaves its registers.
 //
-// fp8: K and V codes are widened to bf16 exactly (every e4m3fn value is a
-// bf16 value) before the products; the per-(block, kv head) K scale
+// Data path per 16-token tile: K and V rows are read from HBM with 16-byte
+// non-temporal loads laid out as whole 256-byte runs of consecutive lanes
+// (the layout that streams best through the memory system), then staged in
+// one LDS buffer per wave as bf16 rows with a padded pitch: K first (read
+// back as the A operands, 16 bytes a lane), then V over it (read back with
+// the gfx950 transposing LDS read, which hands each lane four tokens of one
+// head dim, the B operand of the PV product).  fp8 codes are widened to
+// bf16 exactly on the way into LDS; the per-(block, kv head) K scale then
 // multiplies the scores and the V scale is folded into P.
 //
 // Online softmax: one running max per head (kept by the lanes of column
-// n), raised only when a block brings a larger score; the rescale of O is
+// n), raised only when a tile brings a larger score; the rescale of O is
 // then a wave-uniform branch.  The work split over waves is described in
 // decode_common.hpp.
 
 #include <float.h>
 
 #include "decode_common.hpp"
+
+// Build-time tuning knob: waves per SIMD the register budget is cut for.
+#ifndef PKV_MFMA_WAVES_PER_EU
+#define PKV_MFMA_WAVES_PER_EU 3
+#endif
 
 namespace pkv {
 namespace {
@@ -46,13 +53,16 @@ struct MfmaShape {
   static constexpr int G = G_;
   static constexpr bool FP8 = FP8_;
   static constexpr int EB = FP8 ? 1 : 2;      // bytes per cache element
+  static constexpr int RB = D * EB;           // bytes of one token's head row in the cache
+  static constexpr int LPR = RB / 16;         // lanes per row (16 bytes each)
+  static constexpr int RPI = kWave / LPR;     // rows per wave-wide load
+  static constexpr int NI = 16 / RPI;         // wave-wide loads per 16-token tile
   static constexpr int NKK = D / 32;          // score k-steps (16x16x32)
   static constexpr int NBN = D / 16;          // output n-blocks (16x16x16)
-  static constexpr int SUB = BS / 16;         // 16-token blocks per page
-  static constexpr int CH = D * EB / 64;      // 16-byte loads per lane per 16-token block
-  static constexpr int STRIDE = 2 * D + 16;   // LDS pitch (bytes) of a bf16 V tile row
+  static constexpr int SUB = BS / 16;         // 16-token tiles per page
+  static constexpr int PITCH = 2 * D + 32;    // LDS row pitch (bytes) of a bf16 tile
   static_assert(G >= 1 && G <= 16, "the group is the 16-wide N dimension");
-  static_assert(CH >= 1 && BS % 16 == 0, "shape");
+  static_assert(NI >= 1 && BS % 16 == 0, "shape");
 };
 
 __device__ __forceinline__ short bf16_bits(float x) {
@@ -75,10 +85,50 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16
   }
 }
 
+// Streaming 16-byte load: every KV byte is read once, so it is marked
+// non-temporal (probe measurements on this layout: ~10% more bandwidth).
+__device__ __forceinline__ uint4 load_nt(const unsigned char* p) {
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(p);
+  uint4 v;
+  v.x = __builtin_nontemporal_load(a + 0);
+  v.y = __builtin_nontemporal_load(a + 1);
+  v.z = __builtin_nontemporal_load(a + 2);
+  v.w = __builtin_nontemporal_load(a + 3);
+  return v;
+}
+
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+
+// Store one 16-token tile (this lane's NI chunks, already in registers) into
+// the wave's LDS buffer as bf16 rows of PITCH bytes.  Rows at or past `live`
+// are written as zeros when `zero_dead` (V: P = 0 must meet V = 0, not NaN).
 template <class S>
-__global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const AttnParams p) {
-  constexpr int D = S::D, BS = S::BS, G = S::G, EB = S::EB;
-  constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, CH = S::CH, STRIDE = S::STRIDE;
+__device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch)[S::NI],
+                                           int lane, int live, bool zero_dead) {
+  const int rr = lane / S::LPR, c = lane % S::LPR;
+#pragma unroll
+  for (int s = 0; s < S::NI; ++s) {
+    const int row = s * S::RPI + rr;
+    uint4 v = ch[s];
+    if (zero_dead && row >= live) v = make_uint4(0, 0, 0, 0);
+    unsigned char* dst = tile + row * S::PITCH;
+    if constexpr (S::FP8) {
+      bf16x8_t lo, hi;
+      fp8x16_to_bf16(v, lo, hi);
+      *reinterpret_cast<bf16x8_t*>(dst + 32 * c) = lo;
+      *reinterpret_cast<bf16x8_t*>(dst + 32 * c + 16) = hi;
+    } else {
+      *reinterpret_cast<uint4*>(dst + 16 * c) = v;
+    }
+  }
+}
+
+template <class S>
+__global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU, PKV_MFMA_WAVES_PER_EU)))
+void mfma_partition_kernel(const AttnParams p) {
+  constexpr int D = S::D, BS = S::BS, G = S::G, EB = S::EB, RB = S::RB;
+  constexpr int NI = S::NI, RPI = S::RPI, LPR = S::LPR;
+  constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
@@ -95,15 +145,21 @@ __global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const
   const int wave_in_block = threadIdx.x >> 6;
   const int wave = blockIdx.x * kAttnWavesPerBlock + wave_in_block;
   const size_t pre_bytes = (sizeof(int32_t) * ((size_t)p.B + 1 + kAttnBlockThreads) + 15) & ~size_t(15);
-  unsigned char* vtile = smem + pre_bytes + (size_t)wave_in_block * (16 * STRIDE);
+  unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * (16 * PITCH);
 
-  const int n = lane & 15;        // head column of S^T / O, token row of K and V loads
-  const int r = lane >> 4;        // 4-token group of S^T / O rows; 16-byte chunk of a row
+  const int n = lane & 15;        // head column of S^T and O; K row of the A operand
+  const int r = lane >> 4;        // 4-token group of S^T rows; 4-head group of O rows
   const int W = p.total_waves;
   const int Q = (total + W - 1) / W;
   int x = wave * Q;
   const int x_end = min(total, x + Q);
-  const int64_t row_bytes = (int64_t)Hkv * D * EB;
+  const int64_t row_bytes = (int64_t)Hkv * RB;
+  // this lane's 16-byte chunk of a token row, for the global loads
+  const int load_row = lane / LPR;
+  const int load_off = 16 * (lane % LPR);
+  // tile offsets of the operand reads
+  const int k_rd = n * PITCH + 16 * r;                               // + 64 kk
+  const int v_rd = (4 * r + (n >> 2)) * PITCH + 8 * (n & 3);         // + 32 nb
   const unsigned char* __restrict__ kc = static_cast<const unsigned char*>(p.k_cache);
   const unsigned char* __restrict__ vc = static_cast<const unsigned char*>(p.v_cache);
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(p.q);
@@ -113,21 +169,17 @@ __global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const
     const int b = pc.b, g = pc.g;
     const int L = min(max(p.context_lens[b], 0), p.MBS * BS);
     const int32_t* bt_row = p.block_tables + (int64_t)b * p.MBS;
-    // byte offset of this lane's first chunk inside a token row
-    const int64_t lane_off = (int64_t)g * D * EB + 16 * r;
+    const int64_t head_off = (int64_t)g * RB + load_off;
 
-    // ---- q of the group as the B operand of the score product -------------
-    // element i of k-step kk holds dim d(kk, r, i):
-    //   bf16: 32 kk + 8 r + i        fp8: 64 (kk/2) + 16 r + 8 (kk%2) + i
-    // (any fixed permutation of the head dim works as long as K uses it too)
+    // q of the group as the B operand: element i of k-step kk is head dim
+    // 32 kk + 8 r + i, the same dims the K operand's element i holds
     bf16x8_t qB[NKK];
     {
-      const uint16_t* qrow = qp + ((int64_t)b * p.Hq + g * G + n) * D;
+      const uint16_t* qrow = qp + ((int64_t)b * p.Hq + g * G + n) * D + 8 * r;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int d0 = S::FP8 ? 64 * (kk / 2) + 16 * r + 8 * (kk % 2) : 32 * kk + 8 * r;
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < G) v = *reinterpret_cast<const uint4*>(qrow + d0);
+        if (n < G) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
         qB[kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
@@ -145,70 +197,47 @@ __global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const
         const int v = bt_row[jc + lane];
         phys_l = ((unsigned)v < (unsigned)p.NB) ? v : 0;
       }
-      uint4 kb[2][CH], vb[2][CH];
-      float ksc[2], vsc[2];
-      // one unit = 16 tokens: block k of the chunk, sub-block sb
-      auto issue = [&](int u, int buf) {
+      uint4 kb[NI], vb[NI];
+      float ksc = 1.0f, vsc = 1.0f;
+      // one unit = one 16-token tile: page k of the chunk, tile sb.  Each
+      // wave has the tile's K and V loads in flight while it waits; the
+      // other waves of the CU overlap their compute with those waits
+      // (measured: issuing the next tile early does not pay for the extra
+      // registers it costs).
+      auto issue = [&](int u) {
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
-        const int64_t base = ((int64_t)phys * BS + sb * 16 + n) * row_bytes + lane_off;
+        const int64_t base = ((int64_t)phys * BS + sb * 16 + load_row) * row_bytes + head_off;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          kb[buf][j] = *reinterpret_cast<const uint4*>(kc + base + 64 * j);
-          vb[buf][j] = *reinterpret_cast<const uint4*>(vc + base + 64 * j);
+        for (int s = 0; s < NI; ++s) {
+          kb[s] = load_nt(kc + base + (int64_t)s * RPI * row_bytes);
+          vb[s] = load_nt(vc + base + (int64_t)s * RPI * row_bytes);
         }
         if constexpr (S::FP8) {
-          ksc[buf] = p.k_scale[(int64_t)phys * Hkv + g];
-          vsc[buf] = p.v_scale[(int64_t)phys * Hkv + g];
+          ksc = p.k_scale[(int64_t)phys * Hkv + g];
+          vsc = p.v_scale[(int64_t)phys * Hkv + g];
         }
       };
-      auto consume = [&](int u, int buf) {
+      const int nunits = nchunk * SUB;
+      for (int u = 0; u < nunits; ++u) {
+        issue(u);
         const int k = u / SUB, sb = u % SUB;
-        const int tok0 = (jc + k) * BS + sb * 16;   // position of the unit's first token
-        const bool tail = tok0 + 16 > L;
+        const int tok0 = (jc + k) * BS + sb * 16;   // position of the tile's first token
+        const int live = L - tok0;                  // rows of the tile inside the history
 
-        // scores: S^T (16 tokens x 16 heads), lane holds tokens 4r..4r+3 of head n
+        // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 heads)
+        stage_tile<S>(tile, kb, lane, live, false);
         float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          if constexpr (S::FP8) {
-            bf16x8_t lo, hi;
-            fp8x16_to_bf16(kb[buf][j], lo, hi);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qB[2 * j], s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qB[2 * j + 1], s, 0, 0, 0);
-          } else {
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, kb[buf][j]), qB[j], s, 0, 0, 0);
-          }
+        for (int kk = 0; kk < NKK; ++kk) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tile + k_rd + 64 * kk);
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], s, 0, 0, 0);
         }
-        const float c = S::FP8 ? p.scale_log2 * ksc[buf] : p.scale_log2;
+        const float c = S::FP8 ? p.scale_log2 * ksc : p.scale_log2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] *= c;
-        if (tail) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tok0 + 4 * r + i >= L) s[i] = -INFINITY;
-        }
-
-        // V tile -> LDS as bf16 rows (token n of the unit); rows past the
-        // history are written as zeros so that P = 0 meets V = 0, not NaN
-        {
-          const bool dead = tail && tok0 + n >= L;
-          unsigned char* dst = vtile + n * STRIDE;
-#pragma unroll
-          for (int j = 0; j < CH; ++j) {
-            uint4 v = vb[buf][j];
-            if (dead) v = make_uint4(0, 0, 0, 0);
-            if constexpr (S::FP8) {
-              bf16x8_t lo, hi;
-              fp8x16_to_bf16(v, lo, hi);
-              const int d0 = 64 * j + 16 * r;
-              *reinterpret_cast<bf16x8_t*>(dst + 2 * d0) = lo;
-              *reinterpret_cast<bf16x8_t*>(dst + 2 * d0 + 16) = hi;
-            } else {
-              *reinterpret_cast<uint4*>(dst + 64 * j + 16 * r) = v;
-            }
-          }
+        for (int i = 0; i < 4; ++i) {
+          s[i] *= c;
+          if (4 * r + i >= live) s[i] = -INFINITY;
         }
 
         // online softmax, one max per head (column n)
@@ -228,38 +257,25 @@ __global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const
             for (int nb = 0; nb < NBN; ++nb) O[nb][i] *= a;
           }
         }
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[i] = fast_exp2(s[i] - m_run);
-          l_run += pr[i];
-        }
-        const float pv = S::FP8 ? vsc[buf] : 1.0f;
         short4_t pa;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pa[i] = bf16_bits(pr[i] * pv);
+        for (int i = 0; i < 4; ++i) {
+          const float pr = fast_exp2(s[i] - m_run);
+          l_run += pr;
+          pa[i] = bf16_bits(S::FP8 ? pr * vsc : pr);
+        }
 
-        // O += P V, B operand = V[4r + i][16 nb + n] read back from LDS
-        const unsigned char* src = vtile + (4 * r) * STRIDE + 2 * n;
+        // V tile -> the same LDS buffer (its K reads are done, LDS is in
+        // order within a wave) -> transposed B operands, O += P V
+        stage_tile<S>(tile, vb, lane, live, true);
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
-          short4_t vB;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vB[i] = *reinterpret_cast<const short*>(src + i * STRIDE + 32 * nb);
+          // (C-style cast: generic -> LDS address space)
+          const short4_t vB =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(tile + v_rd + 32 * nb));
           O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vB, O[nb], 0, 0, 0);
         }
-      };
-      const int nunits = nchunk * SUB;
-      issue(0, 0);
-      int u = 0;
-      for (; u + 1 < nunits; u += 2) {
-        issue(u + 1, 1);
-        consume(u, 0);
-        if (u + 2 < nunits) issue(u + 2, 0);
-        consume(u + 1, 1);
       }
-      if (u < nunits) consume(u, 0);
     }
 
     // ---- finish the piece ---------------------------------------------------
@@ -304,7 +320,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void mfma_partition_kernel(const
 }  // namespace
 
 size_t mfma_stage_lds_bytes(int D) {
-  return (size_t)kAttnWavesPerBlock * 16 * (2 * D + 16);
+  return (size_t)kAttnWavesPerBlock * 16 * (2 * D + 32);
 }
 
 static size_t mfma_lds_total(int B, int D) {

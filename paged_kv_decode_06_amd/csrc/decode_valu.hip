@@ -33,9 +33,18 @@ struct ValuShape {
   static_assert(LPP >= 1 && BS % TPW == 0, "page must hold whole token rows");
 };
 
+// Streaming loads: every KV byte is read once, so they are non-temporal.
 template <class S>
 __device__ __forceinline__ typename S::Vec load_row(const uint8_t* __restrict__ base) {
-  return *reinterpret_cast<const typename S::Vec*>(base);
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(base);
+  typename S::Vec v;
+  v.x = __builtin_nontemporal_load(a + 0);
+  v.y = __builtin_nontemporal_load(a + 1);
+  if constexpr (!S::FP8) {
+    v.z = __builtin_nontemporal_load(a + 2);
+    v.w = __builtin_nontemporal_load(a + 3);
+  }
+  return v;
 }
 
 template <class S>
