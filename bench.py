@@ -9,16 +9,18 @@ L * 2 * Hkv * D * bytes per element) divided by the measured step time.
 
 Inputs are resident in HBM before timing starts.  R copies of the KV cache
 (same contents, different addresses) are cycled so that no step finds the
-previous step's pages in the 256 MB memory-side cache.  The partition
-kernel's own duration is taken with HIP events recorded on the stream it is
-launched on, and gives the roofline entry; the oracle timed on the host
-cores gives the CPU baseline.
+previous step's pages in the 256 MB memory-side cache.  The K timed steps
+run with nothing else in the stream; the same K steps are then run again
+with a HIP event pair around every partition launch (recorded on the stream
+the kernel runs on), whose mean gives the roofline entry.  The oracle timed
+on the host cores gives the CPU baseline.
 
   python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +39,39 @@ def kv_bytes(wl) -> int:
         pages = ((wl.lengths + wl.BS - 1) // wl.BS).sum()
         tot += int(pages) * wl.Hkv * 2 * 4
     return tot
+
+
+PARTITION_SOURCES = ["decode_mfma.hip", "decode_valu.hip", "decode_common.hpp", "pkv_device.hpp",
+                     "pkv_internal.hpp"]
+
+
+def partition_source_hash() -> str:
+    """sha256 over the sources the partition kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_decode_06_amd", "csrc")
+    for name in PARTITION_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, kernel: str):
+    """HBM bytes per partition launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known
+    size), or None when there is none for this workload or the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            entries = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for ent in entries:
+        if ent.get("config") == config and ent.get("kernel") == kernel:
+            if ent.get("source_sha256") != partition_source_hash():
+                return None
+            return ent["traffic_bytes_per_launch"]
+    return None
 
 
 def cpu_baseline(wl, budget_s=12.0):
@@ -85,6 +120,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma",
                     help="partition-kernel variant")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reads 1 GiB, writes "
+                         "1 GiB) a few times, to scale hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -99,6 +137,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 3}), flush=True)
+        return
     ops.select_partition_kernel(ops.PARTITION_MFMA if args.kernel == "mfma" else ops.PARTITION_VALU)
     cfg = W.CONFIGS[args.config]
     wl = W.make_config_workload(args.config, device=dev, poison=False)
@@ -108,7 +154,7 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     kvd = ops.KV_FP8 if wl.kv_dtype == "fp8" else ops.KV_BF16
-    ws = torch.empty(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
+    ws = torch.zeros(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(wl.q)
     caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
@@ -128,10 +174,25 @@ def main():
             app, att = steps[i % copies]
             app()
             att()
-        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        # timed region: exactly K steps, nothing else in the stream
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for i in range(K):
+            app, att = steps[(Wm + i) % copies]
+            app()
+            att()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    # the same K steps again with a HIP event pair around every partition
+    # launch, recorded on the stream the kernel runs on (the event records
+    # themselves add a few microseconds to each bracketed launch)
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
         for i in range(K):
             app, att = steps[(Wm + i) % copies]
             app()
@@ -140,8 +201,8 @@ def main():
             ev1[i].record(stream)
             att.merge()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+        t3 = time.perf_counter()
+    ms_per_step_events = (t3 - t2) * 1e3 / K
     part_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
     part_avg_ms = float(np.mean(part_ms))
 
@@ -194,10 +255,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.config, args.kernel),
         },
         "detail": {
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+            "ms_per_step_with_partition_events": round(ms_per_step_events, 5),
             "partition_us_mean": round(part_avg_ms * 1e3, 2),
             "partition_us_median": round(part_med_us, 2),
             "merge_us_median": round(merge_us, 2),

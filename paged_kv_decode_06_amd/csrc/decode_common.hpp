@@ -13,14 +13,18 @@
 // Work split (flash-decoding style split of the context).  The work axis is
 // every (sequence b, kv head g, page j) triple in that order: position
 // Hkv*pre[b] + g*n_b + j, where n_b = ceil(L_b / BS) and pre is the prefix
-// sum of n_b.  A persistent grid of W waves cuts this axis into equal pieces
-// of Q = ceil(Hkv*pre[B] / W) pages, so every wave streams the same number of
-// KV bytes whatever the length mix.  A (b, g) run that one wave covers
-// completely is finished in place (out written as bf16); otherwise each wave
-// that touches it leaves (m, l, o) for its share in workspace row
-// wave + segment (segment = b*Hkv + g), and the merge kernel combines the
-// rows of a segment, which are consecutive.  m is kept in the exp2 domain
-// (scores times scale*log2(e)).
+// sum of n_b.  The axis is cut into consecutive pieces of equal page count
+// for a persistent grid of W waves, so every wave streams the same number of
+// KV bytes whatever the length mix.  kPiecesPerWave pieces per wave are
+// taken from far apart on the axis; the default is one (measured: a second
+// or third piece costs more in per-piece setup than it recovers in balance).
+//
+// A (b, g) run that one piece covers completely is finished in place (out
+// written as bf16); otherwise each piece that touches it leaves (m, l, o)
+// for its share in workspace row k + segment (segment = b*Hkv + g).  Both k
+// and the segment grow along the axis, so the row is unique, and the rows
+// of one segment are consecutive for the merge kernel.  m is kept in the
+// exp2 domain (scores times scale*log2(e)).
 #pragma once
 
 #include "pkv_device.hpp"
@@ -73,6 +77,37 @@ __device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int Hk
       hi = mid - 1;
   }
   return lo;
+}
+
+// The axis is cut into kPiecesPerWave * W consecutive pieces of Qp pages;
+// wave w streams pieces w, w + W, w + 2W, ...
+struct WorkSplit {
+  int total;  // pages on the axis
+  int W;      // waves
+  int Qp;     // piece length (pages)
+};
+
+__device__ __forceinline__ WorkSplit make_split(int total, int W) {
+  WorkSplit s;
+  s.total = total;
+  s.W = W;
+  s.Qp = (total + kPiecesPerWave * W - 1) / (kPiecesPerWave * W);
+  return s;
+}
+
+// Piece containing axis position x.
+__device__ __forceinline__ int piece_of(const WorkSplit& s, int x) { return x / s.Qp; }
+
+// Drives one wave through its pieces; body(x, x_end, k) streams axis pages
+// [x, x_end) of piece k.
+template <class Body>
+__device__ __forceinline__ void run_split(const WorkSplit& s, int wave, Body&& body) {
+  for (int i = 0; i < kPiecesPerWave; ++i) {
+    const int k = i * s.W + wave;
+    const int x = k * s.Qp;
+    if (x >= s.total) break;
+    body(x, min(s.total, x + s.Qp), k);
+  }
 }
 
 // One wave's share of a (sequence, kv head) run: pages [j0, j1) of run

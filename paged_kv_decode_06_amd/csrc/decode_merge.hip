@@ -1,6 +1,6 @@
 // Log-sum-exp merge of the partition kernel's per-wave shares.
 //
-// For a (sequence, query head) whose history was split over waves w0..w1,
+// For a (sequence, query head) whose history was split over pieces k0..k1,
 // share p holds m_p (max score, exp2 domain), l_p = sum_t exp2(s_t - m_p)
 // and o_p = sum_t exp2(s_t - m_p) v_t.  With M = max_p m_p:
 //   out = sum_p exp2(m_p - M) o_p / sum_p exp2(m_p - M) l_p,
@@ -13,76 +13,184 @@
 namespace pkv {
 namespace {
 
-// Merge: one wave per (sequence, query head).  The rows of a (b, g) run are
-// wave + segment for the consecutive waves w0..w1 whose pieces cover it.
+// Merge: one wave per (sequence, query head), four per workgroup.  The
+// rows of a (b, g) run are k + segment for the consecutive pieces k0..k1
+// that cover it.  A row is D floats; TPR lanes take 4 dims each, so
+// the wave reads RPW rows per step, and the unrolled loop keeps several
+// steps of independent loads in flight; the RPW row groups are summed with
+// cross-lane shuffles at the end.
 template <int D>
 __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnParams p, int G) {
-  constexpr int PER = D / kWave;               // head-dim elements per lane
+  constexpr int TPR = D / 4;                   // lanes per row (4 dims each)
+  constexpr int RPW = kWave / TPR;             // rows per wave step
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t bh = (int64_t)blockIdx.x * (kAttnBlockThreads / kWave) + (threadIdx.x >> 6);
+  const int sub = lane / TPR;
+  const int d4 = (lane % TPR) * 4;
+  const int64_t bh = (int64_t)blockIdx.x * kAttnWavesPerBlock + (threadIdx.x >> 6);
   if (bh >= (int64_t)p.B * p.Hq) return;
   const int b = (int)(bh / p.Hq);
   const int h = (int)(bh % p.Hq);
   const int g = h / G;
   const int jj = h % G;
   const int Hkv = p.Hkv;
-  const int total = Hkv * p.ws_pre[p.B];
-  const int n_b = p.ws_pre[b + 1] - p.ws_pre[b];
+  const int32_t* __restrict__ pre = p.ws_pre;
+  const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
+  const int total = Hkv * pre_B;
+  const int n_b = pre_b1 - pre_b;
   uint16_t* op = static_cast<uint16_t*>(p.out) + bh * D;
   if (n_b == 0) {                              // empty history: defined as 0
-#pragma unroll
-    for (int k = 0; k < PER; ++k) op[lane * PER + k] = 0;
+    if (lane < TPR) *reinterpret_cast<uint2*>(op + d4) = make_uint2(0, 0);
     return;
   }
-  const int W = p.total_waves;
-  const int Q = (total + W - 1) / W;
-  const int start = Hkv * p.ws_pre[b] + g * n_b;
-  const int w0 = start / Q;
-  const int w1 = (start + n_b - 1) / Q;
-  if (w0 == w1) return;                        // finished by the partition kernel
+  const WorkSplit split = make_split(total, p.total_waves);
+  const int start = Hkv * pre_b + g * n_b;
+  const int k0 = piece_of(split, start);
+  const int k1 = piece_of(split, start + n_b - 1);
+  if (k0 == k1) return;                        // finished by the partition kernel
   const int seg = b * Hkv + g;
-  const int P = w1 - w0 + 1;
-  const int64_t row0 = (int64_t)w0 + seg;
+  const int P = k1 - k0 + 1;
+  const int64_t rok0 = (int64_t)k0 + seg;
+  const float* __restrict__ ml = p.ws_ml;
+  const float* __restrict__ po = p.ws_o;
 
   float M = -FLT_MAX;
-  for (int i = lane; i < P; i += kWave) M = fmaxf(M, p.ws_ml[((row0 + i) * G + jj) * 2]);
+  for (int i = lane; i < P; i += kWave) M = fmaxf(M, ml[((rok0 + i) * G + jj) * 2]);
   M = wave_max(M);
 
-  float num[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) num[k] = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
-  for (int i0 = 0; i0 < P; i0 += kWave) {
-    const int n = min(kWave, P - i0);
-    float wgt = 0.0f;
-    if (lane < n) {
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + ((row0 + i0 + lane) * G + jj) * 2);
-      wgt = fast_exp2(ml.x - M);
-      den += wgt * ml.y;
-    }
-    for (int i = 0; i < n; ++i) {
-      const float wi = __shfl(wgt, i);
-      const float* src = p.ws_o + ((row0 + i0 + i) * G + jj) * D + lane * PER;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) num[k] = fmaf(wi, src[k], num[k]);
-    }
+#pragma unroll 8
+  for (int i = sub; i < P; i += RPW) {
+    const int64_t row = (rok0 + i) * G + jj;
+    const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
+    const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
+    const float w = fast_exp2(mlv.x - M);
+    den = fmaf(w, mlv.y, den);
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
   }
-  den = wave_sum(den);
-  const float inv = 1.0f / den;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(op + lane * 2) = pack_bf16x2(num[0] * inv, num[1] * inv);
-  } else {
-    op[lane] = (uint16_t)f32_to_bf16_rne(num[0] * inv);
+#pragma unroll
+  for (int off = TPR; off < kWave; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+    den += __shfl_xor(den, off);
+  }
+  if (lane < TPR) {
+    const float inv = 1.0f / den;
+    *reinterpret_cast<uint2*>(op + d4) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+  }
+}
+
+// Merge for few rows with many shares each (long contexts): one workgroup
+// per (sequence, query head); thread t owns 4 head dims of every NGRP-th
+// share, so NGRP shares are read at once, and the groups are summed
+// through LDS.
+template <int D>
+__global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const AttnParams p, int G) {
+  constexpr int TPR = D / 4;
+  constexpr int NGRP = kAttnBlockThreads / TPR;
+  __shared__ float s_acc[NGRP][D];
+  __shared__ float s_den[NGRP];
+  __shared__ float s_max[kAttnWavesPerBlock];
+  const int t = threadIdx.x;
+  const int grp = t / TPR;
+  const int d4 = (t % TPR) * 4;
+  const int64_t bh = blockIdx.x;
+  const int b = (int)(bh / p.Hq);
+  const int h = (int)(bh % p.Hq);
+  const int g = h / G;
+  const int jj = h % G;
+  const int Hkv = p.Hkv;
+  const int32_t* __restrict__ pre = p.ws_pre;
+  const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
+  const int total = Hkv * pre_B;
+  const int n_b = pre_b1 - pre_b;
+  uint16_t* op = static_cast<uint16_t*>(p.out) + bh * D;
+  if (n_b == 0) {
+    if (t < TPR) *reinterpret_cast<uint2*>(op + d4) = make_uint2(0, 0);
+    return;
+  }
+  const WorkSplit split = make_split(total, p.total_waves);
+  const int start = Hkv * pre_b + g * n_b;
+  const int k0 = piece_of(split, start);
+  const int k1 = piece_of(split, start + n_b - 1);
+  if (k0 == k1) return;
+  const int seg = b * Hkv + g;
+  const int P = k1 - k0 + 1;
+  const int64_t row0 = (int64_t)k0 + seg;
+  const float* __restrict__ ml = p.ws_ml;
+  const float* __restrict__ po = p.ws_o;
+
+  float m_loc = -FLT_MAX;
+  for (int i = t; i < P; i += kAttnBlockThreads) m_loc = fmaxf(m_loc, ml[((row0 + i) * G + jj) * 2]);
+  m_loc = wave_max(m_loc);
+  if ((t & (kWave - 1)) == 0) s_max[t >> 6] = m_loc;
+  __syncthreads();
+  float M = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kAttnWavesPerBlock; ++w) M = fmaxf(M, s_max[w]);
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.0f;
+#pragma unroll 4
+  for (int i = grp; i < P; i += NGRP) {
+    const int64_t row = (row0 + i) * G + jj;
+    const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
+    const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
+    const float w = fast_exp2(mlv.x - M);
+    den = fmaf(w, mlv.y, den);
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
+  }
+  *reinterpret_cast<float4*>(&s_acc[grp][d4]) = acc;
+  if (d4 == 0) s_den[grp] = den;
+  __syncthreads();
+  if (t < TPR) {
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dsum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NGRP; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(&s_acc[q][d4]);
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+      dsum += s_den[q];
+    }
+    const float inv = 1.0f / dsum;
+    *reinterpret_cast<uint2*>(op + d4) =
+        make_uint2(pack_bf16x2(sum.x * inv, sum.y * inv), pack_bf16x2(sum.z * inv, sum.w * inv));
   }
 }
 
 }  // namespace
 
+// Fewer (sequence, query head) rows than this get a workgroup each (they
+// are few and have many shares: long contexts); more get a wave each.
+constexpr int64_t kWideMergeRows = 1024;
+
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
   const int64_t rows = (int64_t)p.B * p.Hq;
-  const int waves_per_block = kAttnBlockThreads / kWave;
-  const dim3 grid((unsigned)((rows + waves_per_block - 1) / waves_per_block));
   if (rows == 0) return hipSuccess;
+  if (rows < kWideMergeRows) {
+    if (D == 128)
+      hipLaunchKernelGGL(merge_wide_kernel<128>, dim3((unsigned)rows), dim3(kAttnBlockThreads), 0,
+                         stream, p, G);
+    else if (D == 64)
+      hipLaunchKernelGGL(merge_wide_kernel<64>, dim3((unsigned)rows), dim3(kAttnBlockThreads), 0,
+                         stream, p, G);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((rows + kAttnWavesPerBlock - 1) / kAttnWavesPerBlock));
   if (D == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kAttnBlockThreads), 0, stream, p, G);
   else if (D == 64)

@@ -149,10 +149,7 @@ void mfma_partition_kernel(const AttnParams p) {
 
   const int n = lane & 15;        // head column of S^T and O; K row of the A operand
   const int r = lane >> 4;        // 4-token group of S^T rows; 4-head group of O rows
-  const int W = p.total_waves;
-  const int Q = (total + W - 1) / W;
-  int x = wave * Q;
-  const int x_end = min(total, x + Q);
+  const WorkSplit split = make_split(total, p.total_waves);
   const int64_t row_bytes = (int64_t)Hkv * RB;
   // this lane's 16-byte chunk of a token row, for the global loads
   const int load_row = lane / LPR;
@@ -164,6 +161,7 @@ void mfma_partition_kernel(const AttnParams p) {
   const unsigned char* __restrict__ vc = static_cast<const unsigned char*>(p.v_cache);
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(p.q);
 
+  run_split(split, wave, [&](int x, const int x_end, const int piece) {
   while (x < x_end) {
     const Piece pc = locate_piece(s_pre, p.B, Hkv, x, x_end);
     const int b = pc.b, g = pc.g;
@@ -300,7 +298,7 @@ void mfma_partition_kernel(const AttnParams p) {
         }
       }
     } else {
-      const int64_t row = (int64_t)wave + seg;
+      const int64_t row = (int64_t)piece + seg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
@@ -315,6 +313,7 @@ void mfma_partition_kernel(const AttnParams p) {
     }
     x = pc.run_start + pc.j1;
   }
+  });
 }
 
 }  // namespace

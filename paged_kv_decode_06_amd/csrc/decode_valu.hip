@@ -65,10 +65,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * (kAttnBlockThreads / kWave) + (threadIdx.x >> 6);
-  const int W = p.total_waves;
-  const int Q = (total + W - 1) / W;
-  int x = wave * Q;
-  const int x_end = min(total, x + Q);
+  const WorkSplit split = make_split(total, p.total_waves);
   const int r = lane / LPT;                    // token row within a wave-wide load
   const int c = lane % LPT;                    // 8-element chunk of the head dim
   const int64_t row_bytes = (int64_t)Hkv * D * EB;   // one token, all kv heads
@@ -76,6 +73,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
   const uint8_t* __restrict__ vc = static_cast<const uint8_t*>(p.v_cache);
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(p.q);
 
+  run_split(split, wave, [&](int x, const int x_end, const int piece) {
   while (x < x_end) {
     // ---- locate the (sequence, kv head) run containing x ----------------
     const int b = find_sequence(s_pre, p.B, Hkv, x);
@@ -242,7 +240,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
           *reinterpret_cast<uint4*>(op + ((int64_t)b * p.Hq + g * G + jj) * D + c * 8) = o;
         }
       } else {
-        const int64_t row = (int64_t)wave + seg;
+        const int64_t row = (int64_t)piece + seg;
 #pragma unroll
         for (int jj = 0; jj < G; ++jj) {
           float4* dst = reinterpret_cast<float4*>(p.ws_o + (row * G + jj) * D + c * 8);
@@ -255,6 +253,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
     }
     x = run_start + j1;
   }
+  });
 }
 
 }  // namespace

@@ -19,13 +19,14 @@ __global__ __launch_bounds__(256) void kv_append_bf16_kernel(
     const int32_t* __restrict__ slots, uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
     int row_vecs, int64_t num_slots) {
   const int i = blockIdx.x;
-  const int64_t slot = slots[i];
-  if (slot < 0 || slot >= num_slots) return;
   for (int c = threadIdx.x; c < 2 * row_vecs; c += blockDim.x) {
-    if (c < row_vecs)
-      k_cache[slot * row_vecs + c] = k_new[(int64_t)i * row_vecs + c];
-    else
-      v_cache[slot * row_vecs + (c - row_vecs)] = v_new[(int64_t)i * row_vecs + (c - row_vecs)];
+    // the row load does not wait for the slot: both latencies overlap
+    const bool is_k = c < row_vecs;
+    const int cc = is_k ? c : c - row_vecs;
+    const uint4 v = (is_k ? k_new : v_new)[(int64_t)i * row_vecs + cc];
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= num_slots) return;
+    (is_k ? k_cache : v_cache)[slot * row_vecs + cc] = v;
   }
 }
 
@@ -42,17 +43,16 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(
   const int which = blockIdx.x & 1;          // 0 = K, 1 = V
   const int g = (blockIdx.x >> 1) % Hkv;
   const int i = (blockIdx.x >> 1) / Hkv;
+  const uint16_t* src = (which ? v_new : k_new) + ((int64_t)i * Hkv + g) * D;
+  float x[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) x[k] = __uint_as_float((uint32_t)src[lane + k * kWave] << 16);
   const int64_t slot = slots[i];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / BS;
   const int off = (int)(slot % BS);
-  const uint16_t* src = (which ? v_new : k_new) + ((int64_t)i * Hkv + g) * D;
   uint8_t* dst = (which ? v_cache : k_cache) + (slot * Hkv + g) * D;
   float* scale_slot = (which ? v_scale : k_scale) + blk * Hkv + g;
-
-  float x[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) x[k] = __uint_as_float((uint32_t)src[lane + k * kWave] << 16);
 
   float sc;
   if (off == 0) {

@@ -33,15 +33,20 @@ struct WorkspaceLayout {
   int rows;
 };
 
-// rows = total_waves + B * Hkv: each (wave, (sequence, kv head)) pair that
-// shares work gets row wave + segment, a unique index (both grow together
-// along the work axis).
+// Pieces per wave on the work axis (the split is described in
+// decode_common.hpp); a piece k that shares a (sequence, kv head) segment
+// with other pieces writes row k + segment.
+#ifndef PKV_PIECES_PER_WAVE
+#define PKV_PIECES_PER_WAVE 1
+#endif
+constexpr int kPiecesPerWave = PKV_PIECES_PER_WAVE;
+
 inline WorkspaceLayout workspace_layout(int B, int Hkv, int G, int D, int total_waves) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
-  w.rows = total_waves + B * Hkv;
+  w.rows = kPiecesPerWave * total_waves + B * Hkv;
   w.pre_off = 0;
-  w.ml_off = up(sizeof(int32_t) * (size_t)(B + 1));
+  w.ml_off = w.pre_off + up(sizeof(int32_t) * (size_t)(B + 1));
   w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * G);
   w.total = w.o_off + up(sizeof(float) * (size_t)w.rows * G * D);
   return w;

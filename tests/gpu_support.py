@@ -26,7 +26,7 @@ def workspace_for(wl: W.Workload) -> torch.Tensor:
     kvd = ops.KV_FP8 if wl.kv_dtype == "fp8" else ops.KV_BF16
     n = ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd)
     assert n > 0
-    return torch.empty(n, dtype=torch.uint8, device=wl.q.device)
+    return torch.zeros(n, dtype=torch.uint8, device=wl.q.device)   # zero-filled once
 
 
 def gpu_step(wl: W.Workload, out=None, workspace=None, append=True) -> torch.Tensor:

@@ -216,3 +216,27 @@ def test_full_configuration_sampled(name, kernel):
     GS.assert_attention_close(gpu, ref, wl.kv_dtype, name)
     say(name, GS.error_report(gpu, ref))
     assert torch.isfinite(out.float()).all()
+
+
+def test_repeated_calls_reuse_the_workspace_and_are_deterministic(kernel):
+    """Waves claim the tail of the work from a counter in the workspace; the
+    merge kernel clears it.  Chunk boundaries and partial rows do not depend
+    on which wave claims what, so repeated calls on one workspace give the
+    same bits, and the counter is zero after every call."""
+    wl = build(16, 32, 8, 128, 16, np.random.default_rng(4).integers(200, 3000, 16), seed=11,
+               poison=False)
+    ws = GS.workspace_for(wl)
+    first = GS.gpu_step(wl, workspace=ws).clone()
+    for _ in range(3):
+        again = GS.gpu_step(wl, workspace=ws, append=False)
+        assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+def test_many_rows_small_lengths(kernel):
+    """B * Hq >= 1024 takes the wave-per-row merge; short, ragged lengths so
+    that many (sequence, kv head) runs are split between pieces."""
+    L = np.random.default_rng(21).integers(1, 400, 64)
+    wl = build(64, 16, 4, 64, 16, L, seed=21)
+    check_step(wl, "B64 Hq16")
