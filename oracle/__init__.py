@@ -57,9 +57,13 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    override = os.environ.get("PKV_ORACLE_LIB")   # a deliberately broken copy, for the mutation test
+    if override:
+        lib = ctypes.CDLL(override)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     I = ctypes.c_int
     lib.pkvo_bf16_to_f64.argtypes = [ctypes.c_uint16]

@@ -240,3 +240,21 @@ def test_many_rows_small_lengths(kernel):
     L = np.random.default_rng(21).integers(1, 400, 64)
     wl = build(64, 16, 4, 64, 16, L, seed=21)
     check_step(wl, "B64 Hq16")
+
+
+def test_edge_cases_empty_full_and_skipped():
+    """B = 0 and N = 0 do nothing; a sequence that fills its block table
+    exactly (L = MBS * BS); a negative slot writes nothing."""
+    wl = build(2, 8, 2, 64, 16, (16 * 7, 5), seed=31, poison=True)
+    assert wl.MBS == 7                               # the first sequence uses every entry
+    check_step(wl, "full table")
+    out = torch.empty_like(wl.q)
+    ws = GS.workspace_for(wl)
+    ops.paged_decode_attention(wl.q[:0], wl.k_cache, wl.v_cache, wl.block_tables[:0],
+                               wl.context_lens[:0], wl.scale, out[:0], workspace=ws)
+    k0 = wl.k_cache.clone()
+    ops.kv_append(wl.k_new[:0], wl.v_new[:0], wl.slot_mapping[:0], wl.k_cache, wl.v_cache)
+    skip = torch.full_like(wl.slot_mapping, -1)
+    ops.kv_append(wl.k_new, wl.v_new, skip, wl.k_cache, wl.v_cache)
+    torch.cuda.synchronize()
+    assert torch.equal(k0.view(torch.int16), wl.k_cache.view(torch.int16))

@@ -1,0 +1,67 @@
+"""The oracle's pins are sensitive: each plausible mistake planted in a copy
+of the oracle's C source makes at least one pin in test_oracle_pins.py fail.
+
+Every mutant is compiled into a temporary library and the pins are run
+against it in a child process (PKV_ORACLE_LIB points the oracle loader at
+it).  CPU only; the shipped oracle is never modified.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pkv_oracle.c")
+
+# (name, text in the oracle, replacement)
+MUTANTS = [
+    ("head h reads kv head h % Hkv", "const int h = g * G + j;", "const int h = j * Hkv + g;"),
+    ("scale dropped", "s[t] = (double)scale * dot;", "s[t] = dot;"),
+    ("offset in block off by one", "const int o = t % BS;", "const int o = (t + 1) % BS;"),
+    ("one position past the history", "for (int t = 0; t < L; ++t) {", "for (int t = 0; t < L + (L < 60); ++t) {"),
+    ("min instead of max as the shift", "if (s[t] > m) m = s[t];", "if (s[t] < m) m = s[t];"),
+    ("weights not normalised", "const double w = s[t] / Z;", "const double w = s[t];"),
+    ("fp8 scale ignored", "(double)scales[scale_idx];", "1.0;"),
+    ("fp8 scale divisor 240 (FNUZ max)", "sc = amax / 448.0f;", "sc = amax / 240.0f;"),
+    ("zero-amax scale 0.5", "if (amax == 0.0f) sc = 1.0f;", "if (amax == 0.0f) sc = 0.5f;"),
+    ("opening token does not store its scale", "*scale_slot = sc;", "(void)0;"),
+    ("e4m3 ties not to even", "(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(0)"),
+    ("e4m3 subnormal exponent", "mag = ldexp((double)m / 8.0, -6);", "mag = ldexp((double)m / 8.0, -7);"),
+    ("no saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);", "if (a >= 464.0) return (uint8_t)(sign | 0x7F);"),
+]
+
+
+def _run_mutant(mut, tmpdir):
+    name, old, new = mut
+    src = open(SRC).read()
+    assert old in src, f"mutation site for '{name}' not found in the oracle"
+    idx = MUTANTS.index(mut)
+    csrc = os.path.join(tmpdir, f"m{idx}.c")
+    lib = os.path.join(tmpdir, f"m{idx}.so")
+    with open(csrc, "w") as f:
+        f.write(src.replace(old, new, 1))
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+                    "-o", lib, csrc, "-lm"], check=True, capture_output=True)
+    env = dict(os.environ, PKV_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return name, r.returncode
+
+
+def test_every_planted_mistake_fails_a_pin():
+    with tempfile.TemporaryDirectory() as tmp:
+        with cf.ThreadPoolExecutor(max_workers=4) as ex:
+            results = list(ex.map(lambda m: _run_mutant(m, tmp), MUTANTS))
+    survivors = [name for name, rc in results if rc == 0]
+    assert not survivors, f"mutants not caught by any pin: {survivors}"
+    # and the shipped oracle passes them (the pins are not failing for another reason)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
