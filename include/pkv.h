@@ -85,7 +85,8 @@ extern "C" {
  *         rounded fp32 division, rounded to nearest even and saturated to
  *         +-448.  Same for V with v_scale.
  * Slots outside [0, NB * BS) are skipped.  k_scale and v_scale must be NULL
- * for bf16 and non-NULL for fp8.  N == 0 is a no-op. */
+ * for bf16 and non-NULL for fp8.  N == 0 is a no-op (pointers may then be
+ * NULL). */
 int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                   void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                   int N, int Hkv, int D, int BS, int NB, int kv_dtype, void* stream);
@@ -102,7 +103,7 @@ size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, i
  *   L_b = context_lens[b], K_t = k_cache[block_tables[b][t / BS], t % BS,
  *   h / (Hq / Hkv), :] (times k_scale of that block and head for fp8),
  *   likewise V_t.  No causal mask; nothing past L_b is read.  A sequence with
- *   L_b <= 0 gets out = 0.
+ *   L_b <= 0 gets out = 0.  B == 0 is a no-op (pointers may then be NULL).
  * Accumulation is fp32; out is rounded to bf16 (round to nearest even).
  * The context is split across the whole GPU (a partition kernel writes
  * fp32 partial results into `workspace`, a merge kernel combines them by

@@ -118,6 +118,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (B > pkv::kMaxBatch) return fail(PKV_ERR_UNSUPPORTED, "B=%d exceeds %d", B, pkv::kMaxBatch);
   if ((long long)MBS * BS > (1LL << 30))
     return fail(PKV_ERR_SHAPE, "MBS*BS=%lld is too large", (long long)MBS * BS);
+  if (B == 0) return PKV_OK;   // nothing to do; pointers may be NULL
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
   const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
@@ -285,6 +286,7 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
   if ((D != 64 && D != 128) || (BS != 16 && BS != 32) ||
       (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3FN))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d kv_dtype=%d", D, BS, kv_dtype);
+  if (N == 0) return PKV_OK;   // nothing to do; pointers may be NULL
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
   const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
