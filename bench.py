@@ -1,6 +1,11 @@
 #!/usr/bin/env python3
-"""Benchmark: one decode step = kv_append of the step's token + paged decode
-attention (partition + merge kernels), on one MI355X.
+"""Benchmark: one decode step = the append of each sequence's new token + paged
+decode attention, on one MI355X.
+
+The step is one pkv_decode_step call (the append runs inside the partition
+kernel, then the merge kernel); `--step two-call` times kv_append followed by
+pkv_paged_decode_attention instead (three launches, bit-identical results).
+Both are timed and reported; `value` is the one `--step` selects.
 
 Default workload: the Llama-3-8B-shaped layer (B=64, Hq=32, Hkv=8, D=128,
 block 16, context lengths uniform in [512, 4096], bf16 KV).  Prints ONE JSON
@@ -15,7 +20,7 @@ with a HIP event pair around every partition launch (recorded on the stream
 the kernel runs on), whose mean gives the roofline entry.  The oracle timed
 on the host cores gives the CPU baseline.
 
-  python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--config NAME] [--step fused|two-call] [--no-cpu]
 """
 from __future__ import annotations
 
@@ -120,6 +125,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--kernel", choices=["mfma", "valu"], default="mfma",
                     help="partition-kernel variant")
+    ap.add_argument("--step", choices=["fused", "two-call"], default="fused",
+                    help="decode_step (one call) or kv_append + attention (two calls)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reads 1 GiB, writes "
                          "1 GiB) a few times, to scale hardware byte counters")
@@ -160,64 +167,83 @@ def main():
     caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
     for _ in range(copies - 1):
         caches.append(tuple(None if t is None else t.clone() for t in caches[0]))
-    steps = []
+    fused, split = [], []
     for kc, vc, ks, vs in caches:
-        app = ops.PreparedAppend(wl.k_new, wl.v_new, wl.slot_mapping, kc, vc, ks, vs, stream=stream)
-        att = ops.PreparedAttention(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, out,
-                                    ks, vs, ws, stream=stream)
-        steps.append((app, att))
-    torch.cuda.synchronize()
+        fused.append(ops.PreparedStep(wl.q, wl.k_new, wl.v_new, kc, vc, wl.block_tables,
+                                      wl.context_lens, wl.scale, out, ks, vs, ws, stream=stream))
+        split.append((ops.PreparedAppend(wl.k_new, wl.v_new, wl.slot_mapping, kc, vc, ks, vs,
+                                         stream=stream),
+                      ops.PreparedAttention(wl.q, kc, vc, wl.block_tables, wl.context_lens,
+                                            wl.scale, out, ks, vs, ws, stream=stream)))
 
-    K, Wm = args.steps, args.warmup
-    with torch.cuda.stream(stream):
-        for i in range(Wm):
-            app, att = steps[i % copies]
-            app()
-            att()
-        # timed region: exactly K steps, nothing else in the stream
+    def run_fused(i):
+        fused[i % copies]()
+
+    def run_split(i):
+        app, att = split[i % copies]
+        app()
+        att()
+
+    def timed(run, first):
+        """Wall time per step of K back-to-back steps (ms)."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            app, att = steps[(Wm + i) % copies]
-            app()
-            att()
+            run(first + i)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    K, Wm = args.steps, args.warmup
+    main_run, other_run = (run_fused, run_split) if args.step == "fused" else (run_split, run_fused)
+    with torch.cuda.stream(stream):
+        for i in range(Wm):
+            other_run(i)
+        for i in range(Wm):
+            main_run(i)
+        # timed region: exactly K steps, nothing else in the stream
+        ms_per_step = timed(main_run, Wm)
+        ms_per_step_other = timed(other_run, Wm)
 
     # the same K steps again with a HIP event pair around every partition
     # launch, recorded on the stream the kernel runs on (the event records
     # themselves add a few microseconds to each bracketed launch)
+    def halves(i):
+        if args.step == "fused":
+            st = fused[i % copies]
+            return (lambda: None), st.partition, st.merge
+        app, att = split[i % copies]
+        return app, att.partition, att.merge
+
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
         t2 = time.perf_counter()
         for i in range(K):
-            app, att = steps[(Wm + i) % copies]
-            app()
+            pre, part, merge = halves(Wm + i)
+            pre()
             ev0[i].record(stream)
-            att.partition()
+            part()
             ev1[i].record(stream)
-            att.merge()
+            merge()
         torch.cuda.synchronize()
         t3 = time.perf_counter()
     ms_per_step_events = (t3 - t2) * 1e3 / K
     part_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
     part_avg_ms = float(np.mean(part_ms))
 
-    # breakdown of one step, each kernel between its own pair of events
+    # breakdown of one step, each launch between its own pair of events
     nb = min(K, 50)
     e = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
     with torch.cuda.stream(stream):
         for i in range(nb):
-            app, att = steps[i % copies]
+            pre, part, merge = halves(i)
             e[i][0].record(stream)
-            app()
+            pre()
             e[i][1].record(stream)
-            att.partition()
+            part()
             e[i][2].record(stream)
-            att.merge()
+            merge()
             e[i][3].record(stream)
     torch.cuda.synchronize()
     app_us = float(np.median([x[0].elapsed_time(x[1]) for x in e])) * 1e3
@@ -246,7 +272,8 @@ def main():
             "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.BS,
             "sum_context": int(wl.lengths.sum()), "num_blocks": wl.NB,
             "kv_bytes_per_step": nbytes, "kv_cache_copies_cycled": copies,
-            "step": "kv_append + partition + merge",
+            "step": ("decode_step: partition with the append inside + merge"
+                     if args.step == "fused" else "kv_append + partition + merge"),
         },
         "roofline": {
             "bound": "hbm",
@@ -263,7 +290,9 @@ def main():
             "partition_us_mean": round(part_avg_ms * 1e3, 2),
             "partition_us_median": round(part_med_us, 2),
             "merge_us_median": round(merge_us, 2),
-            "kv_append_us_median": round(app_us, 2),
+            "kv_append_us_median": round(app_us, 2) if args.step == "two-call" else None,
+            "ms_per_step_" + ("two_call" if args.step == "fused" else "fused"):
+                round(ms_per_step_other, 5),
             "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
             "persistent_waves": waves,
         },

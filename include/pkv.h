@@ -132,6 +132,39 @@ int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cac
                            int NB, int MBS, int kv_dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* One decode step: the append of each sequence's new token followed by
+ * attention, in one call ("tiny-vllm part 5": the new token's K/V is written
+ * into its block before attention reads the history; "Decode Phase Attention
+ * Forward Pass", sections 2-5, for the attention).  Exactly equivalent to
+ *   pkv_kv_append(k_new, v_new, slot, ...);  pkv_paged_decode_attention(...);
+ * with slot[b] = block_tables[b][(L_b - 1) / BS] * BS + (L_b - 1) % BS, the
+ * position L_b - 1 that context_lens already counts; sequences with L_b
+ * outside [1, MBS * BS] or a block id outside [0, NB) there get no append.
+ * Caches, scales and out are bit-identical to the two calls.
+ *   k_new, v_new  [B, Hkv, D] bf16, 16-byte aligned; other arguments, the
+ *   workspace and its size as for pkv_paged_decode_attention.
+ * With the MFMA partition kernel the append runs inside it: the one wave
+ * that reads position L_b - 1 of (b, kv head g) stores the row and uses it,
+ * so the step takes two launches instead of three.  The block receiving a
+ * token must not appear in another sequence's table at or past that offset
+ * (as for any append before attention).  B == 0 is a no-op. */
+int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
+                    int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* The first half of pkv_decode_step (the append and the partition kernel),
+ * same arguments; following it with pkv_paged_decode_merge on the same
+ * stream and workspace is exactly pkv_decode_step.  Exposed so that the
+ * step's partition launch can be timed on its own. */
+int pkv_decode_step_partition(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                              int NB, int MBS, int kv_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pkv_status_string(int status);
 

@@ -9,7 +9,9 @@ Two operations sit behind a C-ABI shared library (``libpkv.so``, declared in
 * ``paged_decode_attention``: one query token per sequence attends over its
   whole paged history (GQA grouping, no causal mask, exact masking of
   everything past ``context_lens``), split over the context with a
-  log-sum-exp merge.
+  log-sum-exp merge;
+* ``decode_step``: both in one call (the append runs inside the attention's
+  partition kernel), bit-identical to the two calls in sequence.
 
 The Python functions in :mod:`paged_kv_decode_06_amd.ops` only marshal
 torch tensors into the C calls; every step runs in the HIP kernels.  There is
@@ -19,6 +21,7 @@ from .ops import (  # noqa: F401
     KV_BF16,
     KV_FP8,
     PkvError,
+    decode_step,
     kv_append,
     paged_decode_attention,
     paged_decode_merge,

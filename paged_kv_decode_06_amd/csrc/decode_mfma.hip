@@ -29,6 +29,9 @@
 // n), raised only when a tile brings a larger score; the rescale of O is
 // then a wave-uniform branch.  The work split over waves is described in
 // decode_common.hpp.
+//
+// Decode step: with k_new set, the kernel also performs the one-token append
+// of each sequence (see put_new_chunk), so a step is this kernel plus the merge.
 
 #include <float.h>
 
@@ -123,10 +126,71 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
   }
 }
 
+// Decode-step append inside the partition kernel.  The tile holding
+// position L - 1 of a (sequence, kv head) is read by exactly one wave, the
+// one whose piece holds the segment's last page.  That wave stores the
+// step's new row there and writes the same values over that row of its
+// staged tile in LDS (after the tile's own rows: LDS writes of a wave land
+// in order), so it attends to what an append before the call would have
+// left; no other wave reads the row.  Lanes 0 .. LPR-1 carry the row, 16
+// cache bytes each, as the staging lanes of a row do.  The new rows are
+// read from HBM at the start of the segment, beside q, and wait in LDS, so
+// neither the common path (registers, load order) nor the append tile (no
+// load latency of its own) pays for the append.
+// fp8: a token at offset 0 opens its block and first sets the block's scale
+// (the same arithmetic as the stand-alone append).
+
+// fp8: the 16 codes of lane c's chunk (elements 16c .. 16c + 15 of the bf16
+// row at `src`, in LDS) under scale `sc`; when `opens`, `sc` is first set
+// from the whole row's amax (lanes past the row contribute zeros).
+__device__ __forceinline__ uint4 fp8_new_chunk(const unsigned char* src, bool mine, int c,
+                                               bool opens, float& sc) {
+  uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
+  if (mine) {
+    lo = *reinterpret_cast<const uint4*>(src + 32 * c);
+    hi = *reinterpret_cast<const uint4*>(src + 32 * c + 16);
+  }
+  float xl[8], xh[8];
+  unpack8(lo, xl);
+  unpack8(hi, xh);
+  if (opens) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      amax = fmaxf(amax, fmaxf(__builtin_fabsf(xl[k]), __builtin_fabsf(xh[k])));
+    sc = fp8_block_scale(wave_max(amax));
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float* x = k < 2 ? xl + 4 * k : xh + 4 * (k - 2);
+    w[k] = fp8_encode_scaled(x[0], sc) | (fp8_encode_scaled(x[1], sc) << 8) |
+           (fp8_encode_scaled(x[2], sc) << 16) | (fp8_encode_scaled(x[3], sc) << 24);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Store lane c's chunk of the new row (cache format) into the cache row
+// `dst` and over row `tr` of the staged tile.
+template <class S>
+__device__ __forceinline__ void put_new_chunk(unsigned char* dst, unsigned char* tile, int tr,
+                                              int c, const uint4 v) {
+  *reinterpret_cast<uint4*>(dst + 16 * c) = v;
+  unsigned char* t = tile + tr * S::PITCH;
+  if constexpr (S::FP8) {
+    bf16x8_t lo, hi;
+    fp8x16_to_bf16(v, lo, hi);
+    *reinterpret_cast<bf16x8_t*>(t + 32 * c) = lo;
+    *reinterpret_cast<bf16x8_t*>(t + 32 * c + 16) = hi;
+  } else {
+    *reinterpret_cast<uint4*>(t + 16 * c) = v;
+  }
+}
+
 template <class S>
 __global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU, PKV_MFMA_WAVES_PER_EU)))
 void mfma_partition_kernel(const AttnParams p) {
-  constexpr int D = S::D, BS = S::BS, G = S::G, EB = S::EB, RB = S::RB;
+  constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB;
   constexpr int NI = S::NI, RPI = S::RPI, LPR = S::LPR;
   constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
 
@@ -145,7 +209,9 @@ void mfma_partition_kernel(const AttnParams p) {
   const int wave_in_block = threadIdx.x >> 6;
   const int wave = blockIdx.x * kAttnWavesPerBlock + wave_in_block;
   const size_t pre_bytes = (sizeof(int32_t) * ((size_t)p.B + 1 + kAttnBlockThreads) + 15) & ~size_t(15);
-  unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * (16 * PITCH);
+  constexpr int WAVE_LDS = 16 * PITCH + 4 * D;   // staged tile + the new K and V rows (bf16)
+  unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * WAVE_LDS;
+  unsigned char* new_rows = tile + 16 * PITCH;     // [K row | V row], 2 D bytes each
 
   const int n = lane & 15;        // head column of S^T and O; K row of the A operand
   const int r = lane >> 4;        // 4-token group of S^T rows; 4-head group of O rows
@@ -165,7 +231,10 @@ void mfma_partition_kernel(const AttnParams p) {
   while (x < x_end) {
     const Piece pc = locate_piece(s_pre, p.B, Hkv, x, x_end);
     const int b = pc.b, g = pc.g;
-    const int L = min(max(p.context_lens[b], 0), p.MBS * BS);
+    const int L_in = p.context_lens[b];
+    const int L = min(max(L_in, 0), p.MBS * BS);
+    // a length outside [1, MBS * BS] breaks the contract: no append then
+    const bool append = p.k_new != nullptr && L == L_in && L >= 1;
     const int32_t* bt_row = p.block_tables + (int64_t)b * p.MBS;
     const int64_t head_off = (int64_t)g * RB + load_off;
 
@@ -181,6 +250,19 @@ void mfma_partition_kernel(const AttnParams p) {
         qB[kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
+    // The decode step's new rows, when this piece holds the segment's last
+    // page: loaded now, beside q, and parked in the wave's LDS slot before
+    // the first tile is staged, so the tile that takes them never waits on
+    // a load of its own.  Lane l < D / 4 carries bytes 16 l .. 16 l + 15 of
+    // [K row | V row].
+    bool park_new = append && pc.j1 == pc.n_b;
+    uint4 new_part = make_uint4(0, 0, 0, 0);
+    if (park_new && lane < D / 4) {
+      const int64_t src = ((int64_t)b * Hkv + g) * D;
+      new_part = lane < D / 8
+                     ? *reinterpret_cast<const uint4*>(p.k_new + src + 8 * lane)
+                     : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (lane - D / 8));
+    }
 
     float4_t O[NBN];
 #pragma unroll
@@ -191,40 +273,74 @@ void mfma_partition_kernel(const AttnParams p) {
     for (int jc = pc.j0; jc < pc.j1; jc += kWave) {
       const int nchunk = min(kWave, pc.j1 - jc);
       int phys_l = 0;
+      bool valid_l = false;
       if (lane < nchunk) {
         const int v = bt_row[jc + lane];
-        phys_l = ((unsigned)v < (unsigned)p.NB) ? v : 0;
+        valid_l = (unsigned)v < (unsigned)p.NB;
+        phys_l = valid_l ? v : 0;
       }
+      const uint64_t valid = __builtin_amdgcn_ballot_w64(valid_l);   // pages with a real block id
       uint4 kb[NI], vb[NI];
       float ksc = 1.0f, vsc = 1.0f;
-      // one unit = one 16-token tile: page k of the chunk, tile sb.  Each
-      // wave has the tile's K and V loads in flight while it waits; the
-      // other waves of the CU overlap their compute with those waits
-      // (measured: issuing the next tile early does not pay for the extra
-      // registers it costs).
-      auto issue = [&](int u) {
+      // one unit = one 16-token tile: page k of the chunk, tile sb.  A
+      // wave's V loads are issued only once its K loads have landed (and
+      // the other waves of the CU overlap their compute with the waits):
+      // measured, this order streams much faster than issuing both halves
+      // at once, which doubles the address streams in flight; issuing the
+      // next tile early does not pay for the registers it costs either.
+      auto tile_base = [&](int u) {
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
-        const int64_t base = ((int64_t)phys * BS + sb * 16 + load_row) * row_bytes + head_off;
+        return ((int64_t)phys * BS + sb * 16 + load_row) * row_bytes + head_off;
+      };
+      auto issue = [&](const unsigned char* __restrict__ src, int64_t base, uint4 (&ch)[NI]) {
 #pragma unroll
-        for (int s = 0; s < NI; ++s) {
-          kb[s] = load_nt(kc + base + (int64_t)s * RPI * row_bytes);
-          vb[s] = load_nt(vc + base + (int64_t)s * RPI * row_bytes);
-        }
-        if constexpr (S::FP8) {
-          ksc = p.k_scale[(int64_t)phys * Hkv + g];
-          vsc = p.v_scale[(int64_t)phys * Hkv + g];
-        }
+        for (int s = 0; s < NI; ++s) ch[s] = load_nt(src + base + (int64_t)s * RPI * row_bytes);
       };
       const int nunits = nchunk * SUB;
       for (int u = 0; u < nunits; ++u) {
-        issue(u);
         const int k = u / SUB, sb = u % SUB;
         const int tok0 = (jc + k) * BS + sb * 16;   // position of the tile's first token
         const int live = L - tok0;                  // rows of the tile inside the history
+        // the decode step's new token goes to row live - 1 of this tile
+        int new_blk = -1;
+        if (append && live >= 1 && live <= 16 && ((valid >> k) & 1))
+          new_blk = __builtin_amdgcn_readlane(phys_l, k);
+        const int64_t base = tile_base(u);
+        issue(kc, base, kb);
+        if (park_new) {
+          if (lane < D / 4) *reinterpret_cast<uint4*>(new_rows + 16 * lane) = new_part;
+          park_new = false;
+        }
+        if constexpr (S::FP8) {
+          const int phys = __builtin_amdgcn_readlane(phys_l, k);
+          ksc = p.k_scale[(int64_t)phys * Hkv + g];
+          vsc = p.v_scale[(int64_t)phys * Hkv + g];
+        }
 
         // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 heads)
         stage_tile<S>(tile, kb, lane, live, false);
+        if (new_blk >= 0) {   // K of the new token (fp8: both scales are settled here)
+          const int off = (L - 1) % BS;
+          const int64_t row = ((int64_t)new_blk * BS + off) * row_bytes + (int64_t)g * RB;
+          const unsigned char* src = new_rows;
+          uint4 v;
+          if constexpr (S::FP8) {
+            v = fp8_new_chunk(src, lane < LPR, lane, off == 0, ksc);
+            if (off == 0) {
+              fp8_new_chunk(new_rows + 2 * D, lane < LPR, lane, true, vsc);
+              if (lane == 0) {
+                p.k_scale_w[(int64_t)new_blk * Hkv + g] = ksc;
+                p.v_scale_w[(int64_t)new_blk * Hkv + g] = vsc;
+              }
+            }
+          } else {
+            if (lane < LPR) v = *reinterpret_cast<const uint4*>(src + 16 * lane);
+          }
+          if (lane < LPR) put_new_chunk<S>(p.k_cache_w + row, tile, live - 1, lane, v);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the V loads behind the K wait
+        issue(vc, base, vb);
         float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -266,6 +382,18 @@ void mfma_partition_kernel(const AttnParams p) {
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
         // order within a wave) -> transposed B operands, O += P V
         stage_tile<S>(tile, vb, lane, live, true);
+        if (new_blk >= 0) {   // V of the new token
+          const int off = (L - 1) % BS;
+          const int64_t row = ((int64_t)new_blk * BS + off) * row_bytes + (int64_t)g * RB;
+          const unsigned char* src = new_rows + 2 * D;
+          uint4 v;
+          if constexpr (S::FP8) {
+            v = fp8_new_chunk(src, lane < LPR, lane, false, vsc);
+          } else {
+            if (lane < LPR) v = *reinterpret_cast<const uint4*>(src + 16 * lane);
+          }
+          if (lane < LPR) put_new_chunk<S>(p.v_cache_w + row, tile, live - 1, lane, v);
+        }
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
           // (C-style cast: generic -> LDS address space)
@@ -319,7 +447,7 @@ void mfma_partition_kernel(const AttnParams p) {
 }  // namespace
 
 size_t mfma_stage_lds_bytes(int D) {
-  return (size_t)kAttnWavesPerBlock * 16 * (2 * D + 32);
+  return (size_t)kAttnWavesPerBlock * (16 * (2 * D + 32) + 4 * D);
 }
 
 static size_t mfma_lds_total(int B, int D) {

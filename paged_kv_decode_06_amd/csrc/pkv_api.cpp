@@ -106,7 +106,8 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
                       const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
                       int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
-                      size_t workspace_bytes, AttnCall* call) {
+                      size_t workspace_bytes, AttnCall* call, bool step = false,
+                      const void* k_new = nullptr, const void* v_new = nullptr) {
   g_last_error.clear();
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0 || MBS <= 0)
     return fail(PKV_ERR_SHAPE, "sizes must be positive (B may be 0): B=%d Hq=%d Hkv=%d D=%d BS=%d NB=%d MBS=%d",
@@ -121,11 +122,14 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (B == 0) return PKV_OK;   // nothing to do; pointers may be NULL
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
+  if (step && (!k_new || !v_new)) return fail(PKV_ERR_NULL, "k_new and v_new are required");
   const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
   if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
   if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
+  if (step && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
   if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
   const int blocks = attention_blocks(D, BS, G, kv_dtype, B);
@@ -157,6 +161,12 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   p.ws_o = reinterpret_cast<float*>(ws + lay.o_off);
+  p.k_new = nullptr;
+  p.v_new = nullptr;
+  p.k_cache_w = nullptr;
+  p.v_cache_w = nullptr;
+  p.k_scale_w = nullptr;
+  p.v_scale_w = nullptr;
   call->D = D;
   call->BS = BS;
   call->G = G;
@@ -276,6 +286,72 @@ int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// The decode step's launches: the first half (append + partition) and, when
+// `merge`, the log-sum-exp merge.
+int decode_step_impl(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
+                     const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
+                     int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                     size_t workspace_bytes, void* stream, bool merge) {
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call, true, k_new, v_new);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (pkv::attn_path() == pkv::AttnPath::kMfma) {
+    pkv::AttnParams& p = call.p;
+    p.k_new = static_cast<const uint16_t*>(k_new);
+    p.v_new = static_cast<const uint16_t*>(v_new);
+    p.k_cache_w = static_cast<unsigned char*>(k_cache);
+    p.v_cache_w = static_cast<unsigned char*>(v_cache);
+    p.k_scale_w = k_scale;
+    p.v_scale_w = v_scale;
+    e = launch_partition(call, s);
+    if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  } else {
+    e = pkv::launch_kv_append(k_new, v_new, nullptr, block_tables, context_lens, MBS, k_cache,
+                              v_cache, k_scale, v_scale, B, Hkv, D, BS, NB, call.fp8, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_append kernel launch");
+    e = launch_partition(call, s);
+    if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  }
+  if (!merge) return PKV_OK;
+  e = pkv::launch_merge(call.p, call.D, call.G, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                    void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
+                    const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
+                    int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_step_impl(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                          context_lens, scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype,
+                          workspace, workspace_bytes, stream, true);
+}
+
+int pkv_decode_step_partition(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
+                              int NB, int MBS, int kv_dtype, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_step_impl(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                          context_lens, scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype,
+                          workspace, workspace_bytes, stream, false);
+}
+
 int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                   void* k_cache, void* v_cache, float* k_scale, float* v_scale, int N, int Hkv,
                   int D, int BS, int NB, int kv_dtype, void* stream) {
@@ -295,8 +371,8 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
   if (!fp8 && (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)))
     return fail(PKV_ERR_ALIGN, "k_new, v_new and the caches must be 16-byte aligned");
   if (N == 0) return PKV_OK;
-  hipError_t e = pkv::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale,
-                                       v_scale, N, Hkv, D, BS, NB, fp8,
+  hipError_t e = pkv::launch_kv_append(k_new, v_new, slot_mapping, nullptr, nullptr, 0, k_cache,
+                                       v_cache, k_scale, v_scale, N, Hkv, D, BS, NB, fp8,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_append kernel launch");
 }

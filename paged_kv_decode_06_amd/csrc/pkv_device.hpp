@@ -70,6 +70,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn_rne_sat(float y) {
   return sign | (exp8 << 3) | man3;
 }
 
+// Scale of a block that a new token opens: amax / 448 in fp32 (correctly
+// rounded division), or 1 when the token is all zeros.  Elements are then
+// stored as e4m3fn(x / scale).  Both append paths use exactly this.
+__device__ __forceinline__ float fp8_block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+__device__ __forceinline__ uint32_t fp8_encode_scaled(float x, float scale) {
+  return f32_to_e4m3fn_rne_sat(__fdiv_rn(x, scale));
+}
+
 // ---- cross-lane reductions (DPP within a 16-lane row) -----------------------
 
 template <int CTRL>

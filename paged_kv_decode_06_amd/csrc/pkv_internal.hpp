@@ -26,6 +26,16 @@ struct AttnParams {
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
   float* ws_ml;         // [rows, G, 2] running max (log2 domain) and sum
   float* ws_o;          // [rows, G, D] unnormalised partial outputs
+  // Fused append (the decode step): when k_new is non-NULL, the new token of
+  // sequence b ([B, Hkv, D] bf16) is stored at position context_lens[b] - 1
+  // by the wave that reads that position, which also attends to it.  The
+  // writable views alias k_cache / v_cache / k_scale / v_scale.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  unsigned char* k_cache_w;
+  unsigned char* v_cache_w;
+  float* k_scale_w;
+  float* v_scale_w;
 };
 
 struct WorkspaceLayout {
@@ -81,7 +91,11 @@ std::atomic<int>& path_flag();
 
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
 
+// One-token append.  With `slots` NULL the slot of token i is derived from
+// the block table instead: position context_lens[i] - 1 of sequence i
+// (block_tables is [N, MBS]); a length outside [1, MBS * BS] skips the token.
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slots,
+                            const int32_t* block_tables, const int32_t* context_lens, int MBS,
                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                             int N, int Hkv, int D, int BS, int NB, bool fp8, hipStream_t stream);
 

@@ -60,6 +60,10 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = I
+        for name in ("pkv_decode_step", "pkv_decode_step_partition"):
+            fn = getattr(lib, name)
+            fn.argtypes = [P, P, P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
+            fn.restype = I
         lib.pkv_status_string.argtypes = [I]
         lib.pkv_status_string.restype = ctypes.c_char_p
         lib.pkv_last_error.argtypes = []
@@ -210,6 +214,52 @@ def paged_decode_merge(q, k_cache, v_cache, block_tables, context_lens, scale, o
     args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
                       v_scale, workspace, stream)
     _check("pkv_paged_decode_merge", _load().pkv_paged_decode_merge(*args))
+
+
+def _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+               k_scale, v_scale, workspace, stream):
+    a = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
+                   workspace, stream)
+    _need(k_new, "k_new", torch.bfloat16, 3)
+    _need(v_new, "v_new", torch.bfloat16, 3)
+    B, Hkv, D = q.shape[0], k_cache.shape[2], q.shape[2]
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    # (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, ...)
+    return (a[0], _ptr(k_new), _ptr(v_new)) + a[1:]
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                k_scale=None, v_scale=None, workspace=None, stream=None) -> None:
+    """pkv_decode_step: append each sequence's new token at position
+    context_lens[b] - 1, then attend (one call, bit-identical to kv_append
+    followed by paged_decode_attention)."""
+    args = _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                      k_scale, v_scale, workspace, stream)
+    _check("pkv_decode_step", _load().pkv_decode_step(*args))
+
+
+class PreparedStep:
+    """decode_step with its arguments marshalled once (see PreparedAttention)."""
+
+    def __init__(self, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                 k_scale=None, v_scale=None, workspace=None, stream=None):
+        self._args = _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                scale, out, k_scale, v_scale, workspace, stream)
+        a = self._args
+        self._merge_args = (a[0],) + a[3:]     # the attention call's arguments
+        self._lib = _load()
+
+    def __call__(self):
+        _check("pkv_decode_step", self._lib.pkv_decode_step(*self._args))
+
+    def partition(self):
+        """First half: the append and the partition kernel."""
+        _check("pkv_decode_step_partition", self._lib.pkv_decode_step_partition(*self._args))
+
+    def merge(self):
+        """Second half: the merge kernel."""
+        _check("pkv_paged_decode_merge", self._lib.pkv_paged_decode_merge(*self._merge_args))
 
 
 class PreparedAttention:

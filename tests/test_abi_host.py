@@ -94,3 +94,26 @@ def test_kv_append_argument_checks(lib):
     assert f(*bad) == -6
     zero = list(ok); zero[7] = 0                    # N = 0: nothing to do
     assert f(*zero) == 0
+
+
+def test_decode_step_argument_checks(lib):
+    P = ctypes.c_void_p
+
+    def step(**over):
+        a = dict(q=8, kn=16, vn=32, k=48, v=64, bt=80, cl=96, out=112, B=2, Hq=8, Hkv=2, D=64,
+                 BS=16, NB=4, MBS=2, kv=0)
+        a.update(over)
+        p = lambda x: P(x) if x else None  # noqa: E731
+        return lib.pkv_decode_step(p(a["q"]), p(a["kn"]), p(a["vn"]), p(a["k"]), p(a["v"]),
+                                   None, None, p(a["bt"]), p(a["cl"]), ctypes.c_float(0.125),
+                                   p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["BS"],
+                                   a["NB"], a["MBS"], a["kv"], P(128), ctypes.c_size_t(1 << 20),
+                                   None)
+
+    assert step(kn=0) == -1                        # the new token is required
+    assert step(vn=0) == -1
+    assert step(q=0) == -1
+    assert step(kn=17) == -6                       # misaligned new token
+    assert step(D=96) == -3
+    assert step(Hq=6, Hkv=4) == -2
+    assert step(B=0, q=0, kn=0, vn=0) == 0         # empty batch: nothing to do

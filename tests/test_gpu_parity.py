@@ -219,10 +219,9 @@ def test_full_configuration_sampled(name, kernel):
 
 
 def test_repeated_calls_reuse_the_workspace_and_are_deterministic(kernel):
-    """Waves claim the tail of the work from a counter in the workspace; the
-    merge kernel clears it.  Chunk boundaries and partial rows do not depend
-    on which wave claims what, so repeated calls on one workspace give the
-    same bits, and the counter is zero after every call."""
+    """The split of the work over waves is a pure function of the lengths,
+    so repeated calls on one workspace (left holding the previous call's
+    partial results) give the same bits."""
     wl = build(16, 32, 8, 128, 16, np.random.default_rng(4).integers(200, 3000, 16), seed=11,
                poison=False)
     ws = GS.workspace_for(wl)
@@ -230,8 +229,6 @@ def test_repeated_calls_reuse_the_workspace_and_are_deterministic(kernel):
     for _ in range(3):
         again = GS.gpu_step(wl, workspace=ws, append=False)
         assert torch.equal(again.view(torch.int16), first.view(torch.int16))
-        torch.cuda.synchronize()
-        assert int(ws[:4].view(torch.int32).item()) == 0
 
 
 def test_many_rows_small_lengths(kernel):
