@@ -31,7 +31,7 @@
 // decode_common.hpp.
 //
 // Decode step: with k_new set, the kernel also performs the one-token append
-// of each sequence (see put_new_chunk), so a step is this kernel plus the merge.
+// of each sequence (see park_new_rows), so a step is this kernel plus the merge.
 
 #include <float.h>
 
@@ -64,6 +64,7 @@ struct MfmaShape {
   static constexpr int NBN = D / 16;          // output n-blocks (16x16x16)
   static constexpr int SUB = BS / 16;         // 16-token tiles per page
   static constexpr int PITCH = 2 * D + 32;    // LDS row pitch (bytes) of a bf16 tile
+  static constexpr bool KV_TOGETHER = 16 * RB <= 2048;   // issue a tile's K and V loads at once
   static_assert(G >= 1 && G <= 16, "the group is the 16-wide N dimension");
   static_assert(NI >= 1 && BS % 16 == 0, "shape");
 };
@@ -128,63 +129,93 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
 
 // Decode-step append inside the partition kernel.  The tile holding
 // position L - 1 of a (sequence, kv head) is read by exactly one wave, the
-// one whose piece holds the segment's last page.  That wave stores the
-// step's new row there and writes the same values over that row of its
+// one whose piece holds the run's last page.  That wave stores the step's
+// new row in the cache and writes the same values over that row of its
 // staged tile in LDS (after the tile's own rows: LDS writes of a wave land
 // in order), so it attends to what an append before the call would have
-// left; no other wave reads the row.  Lanes 0 .. LPR-1 carry the row, 16
-// cache bytes each, as the staging lanes of a row do.  The new rows are
-// read from HBM at the start of the segment, beside q, and wait in LDS, so
-// neither the common path (registers, load order) nor the append tile (no
-// load latency of its own) pays for the append.
-// fp8: a token at offset 0 opens its block and first sets the block's scale
-// (the same arithmetic as the stand-alone append).
+// left; no other wave reads the row.  All the work is done early: the new
+// rows are loaded beside q at the start of the run, and when the first tile
+// of the chunk holding the last page has its loads in flight, the rows are
+// encoded (fp8), stored to the cache and parked in the wave's LDS slot in
+// tile format, hidden behind that tile's load latency; the tile holding
+// position L - 1 then only copies two rows within LDS.
+// fp8: a token at offset 0 opens its block and sets the block's scale to
+// amax / 448 first; otherwise the block keeps its scale (the same arithmetic
+// as the stand-alone append).
 
-// fp8: the 16 codes of lane c's chunk (elements 16c .. 16c + 15 of the bf16
-// row at `src`, in LDS) under scale `sc`; when `opens`, `sc` is first set
-// from the whole row's amax (lanes past the row contribute zeros).
-__device__ __forceinline__ uint4 fp8_new_chunk(const unsigned char* src, bool mine, int c,
-                                               bool opens, float& sc) {
-  uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-  if (mine) {
-    lo = *reinterpret_cast<const uint4*>(src + 32 * c);
-    hi = *reinterpret_cast<const uint4*>(src + 32 * c + 16);
-  }
-  float xl[8], xh[8];
-  unpack8(lo, xl);
-  unpack8(hi, xh);
-  if (opens) {
-    float amax = 0.0f;
+// 8 e4m3fn codes -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const uint2 c) {
+  bf16x8_t r;
+  const uint32_t w[2] = {c.x, c.y};
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      amax = fmaxf(amax, fmaxf(__builtin_fabsf(xl[k]), __builtin_fabsf(xh[k])));
-    sc = fp8_block_scale(wave_max(amax));
+  for (int k = 0; k < 2; ++k) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+    r[4 * k + 0] = (__bf16)a[0];
+    r[4 * k + 1] = (__bf16)a[1];
+    r[4 * k + 2] = (__bf16)b[0];
+    r[4 * k + 3] = (__bf16)b[1];
   }
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float* x = k < 2 ? xl + 4 * k : xh + 4 * (k - 2);
-    w[k] = fp8_encode_scaled(x[0], sc) | (fp8_encode_scaled(x[1], sc) << 8) |
-           (fp8_encode_scaled(x[2], sc) << 16) | (fp8_encode_scaled(x[3], sc) << 24);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return r;
 }
 
-// Store lane c's chunk of the new row (cache format) into the cache row
-// `dst` and over row `tr` of the staged tile.
+// Park the new K and V rows of kv head g in the wave's LDS slot `rows`
+// ([K | V], 2 D bytes each, tile format) and store them in the cache rows
+// `kdst` / `vdst`.  Lane l < D / 4 holds `part`, the bf16 elements
+// 8 l' .. 8 l' + 7 of the K row (l < D / 8, l' = l) or of the V row
+// (l' = l - D / 8).  fp8: `sk` / `sv` come in as the block's scales and
+// leave as the scales after the append (set from the rows when `opens`;
+// lane 0 then stores them at `skw` / `svw`).
 template <class S>
-__device__ __forceinline__ void put_new_chunk(unsigned char* dst, unsigned char* tile, int tr,
-                                              int c, const uint4 v) {
-  *reinterpret_cast<uint4*>(dst + 16 * c) = v;
-  unsigned char* t = tile + tr * S::PITCH;
+__device__ __forceinline__ void park_new_rows(const uint4 part, int lane, unsigned char* rows,
+                                              unsigned char* kdst, unsigned char* vdst,
+                                              bool opens, float& sk, float& sv, float* skw,
+                                              float* svw) {
+  constexpr int D = S::D;
+  const bool is_k = lane < D / 8;
+  const bool mine = lane < D / 4;
+  const int c = is_k ? lane : lane - D / 8;
   if constexpr (S::FP8) {
-    bf16x8_t lo, hi;
-    fp8x16_to_bf16(v, lo, hi);
-    *reinterpret_cast<bf16x8_t*>(t + 32 * c) = lo;
-    *reinterpret_cast<bf16x8_t*>(t + 32 * c + 16) = hi;
+    float x[8];
+    unpack8(part, x);   // lanes past the rows hold zeros
+    if (opens) {
+      float am = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, __builtin_fabsf(x[e]));
+      const float amk = wave_max(is_k ? am : 0.0f);
+      const float amv = wave_max(is_k ? 0.0f : am);
+      sk = fp8_block_scale(amk);
+      sv = fp8_block_scale(amv);
+      if (lane == 0) {
+        *skw = sk;
+        *svw = sv;
+      }
+    }
+    const float sc = is_k ? sk : sv;
+    uint2 codes;
+    codes.x = fp8_encode_scaled(x[0], sc) | (fp8_encode_scaled(x[1], sc) << 8) |
+              (fp8_encode_scaled(x[2], sc) << 16) | (fp8_encode_scaled(x[3], sc) << 24);
+    codes.y = fp8_encode_scaled(x[4], sc) | (fp8_encode_scaled(x[5], sc) << 8) |
+              (fp8_encode_scaled(x[6], sc) << 16) | (fp8_encode_scaled(x[7], sc) << 24);
+    if (mine) {
+      *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes;
+      *reinterpret_cast<bf16x8_t*>(rows + 16 * lane) = fp8x8_to_bf16(codes);
+    }
   } else {
-    *reinterpret_cast<uint4*>(t + 16 * c) = v;
+    if (mine) {
+      *reinterpret_cast<uint4*>((is_k ? kdst : vdst) + 16 * c) = part;
+      *reinterpret_cast<uint4*>(rows + 16 * lane) = part;
+    }
   }
+}
+
+// Copy a parked row (2 D bytes in tile format) over row `tr` of the tile.
+template <class S>
+__device__ __forceinline__ void take_new_row(const unsigned char* row, unsigned char* tile, int tr,
+                                             int lane) {
+  if (lane < S::D / 8)
+    *reinterpret_cast<uint4*>(tile + tr * S::PITCH + 16 * lane) =
+        *reinterpret_cast<const uint4*>(row + 16 * lane);
 }
 
 template <class S>
@@ -250,19 +281,17 @@ void mfma_partition_kernel(const AttnParams p) {
         qB[kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    // The decode step's new rows, when this piece holds the segment's last
-    // page: loaded now, beside q, and parked in the wave's LDS slot before
-    // the first tile is staged, so the tile that takes them never waits on
-    // a load of its own.  Lane l < D / 4 carries bytes 16 l .. 16 l + 15 of
-    // [K row | V row].
-    bool park_new = append && pc.j1 == pc.n_b;
+    // The decode step's new rows when this piece holds the run's last page
+    // (loaded beside q; lane l < D / 4 takes 16 bytes of [K row | V row]).
+    const bool has_new = append && pc.j1 == pc.n_b;
     uint4 new_part = make_uint4(0, 0, 0, 0);
-    if (park_new && lane < D / 4) {
+    if (has_new && lane < D / 4) {
       const int64_t src = ((int64_t)b * Hkv + g) * D;
       new_part = lane < D / 8
                      ? *reinterpret_cast<const uint4*>(p.k_new + src + 8 * lane)
                      : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (lane - D / 8));
     }
+    float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8: the last block's scales after the append
 
     float4_t O[NBN];
 #pragma unroll
@@ -280,14 +309,17 @@ void mfma_partition_kernel(const AttnParams p) {
         phys_l = valid_l ? v : 0;
       }
       const uint64_t valid = __builtin_amdgcn_ballot_w64(valid_l);   // pages with a real block id
+      const int k_last = pc.n_b - 1 - jc;             // the run's last page in this chunk, if < nchunk
+      const bool new_here = has_new && k_last < nchunk && ((valid >> k_last) & 1);
       uint4 kb[NI], vb[NI];
       float ksc = 1.0f, vsc = 1.0f;
-      // one unit = one 16-token tile: page k of the chunk, tile sb.  A
-      // wave's V loads are issued only once its K loads have landed (and
-      // the other waves of the CU overlap their compute with the waits):
-      // measured, this order streams much faster than issuing both halves
-      // at once, which doubles the address streams in flight; issuing the
-      // next tile early does not pay for the registers it costs either.
+      // one unit = one 16-token tile: page k of the chunk, tile sb.  Bytes
+      // in flight per wave: a 4 KB half tile (bf16, D = 128) is enough on
+      // its own, so its V loads are issued only once the K loads have
+      // landed (issuing both at once measured ~7% slower); 2 KB halves
+      // (fp8, or D = 64) issue K and V together (~3% faster than in turn).
+      // The other waves of the CU overlap their compute with the waits;
+      // issuing the next tile early does not pay for the registers it costs.
       auto tile_base = [&](int u) {
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
@@ -303,14 +335,23 @@ void mfma_partition_kernel(const AttnParams p) {
         const int tok0 = (jc + k) * BS + sb * 16;   // position of the tile's first token
         const int live = L - tok0;                  // rows of the tile inside the history
         // the decode step's new token goes to row live - 1 of this tile
-        int new_blk = -1;
-        if (append && live >= 1 && live <= 16 && ((valid >> k) & 1))
-          new_blk = __builtin_amdgcn_readlane(phys_l, k);
+        const bool new_tile = new_here && k == k_last && live >= 1 && live <= 16;
         const int64_t base = tile_base(u);
         issue(kc, base, kb);
-        if (park_new) {
-          if (lane < D / 4) *reinterpret_cast<uint4*>(new_rows + 16 * lane) = new_part;
-          park_new = false;
+        if constexpr (S::KV_TOGETHER) issue(vc, base, vb);
+        if (new_here && u == 0) {   // park the new rows while this tile's loads fly
+          const int blk = __builtin_amdgcn_readlane(phys_l, k_last);
+          const int off = (L - 1) % BS;
+          const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g * RB;
+          const int64_t sslot = (int64_t)blk * Hkv + g;
+          if constexpr (S::FP8) {
+            if (off != 0) {
+              new_ksc = p.k_scale[sslot];
+              new_vsc = p.v_scale[sslot];
+            }
+          }
+          park_new_rows<S>(new_part, lane, new_rows, p.k_cache_w + row, p.v_cache_w + row,
+                           off == 0, new_ksc, new_vsc, p.k_scale_w + sslot, p.v_scale_w + sslot);
         }
         if constexpr (S::FP8) {
           const int phys = __builtin_amdgcn_readlane(phys_l, k);
@@ -320,27 +361,17 @@ void mfma_partition_kernel(const AttnParams p) {
 
         // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 heads)
         stage_tile<S>(tile, kb, lane, live, false);
-        if (new_blk >= 0) {   // K of the new token (fp8: both scales are settled here)
-          const int off = (L - 1) % BS;
-          const int64_t row = ((int64_t)new_blk * BS + off) * row_bytes + (int64_t)g * RB;
-          const unsigned char* src = new_rows;
-          uint4 v;
+        if (new_tile) {
+          take_new_row<S>(new_rows, tile, live - 1, lane);
           if constexpr (S::FP8) {
-            v = fp8_new_chunk(src, lane < LPR, lane, off == 0, ksc);
-            if (off == 0) {
-              fp8_new_chunk(new_rows + 2 * D, lane < LPR, lane, true, vsc);
-              if (lane == 0) {
-                p.k_scale_w[(int64_t)new_blk * Hkv + g] = ksc;
-                p.v_scale_w[(int64_t)new_blk * Hkv + g] = vsc;
-              }
-            }
-          } else {
-            if (lane < LPR) v = *reinterpret_cast<const uint4*>(src + 16 * lane);
+            ksc = new_ksc;
+            vsc = new_vsc;
           }
-          if (lane < LPR) put_new_chunk<S>(p.k_cache_w + row, tile, live - 1, lane, v);
         }
-        __builtin_amdgcn_sched_barrier(0);   // keep the V loads behind the K wait
-        issue(vc, base, vb);
+        if constexpr (!S::KV_TOGETHER) {
+          __builtin_amdgcn_sched_barrier(0);   // keep the V loads behind the K wait
+          issue(vc, base, vb);
+        }
         float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -382,18 +413,7 @@ void mfma_partition_kernel(const AttnParams p) {
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
         // order within a wave) -> transposed B operands, O += P V
         stage_tile<S>(tile, vb, lane, live, true);
-        if (new_blk >= 0) {   // V of the new token
-          const int off = (L - 1) % BS;
-          const int64_t row = ((int64_t)new_blk * BS + off) * row_bytes + (int64_t)g * RB;
-          const unsigned char* src = new_rows + 2 * D;
-          uint4 v;
-          if constexpr (S::FP8) {
-            v = fp8_new_chunk(src, lane < LPR, lane, false, vsc);
-          } else {
-            if (lane < LPR) v = *reinterpret_cast<const uint4*>(src + 16 * lane);
-          }
-          if (lane < LPR) put_new_chunk<S>(p.v_cache_w + row, tile, live - 1, lane, v);
-        }
+        if (new_tile) take_new_row<S>(new_rows + 2 * D, tile, live - 1, lane);
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
           // (C-style cast: generic -> LDS address space)
