@@ -36,6 +36,32 @@
  *    fp32.  A token landing in an already-open block keeps the block's
  *    scale and saturates.
  *
+ *  - INT8 KV (the same glossary: the KV cache may be quantised to INT8, with
+ *    dequantisation in the attention kernel; the pages fix no format, so the
+ *    plainest symmetric one is taken): one fp32 scale per (block, kv head);
+ *    a token that opens a block sets it to amax|x| / 127 (1.0 if amax is 0);
+ *    every element is stored as the int8 code clamp(rint(x / scale), -127,
+ *    127), x / scale in fp32 and rint rounding halves to even; the value is
+ *    code * scale.
+ *
+ *  - Generalised attention ("Prefill Forward Prefix Caching Explained",
+ *    section on the bottom-right causal mask; the "Decode Phase" glossary's
+ *    sliding-window and attention-sink bullets): sequence b has q_len_b
+ *    query tokens, the last q_len_b of its L_b = context_lens[b] positions.
+ *    Query i (0 <= i < q_len_b) sees key j iff j <= lim = L_b - q_len_b + i
+ *    and, when a window W > 0 is given, also j > lim - W or j < S (the first
+ *    S "sink" tokens stay visible).  q_len_b = 1 with no window is the
+ *    decode attention above.
+ *
+ *  - RoPE ("tiny-vllm part 5", section "RoPE: one current position,
+ *    recomputed on every call"): the pair (x[2i], x[2i+1]) of every head is
+ *    rotated by the angle pos * f_i, with f_i = theta^(-2i/D) scaled as the
+ *    Llama 3 table path scales it (frequencies whose wavelength exceeds
+ *    original_max / low_freq_factor are divided by `factor`; between that and
+ *    original_max / high_freq_factor they are blended linearly in
+ *    original_max / wavelength).  Everything in fp64; the rotated vector is
+ *    rounded to bf16 (nearest even), as the model's K and Q would be stored.
+ *
  * Layouts (all row-major, contiguous):
  *   q, out            [B, Hq, D]         q is bf16 bits, out is fp64
  *   k_cache, v_cache  [NB, BS, Hkv, D]   bf16 bits or e4m3fn bytes
@@ -55,6 +81,7 @@
 
 #define PKVO_KV_BF16 0
 #define PKVO_KV_FP8 1
+#define PKVO_KV_INT8 2
 
 #define PKVO_OK 0
 #define PKVO_ERR_NULL (-1)
@@ -126,14 +153,31 @@ void pkvo_e4m3fn_encode_array(const float* x, uint8_t* codes, int64_t n) {
   for (int64_t i = 0; i < n; ++i) codes[i] = pkvo_e4m3fn_from_f32(x[i]);
 }
 
+/* INT8: the code of a binary32 quotient y: nearest integer, halves to even
+ * (the C library's rint in the default rounding mode), clamped to
+ * [-127, 127]; NaN gives 0 (the oracle is never fed NaN). */
+int8_t pkvo_int8_from_f32(float y) {
+  if (isnan(y)) return 0;
+  double r = rint((double)y); /* y is exact in double, so this rounds y itself */
+  if (r > 127.0) r = 127.0;
+  if (r < -127.0) r = -127.0;
+  return (int8_t)r;
+}
+
 /* ---- attention ------------------------------------------------------------ */
 
 static double load_kv(const void* cache, const float* scales, int kv_dtype,
                       size_t row, int d, size_t scale_idx) {
   if (kv_dtype == PKVO_KV_BF16)
     return pkvo_bf16_to_f64(((const uint16_t*)cache)[row + (size_t)d]);
+  if (kv_dtype == PKVO_KV_INT8)
+    return (double)((const int8_t*)cache)[row + (size_t)d] * (double)scales[scale_idx];
   return pkvo_e4m3fn_to_f64(((const uint8_t*)cache)[row + (size_t)d]) *
          (double)scales[scale_idx];
+}
+
+static int valid_dtype(int kv_dtype) {
+  return kv_dtype == PKVO_KV_BF16 || kv_dtype == PKVO_KV_FP8 || kv_dtype == PKVO_KV_INT8;
 }
 
 /* out[b, h, :] for every sequence b and query head h.  If `weights` is not
@@ -152,8 +196,8 @@ int pkvo_paged_decode_attention(const uint16_t* q, const void* k_cache,
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0 || MBS <= 0 ||
       Hq % Hkv != 0)
     return PKVO_ERR_SHAPE;
-  if (kv_dtype != PKVO_KV_BF16 && kv_dtype != PKVO_KV_FP8) return PKVO_ERR_SHAPE;
-  if (kv_dtype == PKVO_KV_FP8 && (!k_scale || !v_scale)) return PKVO_ERR_NULL;
+  if (!valid_dtype(kv_dtype)) return PKVO_ERR_SHAPE;
+  if (kv_dtype != PKVO_KV_BF16 && (!k_scale || !v_scale)) return PKVO_ERR_NULL;
   for (int b = 0; b < B; ++b) {
     int L = context_lens[b];
     if (L > MBS * BS) return PKVO_ERR_SHAPE;
@@ -231,6 +275,116 @@ int pkvo_paged_decode_attention(const uint16_t* q, const void* k_cache,
   return status;
 }
 
+/* Generalised attention: out[r, h, :] for every query row r and head h.
+ * q_start == NULL: one query per sequence, row b (q_len_b = 1).  Otherwise
+ * sequence b owns rows q_start[b] .. q_start[b+1]-1.  Query i of sequence b
+ * sees key j iff j <= lim = L - q_len + i and (window <= 0 || j > lim - window
+ * || j < sinks).  A query that sees no key gets out = 0.  `weights`, if not
+ * NULL, is [total_q, Hq, MBS*BS] and receives the weight of every position.
+ * The softmax is the plain two-pass definition over the visible keys. */
+int pkvo_paged_attention(const uint16_t* q, const int32_t* q_start, const void* k_cache,
+                         const void* v_cache, const float* k_scale, const float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         int sinks, int window, double* out, double* weights, int B, int Hq,
+                         int Hkv, int D, int BS, int NB, int MBS, int kv_dtype, int nthreads) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PKVO_ERR_NULL;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0 || MBS <= 0 ||
+      Hq % Hkv != 0 || sinks < 0)
+    return PKVO_ERR_SHAPE;
+  if (!valid_dtype(kv_dtype)) return PKVO_ERR_SHAPE;
+  if (kv_dtype != PKVO_KV_BF16 && (!k_scale || !v_scale)) return PKVO_ERR_NULL;
+  for (int b = 0; b < B; ++b) {
+    const int L = context_lens[b];
+    const int ql = q_start ? q_start[b + 1] - q_start[b] : 1;
+    if (L > MBS * BS || ql < 0) return PKVO_ERR_SHAPE;
+    for (int t = 0; t < L; t += BS) {
+      int p = block_tables[(size_t)b * MBS + t / BS];
+      if (p < 0 || p >= NB) return PKVO_ERR_SHAPE;
+    }
+  }
+  const int G = Hq / Hkv;
+  const int n_units = B * Hkv;
+  int status = PKVO_OK;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int u = 0; u < n_units; ++u) {
+    const int b = u / Hkv;
+    const int g = u % Hkv;
+    const int L = context_lens[b] > 0 ? context_lens[b] : 0;
+    const int r0 = q_start ? q_start[b] : b;
+    const int ql = q_start ? q_start[b + 1] - q_start[b] : 1;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    char* vis = (char*)malloc((size_t)(L > 0 ? L : 1));
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!s || !vis || !acc) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      status = PKVO_ERR_NOMEM;
+      free(s);
+      free(vis);
+      free(acc);
+      continue;
+    }
+    for (int i = 0; i < ql; ++i) {
+      const int lim = L - ql + i; /* bottom-right aligned causal limit */
+      int any = 0;
+      for (int t = 0; t < L; ++t) {
+        int v = t <= lim;
+        if (v && window > 0) v = (t > lim - window) || (t < sinks);
+        vis[t] = (char)v;
+        any |= v;
+      }
+      for (int j = 0; j < G; ++j) {
+        const int h = g * G + j;
+        const size_t rh = (size_t)(r0 + i) * Hq + h;
+        const uint16_t* qh = q + rh * D;
+        double* oh = out + rh * D;
+        if (!any) {
+          for (int d = 0; d < D; ++d) oh[d] = 0.0;
+          continue;
+        }
+        double m = -INFINITY;
+        for (int t = 0; t < L; ++t) {
+          if (!vis[t]) continue;
+          const int p = block_tables[(size_t)b * MBS + t / BS];
+          const size_t row = (((size_t)p * BS + t % BS) * Hkv + g) * D;
+          const size_t si = (size_t)p * Hkv + g;
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d)
+            dot += pkvo_bf16_to_f64(qh[d]) * load_kv(k_cache, k_scale, kv_dtype, row, d, si);
+          s[t] = (double)scale * dot;
+          if (s[t] > m) m = s[t];
+        }
+        double Z = 0.0;
+        for (int t = 0; t < L; ++t) {
+          if (!vis[t]) continue;
+          s[t] = exp(s[t] - m);
+          Z += s[t];
+        }
+        for (int d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int t = 0; t < L; ++t) {
+          if (!vis[t]) continue;
+          const int p = block_tables[(size_t)b * MBS + t / BS];
+          const size_t row = (((size_t)p * BS + t % BS) * Hkv + g) * D;
+          const size_t si = (size_t)p * Hkv + g;
+          const double w = s[t] / Z;
+          if (weights) weights[rh * ((size_t)MBS * BS) + t] = w;
+          for (int d = 0; d < D; ++d) acc[d] += w * load_kv(v_cache, v_scale, kv_dtype, row, d, si);
+        }
+        for (int d = 0; d < D; ++d) oh[d] = acc[d];
+      }
+    }
+    free(s);
+    free(vis);
+    free(acc);
+  }
+  return status;
+}
+
 /* ---- KV append ------------------------------------------------------------ */
 
 static void append_fp8_row(const uint16_t* x, uint8_t* dst, float* scale_slot,
@@ -254,6 +408,27 @@ static void append_fp8_row(const uint16_t* x, uint8_t* dst, float* scale_slot,
   }
 }
 
+static void append_int8_row(const uint16_t* x, int8_t* dst, float* scale_slot,
+                            int opens_block, int D) {
+  float sc;
+  if (opens_block) {
+    float amax = 0.0f;
+    for (int d = 0; d < D; ++d) {
+      float a = fabsf(bf16_to_f32(x[d]));
+      if (a > amax) amax = a;
+    }
+    sc = amax / 127.0f;
+    if (amax == 0.0f) sc = 1.0f;
+    *scale_slot = sc;
+  } else {
+    sc = *scale_slot;
+  }
+  for (int d = 0; d < D; ++d) {
+    const float y = bf16_to_f32(x[d]) / sc; /* binary32, correctly rounded */
+    dst[d] = pkvo_int8_from_f32(y);
+  }
+}
+
 /* In-place append of N tokens into host copies of the caches. */
 int pkvo_kv_append(const uint16_t* k_new, const uint16_t* v_new,
                    const int32_t* slot_mapping, void* k_cache, void* v_cache,
@@ -261,8 +436,8 @@ int pkvo_kv_append(const uint16_t* k_new, const uint16_t* v_new,
                    int NB, int kv_dtype) {
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKVO_ERR_NULL;
   if (N < 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0) return PKVO_ERR_SHAPE;
-  if (kv_dtype != PKVO_KV_BF16 && kv_dtype != PKVO_KV_FP8) return PKVO_ERR_SHAPE;
-  if (kv_dtype == PKVO_KV_FP8 && (!k_scale || !v_scale)) return PKVO_ERR_NULL;
+  if (!valid_dtype(kv_dtype)) return PKVO_ERR_SHAPE;
+  if (kv_dtype != PKVO_KV_BF16 && (!k_scale || !v_scale)) return PKVO_ERR_NULL;
   const size_t row_elems = (size_t)Hkv * D;
   for (int i = 0; i < N; ++i) {
     const int64_t slot = slot_mapping[i];
@@ -276,6 +451,13 @@ int pkvo_kv_append(const uint16_t* k_new, const uint16_t* v_new,
     if (kv_dtype == PKVO_KV_BF16) {
       memcpy((uint16_t*)k_cache + dst, kr, row_elems * 2);
       memcpy((uint16_t*)v_cache + dst, vr, row_elems * 2);
+    } else if (kv_dtype == PKVO_KV_INT8) {
+      for (int g = 0; g < Hkv; ++g) {
+        append_int8_row(kr + (size_t)g * D, (int8_t*)k_cache + dst + (size_t)g * D,
+                        &k_scale[blk * Hkv + g], off == 0, D);
+        append_int8_row(vr + (size_t)g * D, (int8_t*)v_cache + dst + (size_t)g * D,
+                        &v_scale[blk * Hkv + g], off == 0, D);
+      }
     } else {
       for (int g = 0; g < Hkv; ++g) {
         append_fp8_row(kr + (size_t)g * D, (uint8_t*)k_cache + dst + (size_t)g * D,
@@ -286,4 +468,79 @@ int pkvo_kv_append(const uint16_t* k_new, const uint16_t* v_new,
     }
   }
   return PKVO_OK;
+}
+
+/* ---- RoPE ----------------------------------------------------------------- */
+
+/* Frequencies f_i, i < D/2, of the rotary embedding: theta^(-2i/D), then the
+ * Llama 3 scaling of the table path.  With lw = original_max / low_freq_factor
+ * and hw = original_max / high_freq_factor, and wavelength w = 2 pi / f:
+ *   w > lw            -> f / factor
+ *   hw <= w <= lw     -> (1 - a) f / factor + a f,  a = (original_max / w -
+ *                        low_freq_factor) / (high_freq_factor - low_freq_factor)
+ *   w < hw            -> f.
+ * factor = 1 leaves every frequency unscaled. */
+void pkvo_rope_freqs(int D, double theta, double factor, double low_freq_factor,
+                     double high_freq_factor, double original_max, double* f) {
+  const double lw = original_max / low_freq_factor;
+  const double hw = original_max / high_freq_factor;
+  for (int i = 0; i < D / 2; ++i) {
+    const double base = 1.0 / pow(theta, (2.0 * i) / (double)D);
+    const double w = 2.0 * 3.14159265358979323846 / base;   /* 2 pi / f */
+    double fi = base;
+    if (w > lw) {
+      fi = base / factor;
+    } else if (w >= hw) {
+      const double a = (original_max / w - low_freq_factor) / (high_freq_factor - low_freq_factor);
+      fi = (1.0 - a) * (base / factor) + a * base;
+    }
+    f[i] = fi;
+  }
+}
+
+/* Nearest-even rounding of a double straight to bf16 bits (8 significant
+ * bits).  Not via binary32: a double just above a bf16 midpoint could round
+ * to the midpoint in binary32 and then to even, below.  |x| = m 2^e with
+ * m in [0.5, 1); the 8-bit significand is m 2^8 rounded to an integer, ties
+ * to even; the result is exact in binary32, whose top 16 bits are the bf16.
+ * (Normal range only; the oracle's values are O(1).) */
+static uint16_t f64_to_bf16_bits(double x) {
+  if (isnan(x)) return 0x7fc0;
+  if (x == 0.0) return signbit(x) ? 0x8000 : 0x0000;
+  int e;
+  const double m = frexp(fabs(x), &e);
+  double q = m * 256.0; /* exact: a power-of-two scaling */
+  double lo = floor(q);
+  const double frac = q - lo; /* exact */
+  if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0)) lo += 1.0;
+  float f = (float)ldexp(lo, e - 8); /* exact: at most 9 significant bits */
+  if (x < 0) f = -f;
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* Rotate x [N, H, D] (bf16 bits) at positions pos[N]; y gets bf16 bits (may
+ * alias x).  If y_f64 is not NULL it receives the unrounded rotation. */
+void pkvo_rope_apply(const uint16_t* x, const int32_t* pos, int N, int H, int D, const double* f,
+                     uint16_t* y, double* y_f64) {
+  for (int n = 0; n < N; ++n) {
+    for (int h = 0; h < H; ++h) {
+      const size_t base = ((size_t)n * H + h) * D;
+      for (int i = 0; i < D / 2; ++i) {
+        const double a = (double)pos[n] * f[i];
+        const double c = cos(a), sn = sin(a);
+        const double x0 = pkvo_bf16_to_f64(x[base + 2 * i]);
+        const double x1 = pkvo_bf16_to_f64(x[base + 2 * i + 1]);
+        const double r0 = x0 * c - x1 * sn;
+        const double r1 = x0 * sn + x1 * c;
+        if (y_f64) {
+          y_f64[base + 2 * i] = r0;
+          y_f64[base + 2 * i + 1] = r1;
+        }
+        y[base + 2 * i] = f64_to_bf16_bits(r0);
+        y[base + 2 * i + 1] = f64_to_bf16_bits(r1);
+      }
+    }
+  }
 }

@@ -9,7 +9,9 @@ The one place where a value is derived rather than drawn is the pre-filled fp8
 cache: its codes are made by torch's own ``float8_e4m3fn`` cast (a library
 routine) of the N(0,1) source divided by a per-(block, kv head) scale
 amax/448 over the tokens already in that block.  Those bytes are an input to
-both sides; neither side's encoder is involved.
+both sides; neither side's encoder is involved.  The pre-filled int8 cache is
+drawn outright: codes uniform in [-127, 127] and per-(block, kv head) scales
+uniform in [0.02, 0.04] (values within about +-5, like N(0,1) data).
 
 Recipes (lengths from ``numpy.random.default_rng(seed)``, tensors from a
 ``torch.Generator`` seeded ``1000 + seed`` on the target device):
@@ -22,9 +24,18 @@ Recipes (lengths from ``numpy.random.default_rng(seed)``, tensors from a
   fp8           B=128 Hq=32 Hkv=8 D=128 BS=32, lengths uniform in [1024, 16384],
                 then 32 sequences (25%) moved so that the appended token opens a
                 new block; e4m3fn K/V with fp32 scales per (block, kv head)
+  int8          the fp8 recipe with int8 K/V codes (seed 5)
+  llama3_8b_verify4
+                the llama3_8b recipe (seed 1) with 4 query tokens per sequence
+                (a speculative-decoding verify step: the 4 new tokens are
+                appended, then each attends causally, bottom-right aligned)
+  long_context_window
+                the long_context recipe (seed 2) attending a sliding window of
+                the last 8192 tokens plus 16 sink tokens
 
-Every sequence's history holds L-1 tokens before the step; the step appends
-token L-1 (slot = block_tables[b][(L-1)//BS]*BS + (L-1)%BS) and then attends
+Every sequence's history holds L-q_len tokens before the step (q_len = 1
+unless a recipe says otherwise); the step appends tokens L-q_len .. L-1
+(slot = block_tables[b][t//BS]*BS + t%BS for position t) and then attends
 over L tokens.  The pool has ceil(1.1 * pages needed) blocks (64 for tiny),
 handed out in (sequence, logical page) order from a random permutation, so
 about 10% of the blocks are free.  Unused block-table entries are -1.  With
@@ -55,9 +66,13 @@ class Config:
     Hkv: int
     D: int
     BS: int
-    kv_dtype: str  # "bf16" or "fp8"
+    kv_dtype: str  # "bf16", "fp8" or "int8"
     max_len: int   # largest length the recipe can produce (sets max_blocks_per_seq)
     description: str = ""
+    q_len: int = 1     # query tokens per sequence
+    window: int = 0    # sliding window (0: the whole history)
+    sinks: int = 0     # tokens kept visible at the start when a window is set
+    lengths_from: str = ""   # draw lengths with another recipe's rule
 
 
 CONFIGS = {
@@ -71,24 +86,35 @@ CONFIGS = {
                         "70B-shaped mixed batch: B256 Hq64 Hkv8 D128 BS16, lognormal L"),
     "fp8": Config("fp8", 4, 128, 32, 8, 128, 32, "fp8", 16384,
                   "fp8 e4m3fn KV: B128 Hq32 Hkv8 D128 BS32, L~U[1024,16384]"),
+    "int8": Config("int8", 5, 128, 32, 8, 128, 32, "int8", 16384,
+                   "int8 KV: B128 Hq32 Hkv8 D128 BS32, L~U[1024,16384]", lengths_from="fp8"),
+    "llama3_8b_verify4": Config("llama3_8b_verify4", 1, 64, 32, 8, 128, 16, "bf16", 4096,
+                                "speculative verify: llama3_8b shapes, 4 query tokens per "
+                                "sequence, bottom-right causal", q_len=4,
+                                lengths_from="llama3_8b"),
+    "long_context_window": Config("long_context_window", 2, 4, 32, 8, 128, 16, "bf16", 131072,
+                                  "long context, sliding window 8192 + 16 sink tokens",
+                                  window=8192, sinks=16, lengths_from="long_context"),
 }
-CONFIG_ORDER = ["tiny", "llama3_8b", "long_context", "mixed_70b", "fp8"]
+CONFIG_ORDER = ["tiny", "llama3_8b", "long_context", "mixed_70b", "fp8", "int8",
+                "llama3_8b_verify4", "long_context_window"]
 
 
 def draw_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
-    """Context lengths (including the token appended this step) for a config."""
-    if cfg.name == "tiny":
+    """Context lengths (including the tokens appended this step) for a config."""
+    rule = cfg.lengths_from or cfg.name
+    if rule == "tiny":
         L = np.array([1, 17, 33, 100], dtype=np.int64)
-    elif cfg.name == "llama3_8b":
+    elif rule == "llama3_8b":
         L = rng.integers(512, 4096, cfg.B, endpoint=True)
-    elif cfg.name == "long_context":
+    elif rule == "long_context":
         L = np.full(cfg.B, 131072, dtype=np.int64)
-    elif cfg.name == "mixed_70b":
+    elif rule == "mixed_70b":
         x = rng.lognormal(mean=math.log(1500.0), sigma=1.0, size=cfg.B)
         L = np.clip(np.rint(x), 1, 16384).astype(np.int64)
         ones = rng.choice(cfg.B, size=int(round(0.05 * cfg.B)), replace=False)
         L[ones] = 1
-    elif cfg.name == "fp8":
+    elif rule == "fp8":
         L = rng.integers(1024, 16384, cfg.B, endpoint=True)
         cross = rng.choice(cfg.B, size=cfg.B // 4, replace=False)
         is_cross = np.zeros(cfg.B, dtype=bool)
@@ -126,8 +152,13 @@ class Workload:
     v_new: torch.Tensor            # bf16 [B, Hkv, D]
     k_cache: torch.Tensor          # bf16 or uint8 [NB, BS, Hkv, D]
     v_cache: torch.Tensor
-    k_scale: Optional[torch.Tensor] = None  # fp32 [NB, Hkv] (fp8 only)
+    k_scale: Optional[torch.Tensor] = None  # fp32 [NB, Hkv] (fp8 and int8)
     v_scale: Optional[torch.Tensor] = None
+    q_lens: Optional[np.ndarray] = None      # query tokens per sequence (None: all 1)
+    q_start_np: Optional[np.ndarray] = None  # int32 [B + 1] cumulative query counts
+    q_start: Optional[torch.Tensor] = None
+    window: int = 0
+    sinks: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -143,8 +174,12 @@ def build_workload(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int,
                    lengths: Sequence[int], kv_dtype: str = "bf16", seed: int = 0,
                    NB: Optional[int] = None, MBS: Optional[int] = None,
                    scale: Optional[float] = None, device="cpu", poison: bool = False,
-                   rng: Optional[np.random.Generator] = None) -> Workload:
-    """Draw one workload with the given shapes and context lengths."""
+                   rng: Optional[np.random.Generator] = None,
+                   q_lens: Optional[Sequence[int]] = None, window: int = 0,
+                   sinks: int = 0) -> Workload:
+    """Draw one workload with the given shapes and context lengths.  q, k_new,
+    v_new and slot_mapping have one row per query token (sum of q_lens, one
+    per sequence by default); q_start holds the cumulative counts."""
     if rng is None:
         rng = np.random.default_rng(seed)
     L = np.asarray(lengths, dtype=np.int64)
@@ -165,20 +200,26 @@ def build_workload(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int,
         n = int(pages[b])
         bt[b, :n] = perm[pos:pos + n]
         pos += n
-    last = L - 1
-    slots = (bt[np.arange(B), last // BS].astype(np.int64) * BS + last % BS).astype(np.int32)
+    ql = np.ones(B, dtype=np.int64) if q_lens is None else np.asarray(q_lens, dtype=np.int64)
+    assert ql.shape == (B,) and (ql >= 1).all() and (ql <= L).all()
+    q_start = np.zeros(B + 1, dtype=np.int32)
+    q_start[1:] = np.cumsum(ql)
+    TQ = int(q_start[-1])
+    seq_of = np.repeat(np.arange(B), ql)                   # sequence of each query token
+    tpos = np.concatenate([np.arange(L[b] - ql[b], L[b]) for b in range(B)]).astype(np.int64)
+    slots = (bt[seq_of, tpos // BS].astype(np.int64) * BS + tpos % BS).astype(np.int32)
 
     device = torch.device(device)
     gen = torch.Generator(device=device)
     gen.manual_seed(1000 + seed)
-    q = _bf16_randn((B, Hq, D), gen, device)
-    k_new = _bf16_randn((B, Hkv, D), gen, device)
-    v_new = _bf16_randn((B, Hkv, D), gen, device)
+    q = _bf16_randn((TQ, Hq, D), gen, device)
+    k_new = _bf16_randn((TQ, Hkv, D), gen, device)
+    v_new = _bf16_randn((TQ, Hkv, D), gen, device)
 
-    # which (block, in-block slot) pairs hold a pre-filled token (positions < L-1)
+    # which (block, in-block slot) pairs hold a pre-filled token (positions < L-q_len)
     filled = np.zeros((NB, BS), dtype=bool)
     for b in range(B):
-        n_tok = int(L[b]) - 1
+        n_tok = int(L[b]) - int(ql[b])
         full, rem = divmod(n_tok, BS)
         if full:
             filled[bt[b, :full]] = True
@@ -216,6 +257,23 @@ def build_workload(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int,
             del src, y
         k_cache, v_cache = caches
         k_scale, v_scale = scales
+    elif kv_dtype == "int8":
+        caches, scales = [], []
+        used = torch.from_numpy(filled.any(axis=1)).to(device)   # blocks with a pre-filled token
+        for _ in range(2):
+            codes = torch.randint(-127, 128, (NB, BS, Hkv, D), generator=gen, device=device,
+                                  dtype=torch.int8)
+            hole = ~filled_t[:, :, None, None]
+            codes = torch.where(hole, torch.tensor(-128 if poison else 0, dtype=torch.int8,
+                                                   device=device), codes)
+            sc = 0.02 + 0.02 * torch.rand((NB, Hkv), generator=gen, device=device,
+                                          dtype=torch.float32)
+            sc = torch.where(used[:, None], sc,
+                             torch.full_like(sc, float("nan") if poison else 1.0))
+            caches.append(codes.contiguous())
+            scales.append(sc.contiguous())
+        k_cache, v_cache = caches
+        k_scale, v_scale = scales
     else:
         raise ValueError(kv_dtype)
 
@@ -228,7 +286,8 @@ def build_workload(name: str, B: int, Hq: int, Hkv: int, D: int, BS: int,
         block_tables=torch.from_numpy(bt).to(device),
         slot_mapping=torch.from_numpy(slots).to(device),
         q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache,
-        k_scale=k_scale, v_scale=v_scale)
+        k_scale=k_scale, v_scale=v_scale, q_lens=ql, q_start_np=q_start,
+        q_start=torch.from_numpy(q_start).to(device), window=int(window), sinks=int(sinks))
 
 
 def make_config_workload(name: str, device="cpu", poison: bool = False) -> Workload:
@@ -240,7 +299,8 @@ def make_config_workload(name: str, device="cpu", poison: bool = False) -> Workl
     NB = 64 if cfg.name == "tiny" else None
     return build_workload(cfg.name, cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.BS, L,
                           kv_dtype=cfg.kv_dtype, seed=cfg.seed, NB=NB, MBS=MBS,
-                          device=device, poison=poison, rng=rng)
+                          device=device, poison=poison, rng=rng,
+                          q_lens=np.full(cfg.B, cfg.q_len), window=cfg.window, sinks=cfg.sinks)
 
 
 # ---- host views for the oracle ---------------------------------------------
@@ -252,8 +312,9 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def cache_host(t: torch.Tensor) -> np.ndarray:
-    """Host copy of a cache in the oracle's raw form (uint16 bf16 bits or uint8)."""
+    """Host copy of a cache in the oracle's raw form (uint16 bf16 bits, uint8
+    e4m3fn codes or int8 codes)."""
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
-    assert t.dtype == torch.uint8
+    assert t.dtype in (torch.uint8, torch.int8)
     return t.detach().contiguous().cpu().numpy()

@@ -1,5 +1,6 @@
 """The oracle's pins are sensitive: each plausible mistake planted in a copy
-of the oracle's C source makes at least one pin in test_oracle_pins.py fail.
+of the oracle's C source makes at least one pin in test_oracle_pins.py or
+test_oracle_pins_ext.py fail.
 
 Every mutant is compiled into a temporary library and the pins are run
 against it in a child process (PKV_ORACLE_LIB points the oracle loader at
@@ -26,13 +27,33 @@ MUTANTS = [
     ("one position past the history", "for (int t = 0; t < L; ++t) {", "for (int t = 0; t < L + (L < 60); ++t) {"),
     ("min instead of max as the shift", "if (s[t] > m) m = s[t];", "if (s[t] < m) m = s[t];"),
     ("weights not normalised", "const double w = s[t] / Z;", "const double w = s[t];"),
-    ("fp8 scale ignored", "(double)scales[scale_idx];", "1.0;"),
+    ("fp8 scale ignored",
+     "pkvo_e4m3fn_to_f64(((const uint8_t*)cache)[row + (size_t)d]) *\n         (double)scales[scale_idx];",
+     "pkvo_e4m3fn_to_f64(((const uint8_t*)cache)[row + (size_t)d]) * 1.0;"),
     ("fp8 scale divisor 240 (FNUZ max)", "sc = amax / 448.0f;", "sc = amax / 240.0f;"),
     ("zero-amax scale 0.5", "if (amax == 0.0f) sc = 1.0f;", "if (amax == 0.0f) sc = 0.5f;"),
     ("opening token does not store its scale", "*scale_slot = sc;", "(void)0;"),
     ("e4m3 ties not to even", "(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(0)"),
     ("e4m3 subnormal exponent", "mag = ldexp((double)m / 8.0, -6);", "mag = ldexp((double)m / 8.0, -7);"),
     ("no saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);", "if (a >= 464.0) return (uint8_t)(sign | 0x7F);"),
+    # generalised attention
+    ("causal limit one short", "const int lim = L - ql + i;", "const int lim = L - ql + i - 1;"),
+    ("causal mask aligned top-left", "const int lim = L - ql + i;", "const int lim = i;"),
+    ("window one token too wide", "v = (t > lim - window) || (t < sinks);", "v = (t >= lim - window) || (t < sinks);"),
+    ("sinks ignored", "v = (t > lim - window) || (t < sinks);", "v = (t > lim - window);"),
+    # int8
+    ("int8 scale divisor 128", "sc = amax / 127.0f;", "sc = amax / 128.0f;"),
+    ("int8 rounds halves away from zero", "double r = rint((double)y);", "double r = round((double)y);"),
+    ("int8 saturates at 126", "if (r > 127.0) r = 127.0;", "if (r > 126.0) r = 126.0;"),
+    ("int8 scale ignored", "return (double)((const int8_t*)cache)[row + (size_t)d] * (double)scales[scale_idx];",
+     "return (double)((const int8_t*)cache)[row + (size_t)d];"),
+    # RoPE
+    ("rotation sign flipped in one component", "const double r0 = x0 * c - x1 * sn;", "const double r0 = x0 * c + x1 * sn;"),
+    ("pair members swapped", "const double x1 = pkvo_bf16_to_f64(x[base + 2 * i + 1]);",
+     "const double x1 = pkvo_bf16_to_f64(x[base + (2 * i + 2) % D]);"),
+    ("frequencies theta^(-i/D)", "pow(theta, (2.0 * i) / (double)D)", "pow(theta, (double)i / (double)D)"),
+    ("Llama 3 long band starts at the short edge", "if (w > lw) {", "if (w > hw) {"),
+    ("bf16 rounding truncates", "if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0)) lo += 1.0;", "(void)frac;"),
 ]
 
 
@@ -49,7 +70,8 @@ def _run_mutant(mut, tmpdir):
                     "-o", lib, csrc, "-lm"], check=True, capture_output=True)
     env = dict(os.environ, PKV_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_pins_ext.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     return name, r.returncode
 
@@ -62,6 +84,7 @@ def test_every_planted_mistake_fails_a_pin():
     assert not survivors, f"mutants not caught by any pin: {survivors}"
     # and the shipped oracle passes them (the pins are not failing for another reason)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_pins_ext.py")],
                        cwd=ROOT, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]

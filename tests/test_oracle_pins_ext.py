@@ -1,0 +1,384 @@
+"""Pins for the oracle's generalised attention (several query tokens per
+sequence with the bottom-right causal mask; sliding window with attention
+sinks), its INT8 codec and append, and its RoPE, each checked against
+something other than itself: a value the pages print, a closed form, an
+independent dense brute force or a library routine.  CPU only.
+
+Sources: "Prefill Forward Prefix Caching Explained" (bottom-right causal
+mask), the "Decode Phase" glossary (sliding window, attention sinks, INT8 KV
+quantisation), "tiny-vllm part 5" (RoPE section).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_decode_06_amd import workloads as W
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------- helpers ---
+
+def host(wl: W.Workload):
+    """Host copies after the oracle's own append of the step's tokens."""
+    k = W.cache_host(wl.k_cache).copy()
+    v = W.cache_host(wl.v_cache).copy()
+    ks = None if wl.k_scale is None else wl.k_scale.cpu().numpy().copy()
+    vs = None if wl.v_scale is None else wl.v_scale.cpu().numpy().copy()
+    oracle.kv_append(W.bf16_bits(wl.k_new), W.bf16_bits(wl.v_new), wl.slot_mapping_np,
+                     k, v, ks, vs)
+    return dict(q=W.bf16_bits(wl.q), k=k, v=v, bt=wl.block_tables_np,
+                cl=wl.lengths.astype(np.int32), ks=ks, vs=vs, scale=wl.scale,
+                qs=wl.q_start_np, ql=wl.q_lens)
+
+
+def general(h, sinks=0, window=0, q_start=True, **kw):
+    return oracle.paged_attention(h["q"], h["k"], h["v"], h["bt"], h["cl"], h["scale"],
+                                  q_start=h["qs"] if q_start else None, sinks=sinks,
+                                  window=window, k_scale=h["ks"], v_scale=h["vs"], **kw)
+
+
+def dequant(cache, scales):
+    if cache.dtype == np.int8:
+        return cache.astype(np.float64) * scales.astype(np.float64)[:, None, :, None]
+    return brute.dequant_cache(cache, scales)
+
+
+def visible_mask(L, ql, sinks, window):
+    """[ql, L] boolean mask, built from the rule as numpy array algebra."""
+    i = np.arange(ql)[:, None]
+    j = np.arange(L)[None, :]
+    lim = L - ql + i
+    m = j <= lim
+    if window > 0:
+        m &= (j > lim - window) | (j < sinks)
+    return m
+
+
+def dense_masked(h, sinks, window):
+    """Gather each sequence densely, then masked softmax(q K^T scale) V."""
+    q = brute.bf16_bits_to_f64(h["q"])
+    Kf, Vf = dequant(h["k"], h["ks"]), dequant(h["v"], h["vs"])
+    NB, BS, Hkv, D = Kf.shape
+    Hq = q.shape[1]
+    G = Hq // Hkv
+    out = np.zeros_like(q)
+    for b in range(len(h["cl"])):
+        L, r0, ql = int(h["cl"][b]), int(h["qs"][b]), int(h["ql"][b])
+        K = np.repeat(brute.gather_history(Kf, h["bt"][b], L, BS), G, axis=1)
+        V = np.repeat(brute.gather_history(Vf, h["bt"][b], L, BS), G, axis=1)
+        m = visible_mask(L, ql, sinks, window)
+        for i in range(ql):
+            if not m[i].any():
+                continue
+            s = np.einsum("hd,thd->ht", q[r0 + i], K) * float(np.float32(h["scale"]))
+            s = np.where(m[i][None, :], s, -np.inf)
+            s -= s.max(axis=1, keepdims=True)
+            w = np.exp(s)
+            w /= w.sum(axis=1, keepdims=True)
+            out[r0 + i] = np.einsum("ht,thd->hd", w, V)
+    return out
+
+
+def sdpa_masked(h, sinks, window):
+    """The same through torch's CPU scaled_dot_product_attention (fp64) with
+    an explicit boolean mask (a library routine)."""
+    q = torch.from_numpy(brute.bf16_bits_to_f64(h["q"]))
+    Kf, Vf = dequant(h["k"], h["ks"]), dequant(h["v"], h["vs"])
+    BS, Hkv = Kf.shape[1], Kf.shape[2]
+    Hq = q.shape[1]
+    out = torch.zeros_like(q)
+    for b in range(len(h["cl"])):
+        L, r0, ql = int(h["cl"][b]), int(h["qs"][b]), int(h["ql"][b])
+        K = torch.from_numpy(np.ascontiguousarray(brute.gather_history(Kf, h["bt"][b], L, BS)))
+        V = torch.from_numpy(np.ascontiguousarray(brute.gather_history(Vf, h["bt"][b], L, BS)))
+        m = torch.from_numpy(visible_mask(L, ql, sinks, window))
+        qq = q[r0:r0 + ql].permute(1, 0, 2).contiguous()           # [Hq, ql, D]
+        kk = K.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0).contiguous()
+        vv = V.permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0).contiguous()
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, vv, attn_mask=m, scale=float(np.float32(h["scale"])))
+        o = torch.where(m.any(1)[None, :, None], o, torch.zeros_like(o))
+        out[r0:r0 + ql] = o.permute(1, 0, 2)
+    return out.numpy()
+
+
+def mq(B=3, Hq=8, Hkv=2, D=64, BS=16, lengths=(7, 20, 45), q_lens=(1, 3, 4), kv="bf16",
+       seed=11, poison=False):
+    return W.build_workload("t", B, Hq, Hkv, D, BS, list(lengths), kv_dtype=kv, seed=seed,
+                            poison=poison, q_lens=list(q_lens))
+
+
+MQ_CASES = [
+    # (B, Hq, Hkv, D, BS, lengths, q_lens, kv, sinks, window)
+    (3, 8, 2, 64, 16, (7, 20, 45), (1, 3, 4), "bf16", 0, 0),
+    (3, 8, 2, 64, 16, (7, 20, 45), (1, 3, 4), "bf16", 2, 9),
+    (2, 16, 2, 128, 32, (40, 70), (2, 2), "fp8", 0, 0),
+    (2, 16, 2, 128, 32, (40, 70), (2, 2), "fp8", 4, 17),
+    (3, 4, 4, 64, 16, (3, 33, 80), (3, 1, 8), "int8", 0, 0),
+    (3, 4, 4, 64, 16, (3, 33, 80), (3, 1, 8), "int8", 1, 20),
+    (2, 8, 1, 128, 16, (64, 129), (1, 1), "bf16", 16, 32),
+]
+
+
+# ------------------------------------------------- generalised attention ----
+
+@pytest.mark.parametrize("case", MQ_CASES, ids=lambda c: f"{c[7]}-ql{c[6]}-S{c[8]}W{c[9]}")
+def test_general_attention_matches_dense_masked_bruteforce_and_library(case):
+    B, Hq, Hkv, D, BS, L, ql, kv, S, Wn = case
+    h = host(mq(B, Hq, Hkv, D, BS, L, ql, kv))
+    ref = general(h, S, Wn)
+    np.testing.assert_allclose(ref, dense_masked(h, S, Wn), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(ref, sdpa_masked(h, S, Wn), rtol=1e-11, atol=1e-12)
+
+
+def test_bottom_right_mask_matches_the_printed_example():
+    """seqlen_q = 2, seqlen_k = 5: the page prints the mask row by row."""
+    golden = np.loadtxt(os.path.join(GOLDEN, "bottom_right_causal_mask.txt"), dtype=int)
+    h = host(mq(1, 4, 1, 64, 16, (5,), (2,), seed=3))
+    _, w = general(h, return_weights=True)
+    seen = (w[:, 0, :5] > 0).astype(int)
+    assert np.array_equal(seen, golden)
+
+
+def test_one_query_and_no_window_is_the_decode_oracle():
+    h = host(mq(q_lens=(1, 1, 1)))
+    dec = oracle.paged_decode_attention(h["q"], h["k"], h["v"], h["bt"], h["cl"], h["scale"])
+    np.testing.assert_array_equal(general(h), dec)
+    np.testing.assert_array_equal(general(h, q_start=False), dec)
+
+
+def test_query_i_equals_decode_over_its_own_prefix():
+    """Bottom-right alignment: query i of a sequence with q_len new tokens
+    sees exactly what a one-token decode over the first L - q_len + i + 1
+    positions sees."""
+    h = host(mq(lengths=(9, 30, 50), q_lens=(2, 4, 5)))
+    ref = general(h)
+    for b in range(3):
+        L, r0, ql = int(h["cl"][b]), int(h["qs"][b]), int(h["ql"][b])
+        for i in range(ql):
+            cl = h["cl"].copy()
+            cl[b] = L - ql + i + 1
+            dec = oracle.paged_decode_attention(h["q"][[r0 + i]], h["k"], h["v"], h["bt"][[b]],
+                                                cl[[b]], h["scale"])
+            np.testing.assert_allclose(ref[r0 + i], dec[0], rtol=1e-13, atol=1e-15)
+
+
+def test_window_of_one_returns_the_value_at_the_limit_exactly():
+    h = host(mq(lengths=(9, 30, 50), q_lens=(2, 4, 5)))
+    out = general(h, sinks=0, window=1)
+    V = brute.bf16_bits_to_f64(h["v"])
+    Hkv = V.shape[2]
+    G = out.shape[1] // Hkv
+    for b in range(3):
+        L, r0, ql = int(h["cl"][b]), int(h["qs"][b]), int(h["ql"][b])
+        for i in range(ql):
+            t = L - ql + i
+            blk = h["bt"][b, t // 16]
+            for hh in range(out.shape[1]):
+                assert np.array_equal(out[r0 + i, hh], V[blk, t % 16, hh // G])
+
+
+def test_wide_window_or_all_sinks_is_the_full_history():
+    h = host(mq(lengths=(9, 30, 50), q_lens=(2, 4, 5)))
+    full = general(h)
+    np.testing.assert_array_equal(general(h, sinks=0, window=50), full)
+    np.testing.assert_array_equal(general(h, sinks=50, window=3), full)
+
+
+def test_window_weights_sit_on_sinks_and_window_only():
+    h = host(mq(lengths=(9, 30, 50), q_lens=(2, 4, 5)))
+    S, Wn = 3, 7
+    _, w = general(h, sinks=S, window=Wn, return_weights=True)
+    for b in range(3):
+        L, r0, ql = int(h["cl"][b]), int(h["qs"][b]), int(h["ql"][b])
+        m = visible_mask(L, ql, S, Wn)
+        for i in range(ql):
+            wi = w[r0 + i, :, :L]
+            assert (wi[:, ~m[i]] == 0).all()
+            assert (wi[:, m[i]] > 0).all()
+            np.testing.assert_allclose(wi.sum(axis=1), 1.0, rtol=1e-14)
+            assert (w[r0 + i, :, L:] == 0).all()
+
+
+def test_query_with_no_visible_key_gives_zero():
+    """q_len may exceed the keys a query can see only by a broken contract;
+    the oracle then defines the output as 0 (here: window hides nothing,
+    q_len = L, the first query sees key 0 only)."""
+    h = host(mq(lengths=(4, 5, 6), q_lens=(4, 5, 6)))
+    out = general(h)
+    assert np.isfinite(out).all()
+    h["cl"] = h["cl"] - 1      # now query 0 of each sequence has lim = -1
+    out = general(h)
+    for b in range(3):
+        assert (out[int(h["qs"][b])] == 0).all()
+
+
+def test_poison_outside_the_window_is_never_read():
+    """With NaN in every byte outside the pre-filled history, and keys hidden
+    by the window, the result is finite and equals the clean run."""
+    a = general(host(mq(kv="bf16", poison=True)), sinks=2, window=9)
+    b = general(host(mq(kv="bf16", poison=False)), sinks=2, window=9)
+    assert np.isfinite(a).all()
+    np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------------------------ int8 ----
+
+def test_int8_code_rounds_halves_to_even_and_saturates():
+    x = np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.49, 127.5, 1e9, -1e9, 0.0],
+                 np.float32)
+    assert oracle.int8_encode(x).tolist() == [0, 2, 2, 0, -2, -2, 126, 127, 127, 127, -127, 0]
+
+
+def test_int8_code_matches_library_rounding():
+    """torch's round is half-to-even on fp32; clamp to +-127 after it."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * 60).astype(np.float32)
+    x[:200] = np.round(x[:200]) + 0.5          # exact halves
+    lib = torch.from_numpy(x).round().clamp(-127, 127).to(torch.int8).numpy()
+    assert np.array_equal(oracle.int8_encode(x), lib)
+
+
+def test_int8_append_scale_codes_and_error_bound():
+    wl = W.build_workload("t", 3, 8, 2, 64, 16, [1, 17, 40], kv_dtype="int8", seed=9)
+    k = W.cache_host(wl.k_cache).copy()
+    v = W.cache_host(wl.v_cache).copy()
+    ks, vs = wl.k_scale.numpy().copy(), wl.v_scale.numpy().copy()
+    k0, ks0 = k.copy(), ks.copy()
+    kn = W.bf16_bits(wl.k_new)
+    oracle.kv_append(kn, W.bf16_bits(wl.v_new), wl.slot_mapping_np, k, v, ks, vs)
+    x = brute.bf16_bits_to_f64(kn)
+    for i, slot in enumerate(wl.slot_mapping_np):
+        blk, off = divmod(int(slot), 16)
+        for g in range(2):
+            row = x[i, g]
+            if off == 0:     # opens the block: scale = amax / 127 in fp32
+                amax = np.float32(np.abs(row).max())
+                assert ks[blk, g] == np.float32(amax / np.float32(127.0))
+                assert np.abs(k[blk, off, g]).max() == 127
+            else:
+                assert ks[blk, g] == ks0[blk, g]
+            sc = float(ks[blk, g])
+            err = np.abs(k[blk, off, g].astype(np.float64) * sc - row)
+            inside = np.abs(row) <= 127 * sc
+            # half a step, plus the fp32 rounding of x / scale (<= 127 * 2^-24 steps)
+            assert (err[inside] <= sc * (0.5 + 1e-4)).all()
+    # nothing else changed
+    touched = np.zeros(k.shape[:2], bool)
+    for slot in wl.slot_mapping_np:
+        touched[divmod(int(slot), 16)] = True
+    assert np.array_equal(k[~touched], k0[~touched])
+
+
+def test_int8_zero_token_opening_a_block_gets_scale_one():
+    wl = W.build_workload("t", 1, 4, 1, 64, 16, [17], kv_dtype="int8", seed=2)
+    k = W.cache_host(wl.k_cache).copy()
+    v = W.cache_host(wl.v_cache).copy()
+    ks, vs = wl.k_scale.numpy().copy(), wl.v_scale.numpy().copy()
+    zero = np.zeros((1, 1, 64), np.uint16)
+    oracle.kv_append(zero, zero, wl.slot_mapping_np, k, v, ks, vs)
+    blk = int(wl.slot_mapping_np[0]) // 16
+    assert ks[blk, 0] == 1.0 and (k[blk, 0, 0] == 0).all()
+
+
+def test_int8_attention_uses_scaled_codes():
+    h = host(mq(kv="int8", q_lens=(1, 1, 1)))
+    ref = oracle.paged_decode_attention(h["q"], h["k"], h["v"], h["bt"], h["cl"], h["scale"],
+                                        k_scale=h["ks"], v_scale=h["vs"])
+    np.testing.assert_allclose(ref, dense_masked(h, 0, 0), rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------------------ RoPE ----
+
+def test_rope_position_zero_is_the_identity():
+    rng = np.random.default_rng(1)
+    x = W.bf16_bits(torch.from_numpy(rng.standard_normal((3, 4, 128)).astype(np.float32))
+                    .to(torch.bfloat16))
+    y, _ = oracle.rope_apply(x, np.zeros(3, np.int32), oracle.rope_freqs(128))
+    assert np.array_equal(y, x)
+
+
+def test_rope_matches_complex_rotation_and_keeps_pair_norms():
+    """(x0 + i x1) e^{i pos f} with numpy complex128 (a library route)."""
+    rng = np.random.default_rng(2)
+    x = W.bf16_bits(torch.from_numpy(rng.standard_normal((5, 3, 64)).astype(np.float32))
+                    .to(torch.bfloat16))
+    pos = np.array([0, 1, 77, 4095, 131071], np.int32)
+    f = oracle.rope_freqs(64)
+    _, y64 = oracle.rope_apply(x, pos, f)
+    xf = brute.bf16_bits_to_f64(x)
+    z = (xf[..., 0::2] + 1j * xf[..., 1::2]) * np.exp(1j * pos[:, None, None] * f[None, None, :])
+    np.testing.assert_allclose(y64[..., 0::2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y64[..., 1::2], z.imag, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y64[..., 0::2] ** 2 + y64[..., 1::2] ** 2,
+                               xf[..., 0::2] ** 2 + xf[..., 1::2] ** 2, rtol=1e-12)
+
+
+def test_rope_dot_products_depend_only_on_relative_position():
+    rng = np.random.default_rng(3)
+    qk = W.bf16_bits(torch.from_numpy(rng.standard_normal((2, 1, 128)).astype(np.float32))
+                     .to(torch.bfloat16))
+    f = oracle.rope_freqs(128)
+    def dot(m, n):
+        _, a = oracle.rope_apply(qk[[0]], np.array([m], np.int32), f)
+        _, b = oracle.rope_apply(qk[[1]], np.array([n], np.int32), f)
+        return float((a * b).sum())
+    for m, n, s in [(10, 3, 100), (500, 499, 7000), (0, 40, 12345)]:
+        assert abs(dot(m, n) - dot(m + s, n + s)) < 1e-9
+
+
+def test_rope_bf16_output_is_the_nearest_even():
+    rng = np.random.default_rng(4)
+    x = W.bf16_bits(torch.from_numpy(rng.standard_normal((64, 2, 64)).astype(np.float32))
+                    .to(torch.bfloat16))
+    y, y64 = oracle.rope_apply(x, rng.integers(0, 100000, 64).astype(np.int32),
+                               oracle.rope_freqs(64))
+    yv = brute.bf16_bits_to_f64(y)
+    # the neighbours one bf16 step below and above (same sign, normal range)
+    up = brute.bf16_bits_to_f64((y.astype(np.int64) + 1).astype(np.uint16))
+    dn = brute.bf16_bits_to_f64((y.astype(np.int64) - 1).astype(np.uint16))
+    e = np.abs(yv - y64)
+    nz = y64 != 0
+    assert (e[nz] <= np.abs(up - y64)[nz]).all() and (e[nz] <= np.abs(dn - y64)[nz]).all()
+
+
+def test_bf16_rounding_straight_from_double():
+    """A rotation whose exact result lies just above a bf16 midpoint must
+    round up.  Near 2^-8 the bf16 step is 2^-15; v = 2^-8 (1 + 2^-8 + 2^-30)
+    lies 2^-38 above the midpoint 2^-8 (1 + 2^-8), so the nearest bf16 is
+    2^-8 (1 + 2^-7).  (Via binary32, v would first round onto the midpoint,
+    which is binary32-exact, and then to the even 2^-8.)  (1, 0) rotated by
+    a = asin(v) at position 1 has second component sin(a) = v to within
+    2^-60."""
+    x = np.array([[[0x3F80, 0x0000]]], np.uint16)          # (1.0, 0.0)
+    v = 2.0 ** -8 * (1 + 2.0 ** -8 + 2.0 ** -30)
+    y, y64 = oracle.rope_apply(x, np.array([1], np.int32), np.array([math.asin(v)]))
+    assert abs(y64[0, 0, 1] - v) < 2.0 ** -60
+    assert float(np.float32(v)) == 2.0 ** -8 * (1 + 2.0 ** -8)   # the binary32 detour's midpoint
+    assert brute.bf16_bits_to_f64(y[0, 0, 1:2])[0] == 2.0 ** -8 * (1 + 2.0 ** -7)
+
+
+def test_rope_frequencies_follow_the_llama3_bands():
+    """theta 500000, factor 32, bands at wavelengths 8192/4 and 8192/1 (the
+    parameters the page's table path is built with)."""
+    D = 128
+    base = oracle.rope_freqs(D, factor=1.0)
+    f = oracle.rope_freqs(D)
+    assert base[0] == 1.0
+    assert (np.diff(base) < 0).all()
+    w = 2 * math.pi / base
+    short, long_ = w < 8192 / 4, w > 8192 / 1
+    assert short.any() and long_.any() and (~short & ~long_).any()
+    np.testing.assert_array_equal(f[short], base[short])
+    np.testing.assert_allclose(f[long_], base[long_] / 32, rtol=1e-15)
+    mid = ~short & ~long_
+    r = f[mid] / base[mid]
+    assert ((r > 1 / 32) & (r < 1)).all() and (np.diff(r) < 0).all()
