@@ -31,18 +31,40 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
 
 
+def visible_keys(wl):
+    """Per sequence, the keys some query sees: every position without a
+    window; otherwise the first `sinks` plus those from L - q_len - window + 1
+    on.  And the blocks those keys sit in."""
+    L = wl.lengths.astype(np.int64)
+    BS = wl.BS
+    if wl.window <= 0:
+        return L, (L + BS - 1) // BS
+    ql = wl.q_lens.astype(np.int64)
+    lo = np.maximum(L - ql - wl.window + 1, 0)
+    keys = np.where(wl.sinks >= lo, L, np.minimum(wl.sinks, L) + (L - lo))
+    pe = (L + BS - 1) // BS
+    ps = np.minimum((wl.sinks + BS - 1) // BS, pe)
+    pw = lo // BS
+    pages = np.where(pw <= ps, pe, ps + (pe - pw))
+    return keys, pages
+
+
 def kv_bytes(wl) -> int:
-    elem = 1 if wl.kv_dtype == "fp8" else 2
-    tot = int(wl.lengths.sum()) * 2 * wl.Hkv * wl.D * elem
-    if wl.kv_dtype == "fp8":
-        pages = ((wl.lengths + wl.BS - 1) // wl.BS).sum()
-        tot += int(pages) * wl.Hkv * 2 * 4
+    """Algorithmic KV bytes of one step: K and V of every key some query sees
+    (and the per-block scales of a quantised cache)."""
+    elem = 2 if wl.kv_dtype == "bf16" else 1
+    keys, pages = visible_keys(wl)
+    tot = int(keys.sum()) * 2 * wl.Hkv * wl.D * elem
+    if wl.kv_dtype != "bf16":
+        tot += int(pages.sum()) * wl.Hkv * 2 * 4
     return tot
 
 
@@ -80,10 +102,10 @@ def measured_traffic(config: str, kernel: str):
 
 
 def cpu_baseline(wl, budget_s=12.0):
-    """The oracle, as it stands, on the host cores: one full decode step's
-    attention over the same batch (after the oracle's own append), repeated
-    until about `budget_s` of wall time has passed."""
-    import numpy as np
+    """The oracle, as it stands, on the host cores: one full step's attention
+    over the same batch (after the oracle's own append of the step's tokens,
+    in position order), repeated until about `budget_s` of wall time has
+    passed."""
     import oracle
     from paged_kv_decode_06_amd import workloads as W
 
@@ -91,9 +113,13 @@ def cpu_baseline(wl, budget_s=12.0):
     v = W.cache_host(wl.v_cache).copy()
     ks = None if wl.k_scale is None else wl.k_scale.cpu().numpy().copy()
     vs = None if wl.v_scale is None else wl.v_scale.cpu().numpy().copy()
-    oracle.kv_append(W.bf16_bits(wl.k_new), W.bf16_bits(wl.v_new), wl.slot_mapping_np, k, v, ks, vs)
+    pos = np.concatenate([np.arange(q) for q in wl.q_lens])
+    for i in range(int(wl.q_lens.max())):
+        slots = np.where(pos == i, wl.slot_mapping_np, -1).astype(np.int32)
+        oracle.kv_append(W.bf16_bits(wl.k_new), W.bf16_bits(wl.v_new), slots, k, v, ks, vs)
     q = W.bf16_bits(wl.q)
     cl = wl.lengths.astype(np.int32)
+    general = int(wl.q_lens.max()) > 1 or wl.window > 0
     try:
         threads = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -103,8 +129,13 @@ def cpu_baseline(wl, budget_s=12.0):
     t_all = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        oracle.paged_decode_attention(q, k, v, wl.block_tables_np, cl, wl.scale, k_scale=ks,
-                                      v_scale=vs, nthreads=threads)
+        if general:
+            oracle.paged_attention(q, k, v, wl.block_tables_np, cl, wl.scale, q_start=wl.q_start_np,
+                                   sinks=wl.sinks, window=wl.window, k_scale=ks, v_scale=vs,
+                                   nthreads=threads)
+        else:
+            oracle.paged_decode_attention(q, k, v, wl.block_tables_np, cl, wl.scale, k_scale=ks,
+                                          v_scale=vs, nthreads=threads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all > budget_s or len(times) >= 5:
             break
@@ -113,6 +144,97 @@ def cpu_baseline(wl, budget_s=12.0):
             "kind": "oracle",
             "sample": f"full {wl.name} batch (B={wl.B}), fp64 attention of one step, "
                       f"{len(times)} run(s), mean {t:.3f} s per step"}
+
+
+def general_result(args, cfg, wl, dev, nbytes):
+    """Several query tokens per sequence and/or a sliding window: a step is
+    the append of every new token (kv_append, in position order) followed by
+    pkv_paged_attention; the roofline entry times that attention call
+    (partition + merge) with event pairs."""
+    import torch
+    from paged_kv_decode_06_amd import ops
+
+    pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
+    copies = args.copies or max(2, int(np.ceil(2.0e9 / pool_bytes)))
+    stream = torch.cuda.Stream(device=dev)
+    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": 2}[wl.kv_dtype]
+    mq = int(wl.q_lens.max())
+    ws = torch.zeros(ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd,
+                                                   mq), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(wl.q)
+    pos = np.concatenate([np.arange(q) for q in wl.q_lens])
+    # a quantised cache needs the tokens of one sequence appended in order
+    groups = [wl.slot_mapping] if wl.kv_dtype == "bf16" else [
+        torch.from_numpy(np.where(pos == i, wl.slot_mapping_np, -1).astype(np.int32)).to(dev)
+        for i in range(mq)]
+    caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
+    for _ in range(copies - 1):
+        caches.append(tuple(None if t is None else t.clone() for t in caches[0]))
+    steps = []
+    for kc, vc, ks, vs in caches:
+        apps = [ops.PreparedAppend(wl.k_new, wl.v_new, g, kc, vc, ks, vs, stream=stream)
+                for g in groups]
+        att = ops.PreparedGeneralAttention(wl.q, kc, vc, wl.block_tables, wl.context_lens,
+                                           wl.scale, out, q_start=wl.q_start, max_q_len=mq,
+                                           sinks=wl.sinks, window=wl.window, k_scale=ks,
+                                           v_scale=vs, workspace=ws, stream=stream)
+        steps.append((apps, att))
+    torch.cuda.synchronize()
+    K, Wm = args.steps, args.warmup
+
+    def run(i):
+        apps, att = steps[i % copies]
+        for a in apps:
+            a()
+        att()
+
+    with torch.cuda.stream(stream):
+        for i in range(Wm):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            run(Wm + i)
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for i in range(K):
+            apps, att = steps[(Wm + i) % copies]
+            for a in apps:
+                a()
+            ev[i][0].record(stream)
+            att()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+    att_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (att_ms * 1e-3) / 1e9
+    keys, _ = visible_keys(wl)
+    result = {
+        "metric": "KV-read GB/s per decode-attention step (1 MI355X)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}", "kv_dtype": wl.kv_dtype,
+            "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.BS,
+            "q_len": mq, "sinks": wl.sinks, "window": wl.window,
+            "sum_context": int(wl.lengths.sum()), "keys_seen": int(keys.sum()),
+            "num_blocks": wl.NB, "kv_bytes_per_step": nbytes, "kv_cache_copies_cycled": copies,
+            "step": "kv_append of the new tokens + paged_attention (partition + merge)",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "paged_attention call (mfma_partition_kernel + merge)",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        },
+        "detail": {
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+            "attention_call_us_mean": round(att_ms * 1e3, 2),
+            "query_rows_heads_per_s": round(int(wl.q_start_np[-1]) * wl.Hq / (ms_per_step * 1e-3), 1),
+        },
+    }
+    return result
 
 
 def main():
@@ -156,6 +278,12 @@ def main():
     cfg = W.CONFIGS[args.config]
     wl = W.make_config_workload(args.config, device=dev, poison=False)
     nbytes = kv_bytes(wl)
+    if cfg.q_len > 1 or cfg.window > 0:
+        result = general_result(args, cfg, wl, dev, nbytes)
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(wl)
+        print(json.dumps(result), flush=True)
+        return
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = args.copies or max(2, int(np.ceil(2.0e9 / pool_bytes)))
 

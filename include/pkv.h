@@ -132,6 +132,43 @@ int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cac
                            int NB, int MBS, int kv_dtype, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* Generalised paged attention: several query tokens per sequence with the
+ * bottom-right aligned causal mask ("Prefill Forward Prefix Caching
+ * Explained", the section on how the causal mask handles the prefix: query i
+ * of q_len new tokens sees key j iff j <= i + kv_len - q_len), and optionally
+ * a sliding window with attention sinks (the "Decode Phase" glossary's
+ * long-context bullets: only the most recent tokens, plus the first few
+ * kept to stabilise attention).
+ *   Sequence b has L_b = context_lens[b] keys (its new tokens included, as
+ *   stored by pkv_kv_append beforehand) and q_len_b = q_start[b+1] -
+ *   q_start[b] queries, the q/out rows q_start[b] .. q_start[b+1]-1 (with
+ *   q_start NULL: one query, row b, and max_q_len must be 1).  Query i sees
+ *   key j iff j <= lim = L_b - q_len_b + i and, when window_tokens > 0, also
+ *   j > lim - window_tokens or j < sink_tokens.  out[row, h, :] is the
+ *   softmax(scale <q, K_j>) weighted sum of V_j over the keys it sees, as in
+ *   pkv_paged_decode_attention; a query that sees no key gets 0.
+ *   q, out  [total_q, Hq, D] bf16; q_start [B + 1] int32 (device), with
+ *   q_len_b <= max_q_len (larger ones are clamped); G * max_q_len <= 16
+ *   (one wave serves all of a sequence's queries of one kv head).  Other
+ *   arguments as for pkv_paged_decode_attention; the workspace comes from
+ *   pkv_paged_attention_workspace_bytes with the same max_q_len.
+ * Always runs the MFMA partition kernel (the VALU variant serves one query
+ * per sequence without a window).  With q_start NULL, max_q_len 1 and
+ * window_tokens 0 the result is bit-identical to
+ * pkv_paged_decode_attention. */
+int pkv_paged_attention(const void* q, const int32_t* q_start, int max_q_len,
+                        const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, int sink_tokens,
+                        int window_tokens, void* out, int B, int Hq, int Hkv, int D, int BS,
+                        int NB, int MBS, int kv_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Workspace bytes for pkv_paged_attention with at most max_q_len queries per
+ * sequence (0 for sizes the library does not support). */
+size_t pkv_paged_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                           int kv_dtype, int max_q_len);
+
 /* One decode step: the append of each sequence's new token followed by
  * attention, in one call ("tiny-vllm part 5": the new token's K/V is written
  * into its block before attention reads the history; "Decode Phase Attention

@@ -10,6 +10,9 @@ Two operations sit behind a C-ABI shared library (``libpkv.so``, declared in
   whole paged history (GQA grouping, no causal mask, exact masking of
   everything past ``context_lens``), split over the context with a
   log-sum-exp merge;
+* ``paged_attention``: the generalised call -- several query tokens per
+  sequence with the bottom-right causal mask, and an optional sliding window
+  with attention sinks;
 * ``decode_step``: both in one call (the append runs inside the attention's
   partition kernel), bit-identical to the two calls in sequence.
 
@@ -23,6 +26,8 @@ from .ops import (  # noqa: F401
     PkvError,
     decode_step,
     kv_append,
+    paged_attention,
+    attention_workspace_bytes,
     paged_decode_attention,
     paged_decode_merge,
     paged_decode_partition,

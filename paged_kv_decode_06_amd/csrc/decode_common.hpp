@@ -4,6 +4,12 @@
 // token per sequence attends, with no causal mask, over positions
 // t < context_lens[b] of its history; position t lives at
 // (block_tables[b][t / BS], t % BS); query head h reads kv head h / G.
+// Generalised ("Prefill Forward Prefix Caching Explained", the bottom-right
+// causal mask; the "Decode Phase" glossary's sliding-window and attention-sink
+// bullets): sequence b has q_len query tokens, the last q_len of its L
+// positions; query i sees key j iff j <= lim = L - q_len + i and, with a
+// window W > 0, also j > lim - W or j < sinks.  Only pages holding a key
+// some query sees are on the work axis: the sink pages and the window pages.
 // The pages' route gathers the history into a zero-padded dense tensor and
 // calls a dense kernel; here nothing is gathered: each wave reads the pages
 // in place through the block table, and positions past the context length
@@ -32,21 +38,52 @@
 
 namespace pkv {
 
+// Query tokens of sequence b (1 without q_start), clamped to [0, max_q].
+__device__ __forceinline__ int seq_queries(const AttnParams& p, int b) {
+  if (p.q_start == nullptr) return 1;
+  return min(max(p.q_start[b + 1] - p.q_start[b], 0), p.max_q);
+}
+
+// Context length of sequence b, clamped to [0, MBS * BS].
+__device__ __forceinline__ int seq_length(const AttnParams& p, int b, int BS) {
+  return min(max(p.context_lens[b], 0), p.MBS * BS);
+}
+
+// The pages of a sequence on the work axis: axis page j' < ps is table page
+// j'; axis page j' >= ps is table page j' + gap.  Without a window (or when
+// the sink pages reach the window) that is every page up to ceil(L / BS);
+// otherwise the sink pages [0, ceil(sinks / BS)) and the window pages from
+// the one holding L - q_len - W + 1 (the oldest key query 0 sees).
+struct SeqRange {
+  int n, ps, gap;
+};
+
+__device__ __forceinline__ SeqRange seq_range(int L, int ql, int sinks, int window, int BS) {
+  const int pe = (L + BS - 1) / BS;
+  if (window <= 0) return {pe, pe, 0};
+  const int lo = max(L - ql - window + 1, 0);
+  const int pw = lo / BS;
+  const int ps = min((sinks + BS - 1) / BS, pe);
+  if (pw <= ps) return {pe, pe, 0};
+  return {ps + (pe - pw), ps, pw - ps};
+}
+
+__device__ __forceinline__ int seq_pages(const AttnParams& p, int b, int BS) {
+  return seq_range(seq_length(p, b, BS), seq_queries(p, b), p.sinks, p.window, BS).n;
+}
+
 // Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]).
 // Called by every thread of the workgroup.
-__device__ inline void build_prefix(const int32_t* __restrict__ context_lens, int B, int BS,
-                                    int MBS, int32_t* s_pre, int32_t* s_tmp) {
+__device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
+                                    int32_t* s_tmp) {
+  const int B = p.B;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
   const int per = (B + nt - 1) / nt;
   const int b0 = tid * per;
   const int b1 = min(B, b0 + per);
-  const int max_len = MBS * BS;
   int sum = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int L = min(max(context_lens[b], 0), max_len);
-    sum += (L + BS - 1) / BS;
-  }
+  for (int b = b0; b < b1; ++b) sum += seq_pages(p, b, BS);
   s_tmp[tid] = sum;
   __syncthreads();
   // Hillis-Steele inclusive scan of the per-thread sums
@@ -59,8 +96,7 @@ __device__ inline void build_prefix(const int32_t* __restrict__ context_lens, in
   int run = tid == 0 ? 0 : s_tmp[tid - 1];
   for (int b = b0; b < b1; ++b) {
     s_pre[b] = run;
-    const int L = min(max(context_lens[b], 0), max_len);
-    run += (L + BS - 1) / BS;
+    run += seq_pages(p, b, BS);
   }
   if (tid == nt - 1) s_pre[B] = s_tmp[nt - 1];
   __syncthreads();

@@ -1,10 +1,13 @@
 // Log-sum-exp merge of the partition kernel's per-wave shares.
 //
-// For a (sequence, query head) whose history was split over pieces k0..k1,
-// share p holds m_p (max score, exp2 domain), l_p = sum_t exp2(s_t - m_p)
-// and o_p = sum_t exp2(s_t - m_p) v_t.  With M = max_p m_p:
+// For a (sequence, query token, query head) whose history was split over
+// pieces k0..k1, share p holds m_p (max score, exp2 domain),
+// l_p = sum_t exp2(s_t - m_p) and o_p = sum_t exp2(s_t - m_p) v_t over the
+// keys the query sees in that piece.  With M = max_p m_p:
 //   out = sum_p exp2(m_p - M) o_p / sum_p exp2(m_p - M) l_p,
-// which is the softmax over the whole history.
+// which is the softmax over every key the query sees (0 if it sees none).
+// Output rows are (b, i, h) for query i < q_len_b; the share column of
+// query i, head h = g G + jj is i G + jj.
 
 #include <float.h>
 
@@ -26,18 +29,22 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
   const int lane = threadIdx.x & (kWave - 1);
   const int sub = lane / TPR;
   const int d4 = (lane % TPR) * 4;
-  const int64_t bh = (int64_t)blockIdx.x * kAttnWavesPerBlock + (threadIdx.x >> 6);
-  if (bh >= (int64_t)p.B * p.Hq) return;
-  const int b = (int)(bh / p.Hq);
-  const int h = (int)(bh % p.Hq);
+  const int64_t bqh = (int64_t)blockIdx.x * kAttnWavesPerBlock + (threadIdx.x >> 6);
+  if (bqh >= (int64_t)p.B * p.max_q * p.Hq) return;
+  const int b = (int)(bqh / ((int64_t)p.max_q * p.Hq));
+  const int qi = (int)(bqh / p.Hq % p.max_q);
+  const int h = (int)(bqh % p.Hq);
+  if (qi >= seq_queries(p, b)) return;
   const int g = h / G;
-  const int jj = h % G;
+  const int col = qi * G + h % G;
+  const int C = p.cols;
   const int Hkv = p.Hkv;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
   const int total = Hkv * pre_B;
   const int n_b = pre_b1 - pre_b;
-  uint16_t* op = static_cast<uint16_t*>(p.out) + bh * D;
+  const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
+  uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D;
   if (n_b == 0) {                              // empty history: defined as 0
     if (lane < TPR) *reinterpret_cast<uint2*>(op + d4) = make_uint2(0, 0);
     return;
@@ -54,14 +61,14 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
   const float* __restrict__ po = p.ws_o;
 
   float M = -FLT_MAX;
-  for (int i = lane; i < P; i += kWave) M = fmaxf(M, ml[((rok0 + i) * G + jj) * 2]);
+  for (int i = lane; i < P; i += kWave) M = fmaxf(M, ml[((rok0 + i) * C + col) * 2]);
   M = wave_max(M);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
 #pragma unroll 8
   for (int i = sub; i < P; i += RPW) {
-    const int64_t row = (rok0 + i) * G + jj;
+    const int64_t row = (rok0 + i) * C + col;
     const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
     const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
     const float w = fast_exp2(mlv.x - M);
@@ -80,7 +87,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
     den += __shfl_xor(den, off);
   }
   if (lane < TPR) {
-    const float inv = 1.0f / den;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // 0: the query sees no key
     *reinterpret_cast<uint2*>(op + d4) =
         make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
   }
@@ -100,17 +107,21 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   const int t = threadIdx.x;
   const int grp = t / TPR;
   const int d4 = (t % TPR) * 4;
-  const int64_t bh = blockIdx.x;
-  const int b = (int)(bh / p.Hq);
-  const int h = (int)(bh % p.Hq);
+  const int64_t bqh = blockIdx.x;
+  const int b = (int)(bqh / ((int64_t)p.max_q * p.Hq));
+  const int qi = (int)(bqh / p.Hq % p.max_q);
+  const int h = (int)(bqh % p.Hq);
+  if (qi >= seq_queries(p, b)) return;
   const int g = h / G;
-  const int jj = h % G;
+  const int col = qi * G + h % G;
+  const int C = p.cols;
   const int Hkv = p.Hkv;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
   const int total = Hkv * pre_B;
   const int n_b = pre_b1 - pre_b;
-  uint16_t* op = static_cast<uint16_t*>(p.out) + bh * D;
+  const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
+  uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D;
   if (n_b == 0) {
     if (t < TPR) *reinterpret_cast<uint2*>(op + d4) = make_uint2(0, 0);
     return;
@@ -127,7 +138,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   const float* __restrict__ po = p.ws_o;
 
   float m_loc = -FLT_MAX;
-  for (int i = t; i < P; i += kAttnBlockThreads) m_loc = fmaxf(m_loc, ml[((row0 + i) * G + jj) * 2]);
+  for (int i = t; i < P; i += kAttnBlockThreads) m_loc = fmaxf(m_loc, ml[((row0 + i) * C + col) * 2]);
   m_loc = wave_max(m_loc);
   if ((t & (kWave - 1)) == 0) s_max[t >> 6] = m_loc;
   __syncthreads();
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   float den = 0.0f;
 #pragma unroll 4
   for (int i = grp; i < P; i += NGRP) {
-    const int64_t row = (row0 + i) * G + jj;
+    const int64_t row = (row0 + i) * C + col;
     const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
     const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
     const float w = fast_exp2(mlv.x - M);
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
       sum.w += v.w;
       dsum += s_den[q];
     }
-    const float inv = 1.0f / dsum;
+    const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;   // 0: the query sees no key
     *reinterpret_cast<uint2*>(op + d4) =
         make_uint2(pack_bf16x2(sum.x * inv, sum.y * inv), pack_bf16x2(sum.z * inv, sum.w * inv));
   }
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
 constexpr int64_t kWideMergeRows = 1024;
 
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.B * p.Hq;
+  const int64_t rows = (int64_t)p.B * p.max_q * p.Hq;
   if (rows == 0) return hipSuccess;
   if (rows < kWideMergeRows) {
     if (D == 128)

@@ -104,17 +104,19 @@ __device__ __forceinline__ uint4 load_nt(const unsigned char* p) {
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
 // Store one 16-token tile (this lane's NI chunks, already in registers) into
-// the wave's LDS buffer as bf16 rows of PITCH bytes.  Rows at or past `live`
-// are written as zeros when `zero_dead` (V: P = 0 must meet V = 0, not NaN).
+// the wave's LDS buffer as bf16 rows of PITCH bytes.  When `zero_dead`, rows
+// at or past `live` and rows in [gap_lo, gap_hi) (keys between the sinks and
+// the window) are written as zeros (V: P = 0 must meet V = 0, not NaN).
 template <class S>
 __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch)[S::NI],
-                                           int lane, int live, bool zero_dead) {
+                                           int lane, int live, bool zero_dead, int gap_lo = 0,
+                                           int gap_hi = 0) {
   const int rr = lane / S::LPR, c = lane % S::LPR;
 #pragma unroll
   for (int s = 0; s < S::NI; ++s) {
     const int row = s * S::RPI + rr;
     uint4 v = ch[s];
-    if (zero_dead && row >= live) v = make_uint4(0, 0, 0, 0);
+    if (zero_dead && (row >= live || (row >= gap_lo && row < gap_hi))) v = make_uint4(0, 0, 0, 0);
     unsigned char* dst = tile + row * S::PITCH;
     if constexpr (S::FP8) {
       bf16x8_t lo, hi;
@@ -218,7 +220,9 @@ __device__ __forceinline__ void take_new_row(const unsigned char* row, unsigned 
         *reinterpret_cast<const uint4*>(row + 16 * lane);
 }
 
-template <class S>
+// GEN: the generalised call (several queries per sequence, a window); the
+// decode instantiations (GEN = false) carry none of its per-lane state.
+template <class S, bool GEN>
 __global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU, PKV_MFMA_WAVES_PER_EU)))
 void mfma_partition_kernel(const AttnParams p) {
   constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB;
@@ -228,7 +232,7 @@ void mfma_partition_kernel(const AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
   int32_t* s_tmp = s_pre + p.B + 1;                          // [blockDim]
-  build_prefix(p.context_lens, p.B, BS, p.MBS, s_pre, s_tmp);
+  build_prefix(p, BS, s_pre, s_tmp);
 
   const int Hkv = p.Hkv;
   const int total = Hkv * s_pre[p.B];
@@ -265,19 +269,32 @@ void mfma_partition_kernel(const AttnParams p) {
     const int L_in = p.context_lens[b];
     const int L = min(max(L_in, 0), p.MBS * BS);
     // a length outside [1, MBS * BS] breaks the contract: no append then
-    const bool append = p.k_new != nullptr && L == L_in && L >= 1;
+    // (the decode step is one query per sequence: never the GEN instantiation)
+    const bool append = !GEN && p.k_new != nullptr && L == L_in && L >= 1;
     const int32_t* bt_row = p.block_tables + (int64_t)b * p.MBS;
     const int64_t head_off = (int64_t)g * RB + load_off;
+    // query tokens: column n of S^T / row n of O is query n / G, head n % G
+    const int ql = GEN ? seq_queries(p, b) : 1;
+    const int ncol = G * ql;
+    const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;   // first q / out row
+    const SeqRange sr = GEN ? seq_range(L, ql, p.sinks, p.window, BS) : SeqRange{0, 0, 0};
+    auto table_page = [&](int j) { return !GEN || j < sr.ps ? j : j + sr.gap; };
+    // keys column n sees: j <= lim_n (bottom-right causal), and with a window
+    // j >= lo_n or j < sinks
+    const int lim_n = n < ncol ? L - ql + n / G : -1;
+    const int lo_n = lim_n - p.window + 1;
+    const bool windowed = GEN && p.window > 0;
+    const int gap_end = L - ql - p.window + 1;    // keys in [sinks, gap_end) no query sees
 
     // q of the group as the B operand: element i of k-step kk is head dim
     // 32 kk + 8 r + i, the same dims the K operand's element i holds
     bf16x8_t qB[NKK];
     {
-      const uint16_t* qrow = qp + ((int64_t)b * p.Hq + g * G + n) * D + 8 * r;
+      const uint16_t* qrow = qp + ((int64_t)(r0 + n / G) * p.Hq + g * G + n % G) * D + 8 * r;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < G) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+        if (n < ncol) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
         qB[kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
@@ -304,7 +321,7 @@ void mfma_partition_kernel(const AttnParams p) {
       int phys_l = 0;
       bool valid_l = false;
       if (lane < nchunk) {
-        const int v = bt_row[jc + lane];
+        const int v = bt_row[table_page(jc + lane)];
         valid_l = (unsigned)v < (unsigned)p.NB;
         phys_l = valid_l ? v : 0;
       }
@@ -332,7 +349,7 @@ void mfma_partition_kernel(const AttnParams p) {
       const int nunits = nchunk * SUB;
       for (int u = 0; u < nunits; ++u) {
         const int k = u / SUB, sb = u % SUB;
-        const int tok0 = (jc + k) * BS + sb * 16;   // position of the tile's first token
+        const int tok0 = table_page(jc + k) * BS + sb * 16;   // position of the tile's first token
         const int live = L - tok0;                  // rows of the tile inside the history
         // the decode step's new token goes to row live - 1 of this tile
         const bool new_tile = new_here && k == k_last && live >= 1 && live <= 16;
@@ -379,10 +396,18 @@ void mfma_partition_kernel(const AttnParams p) {
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], s, 0, 0, 0);
         }
         const float c = S::FP8 ? p.scale_log2 * ksc : p.scale_log2;
+        // rows past a_rel are in column n's future (decode: past the history)
+        const int a_rel = GEN ? lim_n - tok0 : live - 1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s[i] *= c;
-          if (4 * r + i >= live) s[i] = -INFINITY;
+          if (4 * r + i > a_rel) s[i] = -INFINITY;
+        }
+        if (windowed) {
+          const int lo_rel = lo_n - tok0, sk_rel = p.sinks - tok0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * r + i < lo_rel && 4 * r + i >= sk_rel) s[i] = -INFINITY;
         }
 
         // online softmax, one max per head (column n)
@@ -412,7 +437,10 @@ void mfma_partition_kernel(const AttnParams p) {
 
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
         // order within a wave) -> transposed B operands, O += P V
-        stage_tile<S>(tile, vb, lane, live, true);
+        if (windowed)
+          stage_tile<S>(tile, vb, lane, live, true, p.sinks - tok0, gap_end - tok0);
+        else
+          stage_tile<S>(tile, vb, lane, live, true);
         if (new_tile) take_new_row<S>(new_rows + 2 * D, tile, live - 1, lane);
 #pragma unroll
         for (int nb = 0; nb < NBN; ++nb) {
@@ -436,10 +464,11 @@ void mfma_partition_kernel(const AttnParams p) {
       uint16_t* op = static_cast<uint16_t*>(p.out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r + i;
-        if (h < G) {
-          const float inv = 1.0f / l_row[i];
-          uint16_t* orow = op + ((int64_t)b * p.Hq + g * G + h) * D + n;
+        const int c = 4 * r + i;   // O row: query c / G, head c % G
+        if (c < ncol) {
+          // (a query that sees no key gets 0)
+          const float inv = !GEN || l_row[i] > 0.0f ? 1.0f / l_row[i] : 0.0f;
+          uint16_t* orow = op + ((int64_t)(r0 + c / G) * p.Hq + g * G + c % G) * D + n;
 #pragma unroll
           for (int nb = 0; nb < NBN; ++nb)
             orow[16 * nb] = (uint16_t)f32_to_bf16_rne(O[nb][i] * inv);
@@ -447,17 +476,18 @@ void mfma_partition_kernel(const AttnParams p) {
       }
     } else {
       const int64_t row = (int64_t)piece + seg;
+      const int C = p.cols;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r + i;
-        if (h < G) {
-          float* orow = p.ws_o + (row * G + h) * D + n;
+        const int c = 4 * r + i;
+        if (c < ncol) {
+          float* orow = p.ws_o + (row * C + c) * D + n;
 #pragma unroll
           for (int nb = 0; nb < NBN; ++nb) orow[16 * nb] = O[nb][i];
         }
       }
-      if (lane < G)
-        *reinterpret_cast<float2*>(p.ws_ml + (row * G + lane) * 2) = make_float2(m_run, l_tot);
+      if (lane < ncol)
+        *reinterpret_cast<float2*>(p.ws_ml + (row * C + lane) * 2) = make_float2(m_run, l_tot);
     }
     x = pc.run_start + pc.j1;
   }
@@ -474,25 +504,34 @@ static size_t mfma_lds_total(int B, int D) {
   return ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D);
 }
 
+// Occupancy of the decode instantiation; the generalised one is held to the
+// same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves both.
 int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
-  int blocks = 0;
+  int blocks = 0, blocks_gen = 0;
   const size_t lds = mfma_lds_total(B, D);
   const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, fp8, [&](auto s) {
     using S = decltype(s);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S, false>,
+                                                     kAttnBlockThreads, lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
                                                      kAttnBlockThreads, lds) != hipSuccess)
-      blocks = 0;
+      blocks = blocks_gen = 0;
   });
-  return ok ? blocks : 0;
+  return ok ? (blocks < blocks_gen ? blocks : blocks_gen) : 0;
 }
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
                                  hipStream_t stream) {
   const size_t lds = mfma_lds_total(p.B, D);
+  const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
   const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, fp8, [&](auto s) {
     using S = decltype(s);
-    hipLaunchKernelGGL(mfma_partition_kernel<S>, dim3(blocks), dim3(kAttnBlockThreads), lds,
-                       stream, p);
+    if (gen)
+      hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks), dim3(kAttnBlockThreads),
+                         lds, stream, p);
+    else
+      hipLaunchKernelGGL((mfma_partition_kernel<S, false>), dim3(blocks), dim3(kAttnBlockThreads),
+                         lds, stream, p);
   });
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

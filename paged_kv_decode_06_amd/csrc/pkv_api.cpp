@@ -61,9 +61,8 @@ int cu_count(int dev) {
 
 // LDS of the partition kernel grows with B; occupancy is looked up for B
 // rounded up to a multiple of 1024 so that the cache stays small.
-int blocks_per_cu(int dev, int D, int BS, int G, bool fp8, int B) {
+int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, bool fp8, int B) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const pkv::AttnPath path = pkv::attn_path();
   const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
                                  ((unsigned long long)G << 16) | ((unsigned long long)fp8 << 15) |
@@ -88,26 +87,55 @@ bool supported(int D, int BS, int G, int kv_dtype) {
 }
 
 // Persistent grid: every workgroup that fits at once on every CU.
-int attention_blocks(int D, int BS, int G, int kv_dtype, int B) {
+int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B) {
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
-  const int per_cu = blocks_per_cu(dev, D, BS, G, kv_dtype == PKV_KV_FP8_E4M3FN, B);
+  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype == PKV_KV_FP8_E4M3FN, B);
   return ncu * per_cu;
 }
 
 struct AttnCall {
   pkv::AttnParams p;
+  pkv::AttnPath path;
   int D, BS, G, blocks;
   bool fp8;
 };
+
+// Options beyond one query per sequence; the defaults are the decode call.
+struct QueryOpts {
+  const int32_t* q_start = nullptr;
+  int max_q = 1;
+  int sinks = 0;
+  int window = 0;
+  bool general = false;   // the generalised call: always the MFMA kernel
+};
+
+// The largest G * max_q one partition wave serves (the 16 MFMA columns).
+constexpr int kMaxCols = 16;
+
+int check_query_opts(const QueryOpts& o, int G) {
+  if (o.max_q < 1) return fail(PKV_ERR_SHAPE, "max_q_len=%d must be at least 1", o.max_q);
+  if (o.q_start == nullptr && o.max_q != 1)
+    return fail(PKV_ERR_SHAPE, "max_q_len=%d needs q_start (NULL means one query each)", o.max_q);
+  if ((long long)G * o.max_q > kMaxCols)
+    return fail(PKV_ERR_UNSUPPORTED, "G * max_q_len = %d * %d exceeds %d", G, o.max_q, kMaxCols);
+  if (o.sinks < 0 || o.window < 0)
+    return fail(PKV_ERR_SHAPE, "sink_tokens=%d and window_tokens=%d must be >= 0", o.sinks, o.window);
+  return PKV_OK;
+}
+
+pkv::AttnPath path_for(const QueryOpts& o) {
+  return o.general ? pkv::AttnPath::kMfma : pkv::attn_path();
+}
 
 int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
                       const float* k_scale, const float* v_scale, const int32_t* block_tables,
                       const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
                       int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
                       size_t workspace_bytes, AttnCall* call, bool step = false,
-                      const void* k_new = nullptr, const void* v_new = nullptr) {
+                      const void* k_new = nullptr, const void* v_new = nullptr,
+                      const QueryOpts& opts = QueryOpts()) {
   g_last_error.clear();
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0 || MBS <= 0)
     return fail(PKV_ERR_SHAPE, "sizes must be positive (B may be 0): B=%d Hq=%d Hkv=%d D=%d BS=%d NB=%d MBS=%d",
@@ -116,6 +144,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const int G = Hq / Hkv;
   if (!supported(D, BS, G, kv_dtype))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d G=%d kv_dtype=%d", D, BS, G, kv_dtype);
+  if (int st = check_query_opts(opts, G)) return st;
   if (B > pkv::kMaxBatch) return fail(PKV_ERR_UNSUPPORTED, "B=%d exceeds %d", B, pkv::kMaxBatch);
   if ((long long)MBS * BS > (1LL << 30))
     return fail(PKV_ERR_SHAPE, "MBS*BS=%lld is too large", (long long)MBS * BS);
@@ -123,6 +152,8 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
   if (step && (!k_new || !v_new)) return fail(PKV_ERR_NULL, "k_new and v_new are required");
+  if ((((uintptr_t)opts.q_start) & 3u) != 0)
+    return fail(PKV_ERR_ALIGN, "q_start must be 4-byte aligned");
   const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
   if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
   if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
@@ -132,10 +163,12 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
     return fail(PKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
   if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
-  const int blocks = attention_blocks(D, BS, G, kv_dtype, B);
+  const pkv::AttnPath path = path_for(opts);
+  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
-  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv, G, D, waves);
+  const int cols = G * opts.max_q;
+  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv, cols, D, waves);
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, lay.total);
@@ -156,6 +189,11 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.Hkv = Hkv;
   p.NB = NB;
   p.MBS = MBS;
+  p.q_start = opts.q_start;
+  p.max_q = opts.max_q;
+  p.cols = cols;
+  p.sinks = opts.sinks;
+  p.window = opts.window;
   p.total_waves = waves;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
@@ -167,6 +205,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.v_cache_w = nullptr;
   p.k_scale_w = nullptr;
   p.v_scale_w = nullptr;
+  call->path = path;
   call->D = D;
   call->BS = BS;
   call->G = G;
@@ -176,7 +215,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
 }
 
 hipError_t launch_partition(const AttnCall& c, hipStream_t s) {
-  return pkv::attn_path() == pkv::AttnPath::kMfma
+  return c.path == pkv::AttnPath::kMfma
              ? pkv::launch_partition_mfma(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s)
              : pkv::launch_partition_valu(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s);
 }
@@ -222,18 +261,64 @@ int pkv_partition_kernel(void) { return (int)pkv::attn_path(); }
 
 int pkv_attention_waves(int D, int BS, int G, int kv_dtype) {
   if (!supported(D, BS, G, kv_dtype)) return 0;
-  return attention_blocks(D, BS, G, kv_dtype, 1) * pkv::kAttnWavesPerBlock;
+  return attention_blocks(pkv::attn_path(), D, BS, G, kv_dtype, 1) * pkv::kAttnWavesPerBlock;
 }
+
+}  // extern "C"
+
+namespace {
+size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int kv_dtype,
+                           int max_q, bool general) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || MBS <= 0 || Hq % Hkv != 0 || max_q < 1) return 0;
+  const int G = Hq / Hkv;
+  if (!supported(D, BS, G, kv_dtype) || B > pkv::kMaxBatch || G * max_q > kMaxCols) return 0;
+  QueryOpts o;
+  o.general = general;
+  const int blocks = attention_blocks(path_for(o), D, BS, G, kv_dtype, B);
+  if (blocks <= 0) return 0;
+  const int waves = blocks * pkv::kAttnWavesPerBlock;
+  return pkv::workspace_layout(B, Hkv, G * max_q, D, waves).total;
+}
+}  // namespace
+
+extern "C" {
 
 size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
                                         int kv_dtype) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || MBS <= 0 || Hq % Hkv != 0) return 0;
-  const int G = Hq / Hkv;
-  if (!supported(D, BS, G, kv_dtype) || B > pkv::kMaxBatch) return 0;
-  const int blocks = attention_blocks(D, BS, G, kv_dtype, B);
-  if (blocks <= 0) return 0;
-  const int waves = blocks * pkv::kAttnWavesPerBlock;
-  return pkv::workspace_layout(B, Hkv, G, D, waves).total;
+  return workspace_bytes_for(B, Hq, Hkv, D, BS, MBS, kv_dtype, 1, false);
+}
+
+size_t pkv_paged_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                           int kv_dtype, int max_q_len) {
+  return workspace_bytes_for(B, Hq, Hkv, D, BS, MBS, kv_dtype, max_q_len, true);
+}
+
+int pkv_paged_attention(const void* q, const int32_t* q_start, int max_q_len,
+                        const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, int sink_tokens,
+                        int window_tokens, void* out, int B, int Hq, int Hkv, int D, int BS,
+                        int NB, int MBS, int kv_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  QueryOpts o;
+  o.q_start = q_start;
+  o.max_q = max_q_len;
+  o.sinks = sink_tokens;
+  o.window = window_tokens;
+  o.general = true;
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call, false, nullptr, nullptr, o);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  if (q_start == nullptr && max_q_len != 1)
+    return fail(PKV_ERR_SHAPE, "max_q_len > 1 needs q_start");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partition(call, s);
+  if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  e = pkv::launch_merge(call.p, call.D, call.G, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
 }
 
 int pkv_paged_decode_partition(const void* q, const void* k_cache, const void* v_cache,
@@ -305,7 +390,7 @@ int decode_step_impl(const void* q, const void* k_new, const void* v_new, void* 
   if (B == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (pkv::attn_path() == pkv::AttnPath::kMfma) {
+  if (call.path == pkv::AttnPath::kMfma) {
     pkv::AttnParams& p = call.p;
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);

@@ -21,11 +21,19 @@ struct AttnParams {
   void* out;
   float scale_log2;     // softmax scale * log2(e): scores live in the exp2 domain
   int B, Hq, Hkv, NB, MBS;
+  // Query tokens (bottom-right causal, see decode_common.hpp): sequence b
+  // owns q/out rows q_start[b] .. q_start[b+1]-1 (q_start NULL: row b only);
+  // at most max_q of them, G * max_q <= 16.  cols = G * max_q columns per
+  // share row.  window > 0 hides keys more than window - 1 positions behind a
+  // query except the first `sinks` positions.
+  const int32_t* q_start;
+  int max_q, cols;
+  int sinks, window;
   int total_waves;      // persistent waves of the partition grid
   // workspace (see workspace_layout)
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
-  float* ws_ml;         // [rows, G, 2] running max (log2 domain) and sum
-  float* ws_o;          // [rows, G, D] unnormalised partial outputs
+  float* ws_ml;         // [rows, cols, 2] running max (log2 domain) and sum
+  float* ws_o;          // [rows, cols, D] unnormalised partial outputs
   // Fused append (the decode step): when k_new is non-NULL, the new token of
   // sequence b ([B, Hkv, D] bf16) is stored at position context_lens[b] - 1
   // by the wave that reads that position, which also attends to it.  The
@@ -51,14 +59,15 @@ struct WorkspaceLayout {
 #endif
 constexpr int kPiecesPerWave = PKV_PIECES_PER_WAVE;
 
-inline WorkspaceLayout workspace_layout(int B, int Hkv, int G, int D, int total_waves) {
+// `cols` = G * (query tokens per sequence, at most).
+inline WorkspaceLayout workspace_layout(int B, int Hkv, int cols, int D, int total_waves) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
   w.rows = kPiecesPerWave * total_waves + B * Hkv;
   w.pre_off = 0;
   w.ml_off = w.pre_off + up(sizeof(int32_t) * (size_t)(B + 1));
-  w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * G);
-  w.total = w.o_off + up(sizeof(float) * (size_t)w.rows * G * D);
+  w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * cols);
+  w.total = w.o_off + up(sizeof(float) * (size_t)w.rows * cols * D);
   return w;
 }
 
@@ -78,6 +87,7 @@ enum class AttnPath { kValu = 0, kMfma = 1 };
 hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
                                  hipStream_t stream);
 int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B);
+// (the VALU variant handles one query per sequence and no window only)
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
                                  hipStream_t stream);
 int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B);

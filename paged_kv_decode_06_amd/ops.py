@@ -60,6 +60,11 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = I
+        lib.pkv_paged_attention.argtypes = [P, P, I, P, P, P, P, P, P, F, I, I, P, I, I, I, I,
+                                            I, I, I, I, P, S, P]
+        lib.pkv_paged_attention.restype = I
+        lib.pkv_paged_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+        lib.pkv_paged_attention_workspace_bytes.restype = S
         for name in ("pkv_decode_step", "pkv_decode_step_partition"):
             fn = getattr(lib, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
@@ -214,6 +219,71 @@ def paged_decode_merge(q, k_cache, v_cache, block_tables, context_lens, scale, o
     args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
                       v_scale, workspace, stream)
     _check("pkv_paged_decode_merge", _load().pkv_paged_decode_merge(*args))
+
+
+def attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16, max_q_len=1) -> int:
+    return int(_load().pkv_paged_attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype,
+                                                           max_q_len))
+
+
+def _general_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, q_start,
+                  max_q_len, sinks, window, k_scale, v_scale, workspace, stream):
+    kvd = _kv_dtype(k_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(k_cache, "k_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    if kvd != KV_BF16:
+        _need(k_scale, "k_scale", torch.float32, 2)
+        _need(v_scale, "v_scale", torch.float32, 2)
+    B = context_lens.shape[0]
+    if q_start is not None:
+        _need(q_start, "q_start", torch.int32, 1)
+        if q_start.shape[0] != B + 1:
+            raise ValueError("q_start must have B + 1 entries")
+    elif q.shape[0] != B:
+        raise ValueError("without q_start, q has one row per sequence")
+    TQ, Hq, D = q.shape
+    NB, BS, Hkv, D2 = k_cache.shape
+    MBS = block_tables.shape[1]
+    if D2 != D or v_cache.shape != k_cache.shape or tuple(out.shape) != (TQ, Hq, D):
+        raise ValueError("q/out/cache shapes disagree")
+    if block_tables.shape[0] != B:
+        raise ValueError("block_tables must have B rows")
+    if workspace is None or workspace.dtype != torch.uint8 or not workspace.is_cuda:
+        raise ValueError("workspace must be a uint8 GPU tensor (see attention_workspace_bytes)")
+    return (_ptr(q), _ptr(q_start), int(max_q_len), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+            _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale),
+            int(sinks), int(window), _ptr(out), B, Hq, Hkv, D, BS, NB, MBS, kvd,
+            _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, out, q_start=None,
+                    max_q_len=1, sinks=0, window=0, k_scale=None, v_scale=None, workspace=None,
+                    stream=None) -> None:
+    """pkv_paged_attention: q_start[b] .. q_start[b+1]-1 are sequence b's query
+    rows (bottom-right causal over its L_b keys); window > 0 keeps only keys
+    within the window of each query plus the first `sinks` keys."""
+    args = _general_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, q_start,
+                         max_q_len, sinks, window, k_scale, v_scale, workspace, stream)
+    _check("pkv_paged_attention", _load().pkv_paged_attention(*args))
+
+
+class PreparedGeneralAttention:
+    """paged_attention with its arguments marshalled once (see PreparedAttention)."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, out, q_start=None,
+                 max_q_len=1, sinks=0, window=0, k_scale=None, v_scale=None, workspace=None,
+                 stream=None):
+        self._args = _general_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                   q_start, max_q_len, sinks, window, k_scale, v_scale,
+                                   workspace, stream)
+        self._lib = _load()
+
+    def __call__(self):
+        _check("pkv_paged_attention", self._lib.pkv_paged_attention(*self._args))
 
 
 def _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,

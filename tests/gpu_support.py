@@ -108,3 +108,94 @@ def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, kv_dtype: str, what
         raise AssertionError(
             f"{what}: {bad.sum()} elements out of tolerance, first at {tuple(i)}: "
             f"gpu={gpu[tuple(i)]!r} ref={ref[tuple(i)]!r}; {error_report(gpu, ref)}")
+
+
+class GeneralHost:
+    """Host (numpy) copy of a workload with several query tokens per sequence,
+    or of a subset of its sequences with their pages renumbered into a compact
+    pool, taken before the GPU runs.  The oracle appends the step's tokens in
+    position order, then runs the generalised attention."""
+
+    def __init__(self, wl: W.Workload, seqs=None):
+        BS = wl.BS
+        seqs = list(range(wl.B)) if seqs is None else list(seqs)
+        pages = [wl.block_tables_np[b, : (int(wl.lengths[b]) + BS - 1) // BS] for b in seqs]
+        old = np.concatenate(pages).astype(np.int64)
+        self.old_blocks = old
+        remap = {int(p): i for i, p in enumerate(old)}
+        idx = torch.from_numpy(old).to(wl.k_cache.device)
+        self.k = W.cache_host(wl.k_cache.index_select(0, idx)).copy()
+        self.v = W.cache_host(wl.v_cache.index_select(0, idx)).copy()
+        if wl.k_scale is not None:
+            self.ks = wl.k_scale.index_select(0, idx).cpu().numpy().copy()
+            self.vs = wl.v_scale.index_select(0, idx).cpu().numpy().copy()
+        else:
+            self.ks = self.vs = None
+        mbs = max(len(p) for p in pages)
+        self.bt = np.full((len(seqs), mbs), -1, np.int32)
+        for i, p in enumerate(pages):
+            self.bt[i, : len(p)] = [remap[int(x)] for x in p]
+        self.cl = wl.lengths[seqs].astype(np.int32)
+        qs = wl.q_start_np
+        rows = np.concatenate([np.arange(qs[b], qs[b + 1]) for b in seqs])
+        self.rows = rows                                 # q rows of the subset, in order
+        self.q_start = np.zeros(len(seqs) + 1, np.int32)
+        self.q_start[1:] = np.cumsum([qs[b + 1] - qs[b] for b in seqs])
+        sel = torch.from_numpy(rows).to(wl.q.device)
+        self.q = W.bf16_bits(wl.q.index_select(0, sel))
+        self.k_new = W.bf16_bits(wl.k_new.index_select(0, sel))
+        self.v_new = W.bf16_bits(wl.v_new.index_select(0, sel))
+        slots = []
+        for r in rows:
+            blk, off = divmod(int(wl.slot_mapping_np[r]), BS)
+            slots.append(remap[blk] * BS + off)
+        self.slots = np.array(slots, np.int32)
+        self.pos_in_seq = np.concatenate([np.arange(qs[b + 1] - qs[b]) for b in seqs])
+        self.scale = wl.scale
+        self.window, self.sinks = wl.window, wl.sinks
+
+    def append(self):
+        """In position order: a token that opens a block comes before the
+        tokens that land in it."""
+        for i in range(int(self.pos_in_seq.max()) + 1):
+            s = np.where(self.pos_in_seq == i, self.slots, -1).astype(np.int32)
+            oracle.kv_append(self.k_new, self.v_new, s, self.k, self.v, self.ks, self.vs)
+
+    def attention(self, sinks=None, window=None, nthreads=0):
+        return oracle.paged_attention(
+            self.q, self.k, self.v, self.bt, self.cl, self.scale, q_start=self.q_start,
+            sinks=self.sinks if sinks is None else sinks,
+            window=self.window if window is None else window,
+            k_scale=self.ks, v_scale=self.vs, nthreads=nthreads)
+
+
+def append_in_order(wl: W.Workload):
+    """kv_append of the step's tokens on the GPU, one position at a time (a
+    token that opens an fp8/int8 block comes before the tokens landing in it)."""
+    ql = wl.q_lens
+    pos = np.concatenate([np.arange(q) for q in ql])
+    for i in range(int(ql.max())):
+        s = torch.from_numpy(np.where(pos == i, wl.slot_mapping_np, -1).astype(np.int32))
+        ops.kv_append(wl.k_new, wl.v_new, s.to(wl.q.device), wl.k_cache, wl.v_cache,
+                      wl.k_scale, wl.v_scale)
+
+
+def general_step(wl: W.Workload, sinks=None, window=None, out=None, workspace=None,
+                 append=True) -> torch.Tensor:
+    """The step's appends, then the generalised attention; returns out."""
+    if append:
+        append_in_order(wl)
+    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": 2}[wl.kv_dtype]
+    mq = int(wl.q_lens.max())
+    if workspace is None:
+        n = ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd, mq)
+        assert n > 0
+        workspace = torch.zeros(n, dtype=torch.uint8, device=wl.q.device)
+    if out is None:
+        out = torch.empty_like(wl.q)
+    ops.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.scale,
+                        out, q_start=wl.q_start, max_q_len=mq,
+                        sinks=wl.sinks if sinks is None else sinks,
+                        window=wl.window if window is None else window,
+                        k_scale=wl.k_scale, v_scale=wl.v_scale, workspace=workspace)
+    return out
