@@ -157,7 +157,7 @@ def general_result(args, cfg, wl, dev, nbytes):
     pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
     copies = args.copies or max(2, int(np.ceil(2.0e9 / pool_bytes)))
     stream = torch.cuda.Stream(device=dev)
-    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": 2}[wl.kv_dtype]
+    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": ops.KV_INT8}[wl.kv_dtype]
     mq = int(wl.q_lens.max())
     ws = torch.zeros(ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd,
                                                    mq), dtype=torch.uint8, device=dev)
@@ -288,7 +288,7 @@ def main():
     copies = args.copies or max(2, int(np.ceil(2.0e9 / pool_bytes)))
 
     stream = torch.cuda.Stream(device=dev)
-    kvd = ops.KV_FP8 if wl.kv_dtype == "fp8" else ops.KV_BF16
+    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": ops.KV_INT8}[wl.kv_dtype]
     ws = torch.zeros(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(wl.q)

@@ -14,8 +14,9 @@
  *     16-token blocks: the new token's rows are written at
  *     (slot / block_size, slot % block_size) before attention runs.
  *   - the "Decode Phase" glossary (memory-bound decode; KV-cache quantisation
- *     to FP8): the fp8 variant stores OCP e4m3fn codes with an fp32 scale per
- *     (block, kv head).
+ *     to FP8 or INT8, with dequantisation inside the attention kernel): the
+ *     fp8 variant stores OCP e4m3fn codes and the int8 variant symmetric
+ *     int8 codes, each with an fp32 scale per (block, kv head).
  *
  * Conventions for every call:
  *   - Tensors are caller-owned, contiguous, row-major device memory.  The
@@ -36,10 +37,10 @@
  *
  * Layouts:
  *   q, out            [B, Hq, D]           bf16
- *   k_cache, v_cache  [NB, BS, Hkv, D]     bf16 or e4m3fn (one token's heads
+ *   k_cache, v_cache  [NB, BS, Hkv, D]     bf16, e4m3fn or int8 (one token's heads
  *                                          form one contiguous row, blocks
  *                                          are token-major, as in the pages)
- *   k_scale, v_scale  [NB, Hkv]            fp32 (fp8 only, else NULL)
+ *   k_scale, v_scale  [NB, Hkv]            fp32 (fp8 and int8, else NULL)
  *   block_tables      [B, MBS]             int32; entries past the history
  *                                          are never read
  *   context_lens      [B]                  int32
@@ -69,6 +70,7 @@ extern "C" {
 /* KV cache element types */
 #define PKV_KV_BF16 0
 #define PKV_KV_FP8_E4M3FN 1
+#define PKV_KV_INT8 2
 
 /* Store the step's new token of each of N sequences into the paged cache
  * ("tiny-vllm part 5", scattering into blocks; the first page's note that
@@ -84,9 +86,14 @@ extern "C" {
  *         element is stored as e4m3fn(x / scale), x / scale a correctly
  *         rounded fp32 division, rounded to nearest even and saturated to
  *         +-448.  Same for V with v_scale.
+ *   int8: as fp8 with scale = amax / 127 (1.0 if the amax is 0) and each
+ *         element stored as clamp(rint(x / scale), -127, 127), rint rounding
+ *         halves to even; the value of a code is code * scale.  (The pages
+ *         fix no int8 format; this is the plain symmetric one.)
  * Slots outside [0, NB * BS) are skipped.  k_scale and v_scale must be NULL
- * for bf16 and non-NULL for fp8.  N == 0 is a no-op (pointers may then be
- * NULL). */
+ * for bf16 and non-NULL for fp8 and int8.  Two tokens of one call must not
+ * share a block when one of them opens it (append them in position order,
+ * one call each).  N == 0 is a no-op (pointers may then be NULL). */
 int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                   void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                   int N, int Hkv, int D, int BS, int NB, int kv_dtype, void* stream);
@@ -101,7 +108,7 @@ size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, i
  * sections 2-5):
  *   out[b, h, :] = sum_{t < L_b} softmax_t(scale * <q[b, h], K_t>) * V_t,
  *   L_b = context_lens[b], K_t = k_cache[block_tables[b][t / BS], t % BS,
- *   h / (Hq / Hkv), :] (times k_scale of that block and head for fp8),
+ *   h / (Hq / Hkv), :] (times k_scale of that block and head for fp8 and int8),
  *   likewise V_t.  No causal mask; nothing past L_b is read.  A sequence with
  *   L_b <= 0 gets out = 0.  B == 0 is a no-op (pointers may then be NULL).
  * Accumulation is fp32; out is rounded to bf16 (round to nearest even).

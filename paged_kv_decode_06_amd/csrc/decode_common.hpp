@@ -165,19 +165,20 @@ __device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int H
   return pc;
 }
 
-// Calls f(Sh<D, BS, G, fp8>{}) for the supported combination given at run
+// Calls f(Sh<D, BS, G, kind>{}) for the supported combination given at run
 // time; false if it is not supported.
-template <template <int, int, int, bool> class Sh, class F>
-bool dispatch_shapes(int D, int BS, int G, bool fp8, F&& f) {
-#define PKV_CASE(d, bs, gg, f8)                     \
-  if (D == d && BS == bs && G == gg && fp8 == f8) { \
-    f(Sh<d, bs, gg, f8>{});                         \
-    return true;                                    \
+template <template <int, int, int, int> class Sh, class F>
+bool dispatch_shapes(int D, int BS, int G, int kind, F&& f) {
+#define PKV_CASE(d, bs, gg, k)                     \
+  if (D == d && BS == bs && G == gg && kind == k) { \
+    f(Sh<d, bs, gg, k>{});                         \
+    return true;                                   \
   }
-#define PKV_G(d, bs, f8) \
-  PKV_CASE(d, bs, 1, f8) PKV_CASE(d, bs, 2, f8) PKV_CASE(d, bs, 4, f8) PKV_CASE(d, bs, 8, f8)
-#define PKV_BS(d, f8) PKV_G(d, 16, f8) PKV_G(d, 32, f8)
-  PKV_BS(64, false) PKV_BS(128, false) PKV_BS(64, true) PKV_BS(128, true)
+#define PKV_G(d, bs, k) \
+  PKV_CASE(d, bs, 1, k) PKV_CASE(d, bs, 2, k) PKV_CASE(d, bs, 4, k) PKV_CASE(d, bs, 8, k)
+#define PKV_BS(d, k) PKV_G(d, 16, k) PKV_G(d, 32, k)
+  PKV_BS(64, kKvBf16) PKV_BS(128, kKvBf16) PKV_BS(64, kKvFp8) PKV_BS(128, kKvFp8)
+  PKV_BS(64, kKvInt8) PKV_BS(128, kKvInt8)
 #undef PKV_BS
 #undef PKV_G
 #undef PKV_CASE

@@ -21,7 +21,7 @@
 // one LDS buffer per wave as bf16 rows with a padded pitch: K first (read
 // back as the A operands, 16 bytes a lane), then V over it (read back with
 // the gfx950 transposing LDS read, which hands each lane four tokens of one
-// head dim, the B operand of the PV product).  fp8 codes are widened to
+// head dim, the B operand of the PV product).  fp8 and int8 codes are widened to
 // bf16 exactly on the way into LDS; the per-(block, kv head) K scale then
 // multiplies the scores and the V scale is folded into P.
 //
@@ -49,13 +49,14 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-template <int D_, int BS_, int G_, bool FP8_>
+template <int D_, int BS_, int G_, int KIND_>
 struct MfmaShape {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr int G = G_;
-  static constexpr bool FP8 = FP8_;
-  static constexpr int EB = FP8 ? 1 : 2;      // bytes per cache element
+  static constexpr bool Q8 = KIND_ != kKvBf16;    // one-byte codes with per-block scales
+  static constexpr bool INT8 = KIND_ == kKvInt8;  // (else fp8 e4m3fn when Q8)
+  static constexpr int EB = Q8 ? 1 : 2;         // bytes per cache element
   static constexpr int RB = D * EB;           // bytes of one token's head row in the cache
   static constexpr int LPR = RB / 16;         // lanes per row (16 bytes each)
   static constexpr int RPI = kWave / LPR;     // rows per wave-wide load
@@ -89,6 +90,26 @@ __device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16
   }
 }
 
+// 16 int8 codes -> 16 bf16 (exact: |code| <= 128 has at most 8 significant bits).
+__device__ __forceinline__ void i8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16x8_t& hi) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bf16x8_t& dst = k < 2 ? lo : hi;
+    const int o = (k & 1) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[o + e] = (__bf16)(float)(int8_t)(w[k] >> (8 * e));
+  }
+}
+
+template <class S>
+__device__ __forceinline__ void q8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16x8_t& hi) {
+  if constexpr (S::INT8)
+    i8x16_to_bf16(c, lo, hi);
+  else
+    fp8x16_to_bf16(c, lo, hi);
+}
+
 // Streaming 16-byte load: every KV byte is read once, so it is marked
 // non-temporal (probe measurements on this layout: ~10% more bandwidth).
 __device__ __forceinline__ uint4 load_nt(const unsigned char* p) {
@@ -118,9 +139,9 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
     uint4 v = ch[s];
     if (zero_dead && (row >= live || (row >= gap_lo && row < gap_hi))) v = make_uint4(0, 0, 0, 0);
     unsigned char* dst = tile + row * S::PITCH;
-    if constexpr (S::FP8) {
+    if constexpr (S::Q8) {
       bf16x8_t lo, hi;
-      fp8x16_to_bf16(v, lo, hi);
+      q8x16_to_bf16<S>(v, lo, hi);
       *reinterpret_cast<bf16x8_t*>(dst + 32 * c) = lo;
       *reinterpret_cast<bf16x8_t*>(dst + 32 * c + 16) = hi;
     } else {
@@ -138,12 +159,23 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
 // left; no other wave reads the row.  All the work is done early: the new
 // rows are loaded beside q at the start of the run, and when the first tile
 // of the chunk holding the last page has its loads in flight, the rows are
-// encoded (fp8), stored to the cache and parked in the wave's LDS slot in
+// encoded (fp8 / int8), stored to the cache and parked in the wave's LDS slot in
 // tile format, hidden behind that tile's load latency; the tile holding
 // position L - 1 then only copies two rows within LDS.
-// fp8: a token at offset 0 opens its block and sets the block's scale to
-// amax / 448 first; otherwise the block keeps its scale (the same arithmetic
-// as the stand-alone append).
+// fp8 / int8: a token at offset 0 opens its block and sets the block's scale
+// to amax / 448 (fp8) or amax / 127 (int8) first; otherwise the block keeps
+// its scale (the same arithmetic as the stand-alone append).
+
+// 8 int8 codes -> 8 bf16 (exact).
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16(const uint2 c) {
+  bf16x8_t r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)(float)(int8_t)(c.x >> (8 * e));
+    r[4 + e] = (__bf16)(float)(int8_t)(c.y >> (8 * e));
+  }
+  return r;
+}
 
 // 8 e4m3fn codes -> 8 bf16 (exact).
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const uint2 c) {
@@ -165,7 +197,7 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const uint2 c) {
 // ([K | V], 2 D bytes each, tile format) and store them in the cache rows
 // `kdst` / `vdst`.  Lane l < D / 4 holds `part`, the bf16 elements
 // 8 l' .. 8 l' + 7 of the K row (l < D / 8, l' = l) or of the V row
-// (l' = l - D / 8).  fp8: `sk` / `sv` come in as the block's scales and
+// (l' = l - D / 8).  fp8 / int8: `sk` / `sv` come in as the block's scales and
 // leave as the scales after the append (set from the rows when `opens`;
 // lane 0 then stores them at `skw` / `svw`).
 template <class S>
@@ -177,17 +209,23 @@ __device__ __forceinline__ void park_new_rows(const uint4 part, int lane, unsign
   const bool is_k = lane < D / 8;
   const bool mine = lane < D / 4;
   const int c = is_k ? lane : lane - D / 8;
-  if constexpr (S::FP8) {
+  if constexpr (S::Q8) {
     float x[8];
     unpack8(part, x);   // lanes past the rows hold zeros
+    auto block_scale = [](float amax) {
+      return S::INT8 ? int8_block_scale(amax) : fp8_block_scale(amax);
+    };
+    auto enc = [](float v, float sc) {
+      return S::INT8 ? int8_encode_scaled(v, sc) : fp8_encode_scaled(v, sc);
+    };
     if (opens) {
       float am = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) am = fmaxf(am, __builtin_fabsf(x[e]));
       const float amk = wave_max(is_k ? am : 0.0f);
       const float amv = wave_max(is_k ? 0.0f : am);
-      sk = fp8_block_scale(amk);
-      sv = fp8_block_scale(amv);
+      sk = block_scale(amk);
+      sv = block_scale(amv);
       if (lane == 0) {
         *skw = sk;
         *svw = sv;
@@ -195,13 +233,12 @@ __device__ __forceinline__ void park_new_rows(const uint4 part, int lane, unsign
     }
     const float sc = is_k ? sk : sv;
     uint2 codes;
-    codes.x = fp8_encode_scaled(x[0], sc) | (fp8_encode_scaled(x[1], sc) << 8) |
-              (fp8_encode_scaled(x[2], sc) << 16) | (fp8_encode_scaled(x[3], sc) << 24);
-    codes.y = fp8_encode_scaled(x[4], sc) | (fp8_encode_scaled(x[5], sc) << 8) |
-              (fp8_encode_scaled(x[6], sc) << 16) | (fp8_encode_scaled(x[7], sc) << 24);
+    codes.x = enc(x[0], sc) | (enc(x[1], sc) << 8) | (enc(x[2], sc) << 16) | (enc(x[3], sc) << 24);
+    codes.y = enc(x[4], sc) | (enc(x[5], sc) << 8) | (enc(x[6], sc) << 16) | (enc(x[7], sc) << 24);
     if (mine) {
       *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes;
-      *reinterpret_cast<bf16x8_t*>(rows + 16 * lane) = fp8x8_to_bf16(codes);
+      *reinterpret_cast<bf16x8_t*>(rows + 16 * lane) =
+          S::INT8 ? i8x8_to_bf16(codes) : fp8x8_to_bf16(codes);
     }
   } else {
     if (mine) {
@@ -308,7 +345,7 @@ void mfma_partition_kernel(const AttnParams p) {
                      ? *reinterpret_cast<const uint4*>(p.k_new + src + 8 * lane)
                      : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (lane - D / 8));
     }
-    float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8: the last block's scales after the append
+    float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: the last block's scales after the append
 
     float4_t O[NBN];
 #pragma unroll
@@ -334,7 +371,7 @@ void mfma_partition_kernel(const AttnParams p) {
       // in flight per wave: a 4 KB half tile (bf16, D = 128) is enough on
       // its own, so its V loads are issued only once the K loads have
       // landed (issuing both at once measured ~7% slower); 2 KB halves
-      // (fp8, or D = 64) issue K and V together (~3% faster than in turn).
+      // (fp8 / int8, or D = 64) issue K and V together (~3% faster than in turn).
       // The other waves of the CU overlap their compute with the waits;
       // issuing the next tile early does not pay for the registers it costs.
       auto tile_base = [&](int u) {
@@ -361,7 +398,7 @@ void mfma_partition_kernel(const AttnParams p) {
           const int off = (L - 1) % BS;
           const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g * RB;
           const int64_t sslot = (int64_t)blk * Hkv + g;
-          if constexpr (S::FP8) {
+          if constexpr (S::Q8) {
             if (off != 0) {
               new_ksc = p.k_scale[sslot];
               new_vsc = p.v_scale[sslot];
@@ -370,7 +407,7 @@ void mfma_partition_kernel(const AttnParams p) {
           park_new_rows<S>(new_part, lane, new_rows, p.k_cache_w + row, p.v_cache_w + row,
                            off == 0, new_ksc, new_vsc, p.k_scale_w + sslot, p.v_scale_w + sslot);
         }
-        if constexpr (S::FP8) {
+        if constexpr (S::Q8) {
           const int phys = __builtin_amdgcn_readlane(phys_l, k);
           ksc = p.k_scale[(int64_t)phys * Hkv + g];
           vsc = p.v_scale[(int64_t)phys * Hkv + g];
@@ -380,7 +417,7 @@ void mfma_partition_kernel(const AttnParams p) {
         stage_tile<S>(tile, kb, lane, live, false);
         if (new_tile) {
           take_new_row<S>(new_rows, tile, live - 1, lane);
-          if constexpr (S::FP8) {
+          if constexpr (S::Q8) {
             ksc = new_ksc;
             vsc = new_vsc;
           }
@@ -395,7 +432,7 @@ void mfma_partition_kernel(const AttnParams p) {
           const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tile + k_rd + 64 * kk);
           s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], s, 0, 0, 0);
         }
-        const float c = S::FP8 ? p.scale_log2 * ksc : p.scale_log2;
+        const float c = S::Q8 ? p.scale_log2 * ksc : p.scale_log2;
         // rows past a_rel are in column n's future (decode: past the history)
         const int a_rel = GEN ? lim_n - tok0 : live - 1;
 #pragma unroll
@@ -432,7 +469,7 @@ void mfma_partition_kernel(const AttnParams p) {
         for (int i = 0; i < 4; ++i) {
           const float pr = fast_exp2(s[i] - m_run);
           l_run += pr;
-          pa[i] = bf16_bits(S::FP8 ? pr * vsc : pr);
+          pa[i] = bf16_bits(S::Q8 ? pr * vsc : pr);
         }
 
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
@@ -506,10 +543,10 @@ static size_t mfma_lds_total(int B, int D) {
 
 // Occupancy of the decode instantiation; the generalised one is held to the
 // same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves both.
-int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B) {
   int blocks = 0, blocks_gen = 0;
   const size_t lds = mfma_lds_total(B, D);
-  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, fp8, [&](auto s) {
+  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, kind, [&](auto s) {
     using S = decltype(s);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S, false>,
                                                      kAttnBlockThreads, lds) != hipSuccess ||
@@ -520,11 +557,11 @@ int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
   return ok ? (blocks < blocks_gen ? blocks : blocks_gen) : 0;
 }
 
-hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
   const size_t lds = mfma_lds_total(p.B, D);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
-  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, fp8, [&](auto s) {
+  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, kind, [&](auto s) {
     using S = decltype(s);
     if (gen)
       hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks), dim3(kAttnBlockThreads),

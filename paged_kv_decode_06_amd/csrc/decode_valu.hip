@@ -2,7 +2,7 @@
 //
 // Inside a wave, lanes are laid out as TPW token rows of LPT lanes; a lane
 // holds 8 consecutive head-dim elements of one token (one 16-byte load for
-// bf16, 8 bytes for fp8).  q for the G heads of the group sits in registers
+// bf16, 8 bytes for fp8 / int8).  q for the G heads of the group sits in registers
 // as fp32, so each K/V byte is loaded once for the whole GQA group.  Per
 // page: partial dot products, a DPP reduction over the LPT lanes of a row,
 // online softmax per row in the exp2 domain, PV accumulation with fp32 FMAs.
@@ -18,18 +18,19 @@
 namespace pkv {
 namespace {
 
-template <int D_, int BS_, int G_, bool FP8_>
+template <int D_, int BS_, int G_, int KIND_>
 struct ValuShape {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr int G = G_;
-  static constexpr bool FP8 = FP8_;
+  static constexpr bool Q8 = KIND_ != kKvBf16;    // one-byte codes with per-block scales
+  static constexpr bool INT8 = KIND_ == kKvInt8;
   static constexpr int VEC = 8;            // head-dim elements per lane per load
   static constexpr int LPT = D / VEC;      // lanes per token row
   static constexpr int TPW = kWave / LPT;  // token rows per wave-wide load
   static constexpr int LPP = BS / TPW;     // wave-wide loads per page
-  static constexpr int EB = FP8 ? 1 : 2;   // bytes per cache element
-  using Vec = typename std::conditional<FP8, uint2, uint4>::type;
+  static constexpr int EB = Q8 ? 1 : 2;    // bytes per cache element
+  using Vec = typename std::conditional<Q8, uint2, uint4>::type;
   static_assert(LPP >= 1 && BS % TPW == 0, "page must hold whole token rows");
 };
 
@@ -40,7 +41,7 @@ __device__ __forceinline__ typename S::Vec load_row(const uint8_t* __restrict__ 
   typename S::Vec v;
   v.x = __builtin_nontemporal_load(a + 0);
   v.y = __builtin_nontemporal_load(a + 1);
-  if constexpr (!S::FP8) {
+  if constexpr (!S::Q8) {
     v.z = __builtin_nontemporal_load(a + 2);
     v.w = __builtin_nontemporal_load(a + 3);
   }
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
           kb[buf][sl] = load_row<S>(kpage + o);
           vb[buf][sl] = load_row<S>(vpage + o);
         }
-        if constexpr (S::FP8) {
+        if constexpr (S::Q8) {
           ksc[buf] = p.k_scale[(int64_t)phys * Hkv + g];
           vsc[buf] = p.v_scale[(int64_t)phys * Hkv + g];
         }
@@ -140,7 +141,10 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
 #pragma unroll
         for (int sl = 0; sl < LPP; ++sl) {
           float kf[8];
-          unpack8(kb[buf][sl], kf);
+          if constexpr (S::INT8)
+            unpack8_i8(kb[buf][sl], kf);
+          else
+            unpack8(kb[buf][sl], kf);
 #pragma unroll
           for (int jj = 0; jj < G; ++jj) {
             float d = 0.0f;
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
             s[sl][jj] = group_sum<LPT>(d);
           }
         }
-        if constexpr (S::FP8) {
+        if constexpr (S::Q8) {
 #pragma unroll
           for (int sl = 0; sl < LPP; ++sl)
 #pragma unroll
@@ -176,7 +180,10 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
 #pragma unroll
         for (int sl = 0; sl < LPP; ++sl) {
           float vf[8];
-          unpack8(vb[buf][sl], vf);
+          if constexpr (S::INT8)
+            unpack8_i8(vb[buf][sl], vf);
+          else
+            unpack8(vb[buf][sl], vf);
           if (tail && tok0 + sl * TPW + r >= L) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vf[e] = 0.0f;
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
           for (int jj = 0; jj < G; ++jj) {
             const float pr = fast_exp2(s[sl][jj] - m[jj]);
             l[jj] += pr;
-            const float pv = S::FP8 ? pr * vsc[buf] : pr;
+            const float pv = S::Q8 ? pr * vsc[buf] : pr;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[jj][e] = fmaf(pv, vf[e], acc[jj][e]);
           }
@@ -258,10 +265,10 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
 
 }  // namespace
 
-int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
+int valu_blocks_per_cu(int D, int BS, int G, int kind, int B) {
   int blocks = 0;
   const size_t lds_bytes = prefix_lds_bytes(B);
-  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, fp8, [&](auto s) {
+  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, kind, [&](auto s) {
     using S = decltype(s);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, valu_partition_kernel<S>,
                                                      kAttnBlockThreads, lds_bytes) != hipSuccess)
@@ -270,10 +277,10 @@ int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B) {
   return ok ? blocks : 0;
 }
 
-hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
   const size_t lds = prefix_lds_bytes(p.B);
-  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, fp8, [&](auto s) {
+  const bool ok = dispatch_shapes<ValuShape>(D, BS, G, kind, [&](auto s) {
     using S = decltype(s);
     hipLaunchKernelGGL(valu_partition_kernel<S>, dim3(blocks), dim3(kAttnBlockThreads), lds, stream, p);
   });

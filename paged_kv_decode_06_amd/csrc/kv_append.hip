@@ -5,8 +5,9 @@
 // (section on scattering into blocks); the caller resolves the slot (or, for
 // the decode step with the VALU partition kernel, the slot is position
 // context_lens[i] - 1 through the block table) and one launch writes every
-// sequence's K and V rows.  fp8: the token that opens a block (offset 0)
-// sets that block's per-head scale to amax/448.
+// sequence's K and V rows.  fp8 / int8: the token that opens a block
+// (offset 0) sets that block's per-head scale to amax/448 (fp8) or amax/127
+// (int8).
 
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
@@ -50,10 +51,10 @@ __global__ __launch_bounds__(256) void kv_append_bf16_kernel(
   }
 }
 
-// fp8: one wave per (token, kv head, K or V).  Lane l holds elements
+// fp8 / int8: one wave per (token, kv head, K or V).  Lane l holds elements
 // l, l + 64, ... of the head's D values.
-template <int D>
-__global__ __launch_bounds__(64) void kv_append_fp8_kernel(
+template <int D, bool INT8>
+__global__ __launch_bounds__(64) void kv_append_q8_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ slots, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int MBS, uint8_t* __restrict__ k_cache,
@@ -81,14 +82,15 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(
 #pragma unroll
     for (int k = 0; k < PER; ++k) amax = fmaxf(amax, __builtin_fabsf(x[k]));
     amax = wave_max(amax);
-    sc = fp8_block_scale(amax);
+    sc = INT8 ? int8_block_scale(amax) : fp8_block_scale(amax);
     if (lane == 0) *scale_slot = sc;
   } else {
     sc = *scale_slot;
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k)
-    dst[lane + k * kWave] = (uint8_t)fp8_encode_scaled(x[k], sc);
+    dst[lane + k * kWave] =
+        (uint8_t)(INT8 ? int8_encode_scaled(x[k], sc) : fp8_encode_scaled(x[k], sc));
 }
 
 }  // namespace
@@ -96,28 +98,28 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slots,
                             const int32_t* block_tables, const int32_t* context_lens, int MBS,
                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                            int N, int Hkv, int D, int BS, int NB, bool fp8, hipStream_t stream) {
+                            int N, int Hkv, int D, int BS, int NB, int kind, hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  if (!fp8) {
+  if (kind == kKvBf16) {
     const int row_vecs = Hkv * D / 8;
     hipLaunchKernelGGL(kv_append_bf16_kernel, dim3(N), dim3(256), 0, stream,
                        (const uint4*)k_new, (const uint4*)v_new, slots, block_tables,
                        context_lens, MBS, (uint4*)k_cache, (uint4*)v_cache, row_vecs, BS, NB);
-  } else {
-    const dim3 grid((unsigned)N * Hkv * 2);
-    if (D == 128)
-      hipLaunchKernelGGL(kv_append_fp8_kernel<128>, grid, dim3(64), 0, stream,
-                         (const uint16_t*)k_new, (const uint16_t*)v_new, slots, block_tables,
-                         context_lens, MBS, (uint8_t*)k_cache, (uint8_t*)v_cache, k_scale,
-                         v_scale, Hkv, BS, NB);
-    else if (D == 64)
-      hipLaunchKernelGGL(kv_append_fp8_kernel<64>, grid, dim3(64), 0, stream,
-                         (const uint16_t*)k_new, (const uint16_t*)v_new, slots, block_tables,
-                         context_lens, MBS, (uint8_t*)k_cache, (uint8_t*)v_cache, k_scale,
-                         v_scale, Hkv, BS, NB);
-    else
-      return hipErrorInvalidValue;
+    return hipGetLastError();
   }
+  const dim3 grid((unsigned)N * Hkv * 2);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, stream, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, slots, block_tables, context_lens, MBS,
+                       (uint8_t*)k_cache, (uint8_t*)v_cache, k_scale, v_scale, Hkv, BS, NB);
+  };
+  const bool i8 = kind == kKvInt8;
+  if (D == 128)
+    i8 ? launch(kv_append_q8_kernel<128, true>) : launch(kv_append_q8_kernel<128, false>);
+  else if (D == 64)
+    i8 ? launch(kv_append_q8_kernel<64, true>) : launch(kv_append_q8_kernel<64, false>);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -61,11 +61,11 @@ int cu_count(int dev) {
 
 // LDS of the partition kernel grows with B; occupancy is looked up for B
 // rounded up to a multiple of 1024 so that the cache stays small.
-int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, bool fp8, int B) {
+int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B) {
   const int Bq = ((B + 1023) / 1024) * 1024;
   const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
-                                 ((unsigned long long)G << 16) | ((unsigned long long)fp8 << 15) |
+                                 ((unsigned long long)G << 16) | ((unsigned long long)kind << 12) |
                                  (unsigned long long)(Bq / 1024);
   auto& c = cache();
   {
@@ -73,8 +73,8 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, bool fp8, i
     auto it = c.blocks.find(key);
     if (it != c.blocks.end()) return it->second;
   }
-  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, fp8, Bq)
-                                             : pkv::valu_blocks_per_cu(D, BS, G, fp8, Bq);
+  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq)
+                                             : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
   return n;
@@ -83,7 +83,7 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, bool fp8, i
 bool supported(int D, int BS, int G, int kv_dtype) {
   return (D == 64 || D == 128) && (BS == 16 || BS == 32) &&
          (G == 1 || G == 2 || G == 4 || G == 8) &&
-         (kv_dtype == PKV_KV_BF16 || kv_dtype == PKV_KV_FP8_E4M3FN);
+         (kv_dtype == PKV_KV_BF16 || kv_dtype == PKV_KV_FP8_E4M3FN || kv_dtype == PKV_KV_INT8);
 }
 
 // Persistent grid: every workgroup that fits at once on every CU.
@@ -91,7 +91,7 @@ int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
-  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype == PKV_KV_FP8_E4M3FN, B);
+  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B);
   return ncu * per_cu;
 }
 
@@ -99,7 +99,7 @@ struct AttnCall {
   pkv::AttnParams p;
   pkv::AttnPath path;
   int D, BS, G, blocks;
-  bool fp8;
+  int kind;   // pkv::KvKind (= kv_dtype)
 };
 
 // Options beyond one query per sequence; the defaults are the decode call.
@@ -154,14 +154,14 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (step && (!k_new || !v_new)) return fail(PKV_ERR_NULL, "k_new and v_new are required");
   if ((((uintptr_t)opts.q_start) & 3u) != 0)
     return fail(PKV_ERR_ALIGN, "q_start must be 4-byte aligned");
-  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
-  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
+  const bool q8 = kv_dtype != PKV_KV_BF16;
+  if (q8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 / int8 cache needs k_scale and v_scale");
+  if (!q8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_ALIGN, "q, caches and out must be 16-byte aligned");
   if (step && (!aligned16(k_new) || !aligned16(v_new)))
     return fail(PKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
-  if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
+  if (q8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
   const pkv::AttnPath path = path_for(opts);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B);
@@ -209,15 +209,15 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   call->D = D;
   call->BS = BS;
   call->G = G;
-  call->fp8 = fp8;
+  call->kind = kv_dtype;
   call->blocks = blocks;
   return PKV_OK;
 }
 
 hipError_t launch_partition(const AttnCall& c, hipStream_t s) {
   return c.path == pkv::AttnPath::kMfma
-             ? pkv::launch_partition_mfma(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s)
-             : pkv::launch_partition_valu(c.p, c.D, c.BS, c.G, c.fp8, c.blocks, s);
+             ? pkv::launch_partition_mfma(c.p, c.D, c.BS, c.G, c.kind, c.blocks, s)
+             : pkv::launch_partition_valu(c.p, c.D, c.BS, c.G, c.kind, c.blocks, s);
 }
 
 }  // namespace
@@ -402,7 +402,7 @@ int decode_step_impl(const void* q, const void* k_new, const void* v_new, void* 
     if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   } else {
     e = pkv::launch_kv_append(k_new, v_new, nullptr, block_tables, context_lens, MBS, k_cache,
-                              v_cache, k_scale, v_scale, B, Hkv, D, BS, NB, call.fp8, s);
+                              v_cache, k_scale, v_scale, B, Hkv, D, BS, NB, call.kind, s);
     if (e != hipSuccess) return hip_fail(e, "kv_append kernel launch");
     e = launch_partition(call, s);
     if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
@@ -445,19 +445,19 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
     return fail(PKV_ERR_SHAPE, "sizes must be positive (N may be 0): N=%d Hkv=%d D=%d BS=%d NB=%d",
                 N, Hkv, D, BS, NB);
   if ((D != 64 && D != 128) || (BS != 16 && BS != 32) ||
-      (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3FN))
+      (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3FN && kv_dtype != PKV_KV_INT8))
     return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d kv_dtype=%d", D, BS, kv_dtype);
   if (N == 0) return PKV_OK;   // nothing to do; pointers may be NULL
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
-  const bool fp8 = kv_dtype == PKV_KV_FP8_E4M3FN;
-  if (fp8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 cache needs k_scale and v_scale");
-  if (!fp8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
-  if (!fp8 && (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)))
+  const bool q8 = kv_dtype != PKV_KV_BF16;
+  if (q8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 / int8 cache needs k_scale and v_scale");
+  if (!q8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
+  if (!q8 && (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)))
     return fail(PKV_ERR_ALIGN, "k_new, v_new and the caches must be 16-byte aligned");
   if (N == 0) return PKV_OK;
   hipError_t e = pkv::launch_kv_append(k_new, v_new, slot_mapping, nullptr, nullptr, 0, k_cache,
-                                       v_cache, k_scale, v_scale, N, Hkv, D, BS, NB, fp8,
+                                       v_cache, k_scale, v_scale, N, Hkv, D, BS, NB, kv_dtype,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : hip_fail(e, "kv_append kernel launch");
 }

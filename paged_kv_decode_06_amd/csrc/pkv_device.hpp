@@ -80,6 +80,31 @@ __device__ __forceinline__ uint32_t fp8_encode_scaled(float x, float scale) {
   return f32_to_e4m3fn_rne_sat(__fdiv_rn(x, scale));
 }
 
+// ---- INT8 --------------------------------------------------------------------
+
+// Eight int8 codes -> eight floats (exact).
+__device__ __forceinline__ void unpack8_i8(const uint2 v, float (&f)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f[k] = (float)(int8_t)(v.x >> (8 * k));
+    f[4 + k] = (float)(int8_t)(v.y >> (8 * k));
+  }
+}
+
+// Scale of a block that a new token opens: amax / 127 in fp32 (correctly
+// rounded division), or 1 when the token is all zeros; elements are stored
+// as clamp(rint(x / scale), -127, 127), rint rounding halves to even.
+// Both append paths use exactly this.
+__device__ __forceinline__ float int8_block_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
+}
+__device__ __forceinline__ uint32_t int8_encode_scaled(float x, float scale) {
+  const float y = __fdiv_rn(x, scale);
+  if (y != y) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xffu;
+}
+
 // ---- cross-lane reductions (DPP within a 16-lane row) -----------------------
 
 template <int CTRL>

@@ -9,6 +9,10 @@
 
 namespace pkv {
 
+// Cache element kinds (the PKV_KV_* values of the C ABI).  fp8 and int8
+// caches hold one-byte codes with an fp32 scale per (block, kv head).
+enum KvKind : int { kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2 };
+
 // Arguments of the attention kernels.  Pointers are device pointers.
 struct AttnParams {
   const void* q;
@@ -81,16 +85,16 @@ inline size_t prefix_lds_bytes(int B) {
 }
 
 // The two partition-kernel variants.  Launchers return hipErrorInvalidValue
-// for an unsupported (D, BS, G, fp8) combination; *_blocks_per_cu give the
+// for an unsupported (D, BS, G, kind) combination; *_blocks_per_cu give the
 // workgroups that fit on one compute unit (0 if unsupported).
 enum class AttnPath { kValu = 0, kMfma = 1 };
-hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream);
-int valu_blocks_per_cu(int D, int BS, int G, bool fp8, int B);
+int valu_blocks_per_cu(int D, int BS, int G, int kind, int B);
 // (the VALU variant handles one query per sequence and no window only)
-hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, bool fp8, int blocks,
+hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream);
-int mfma_blocks_per_cu(int D, int BS, int G, bool fp8, int B);
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
 size_t mfma_stage_lds_bytes(int D);
 
@@ -107,6 +111,6 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int32_t* slots,
                             const int32_t* block_tables, const int32_t* context_lens, int MBS,
                             void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                            int N, int Hkv, int D, int BS, int NB, bool fp8, hipStream_t stream);
+                            int N, int Hkv, int D, int BS, int NB, int kind, hipStream_t stream);
 
 }  // namespace pkv

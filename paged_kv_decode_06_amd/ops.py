@@ -17,6 +17,7 @@ import torch
 
 KV_BF16 = 0
 KV_FP8 = 1
+KV_INT8 = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpkv.so"
@@ -123,7 +124,9 @@ def _kv_dtype(k_cache: torch.Tensor) -> int:
         return KV_BF16
     if k_cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         return KV_FP8
-    raise TypeError(f"cache dtype must be bfloat16 or uint8/float8_e4m3fn, got {k_cache.dtype}")
+    if k_cache.dtype == torch.int8:
+        return KV_INT8
+    raise TypeError(f"cache dtype must be bfloat16, uint8/float8_e4m3fn or int8, got {k_cache.dtype}")
 
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
@@ -135,7 +138,7 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scal
     _need(slot_mapping, "slot_mapping", torch.int32, 1)
     _need(k_cache, "k_cache", k_cache.dtype, 4)
     _need(v_cache, "v_cache", k_cache.dtype, 4)
-    if kvd == KV_FP8:
+    if kvd != KV_BF16:
         _need(k_scale, "k_scale", torch.float32, 2)
         _need(v_scale, "v_scale", torch.float32, 2)
     N, Hkv, D = k_new.shape
@@ -177,7 +180,7 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sc
     _need(v_cache, "v_cache", k_cache.dtype, 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    if kvd == KV_FP8:
+    if kvd != KV_BF16:
         _need(k_scale, "k_scale", torch.float32, 2)
         _need(v_scale, "v_scale", torch.float32, 2)
     B, Hq, D = q.shape

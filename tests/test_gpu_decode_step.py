@@ -88,14 +88,15 @@ def test_step_equals_two_calls_every_variant(kernel):
     """Every (D, BS, G, dtype) instantiation; lengths 1 and BS + 1 put the new
     token at offset 0 (it opens a block and, for fp8, sets the scale), the
     others put it mid-block and on the last offset of a block."""
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8), ("bf16", "fp8")):
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+                                          ("bf16", "fp8", "int8")):
         Hkv = 2
         wl = build(5, Hkv * G, Hkv, D, BS, (1, BS + 1, 2 * BS, 9 * BS + 5, 3 * BS - 1), kv=kv,
                    seed=D + BS + G + 7)
         assert_same_as_two_calls(wl, f"D{D} BS{BS} G{G} {kv}")
 
 
-@pytest.mark.parametrize("name", ["llama3_8b", "long_context", "mixed_70b", "fp8"])
+@pytest.mark.parametrize("name", ["llama3_8b", "long_context", "mixed_70b", "fp8", "int8"])
 def test_step_equals_two_calls_full_configuration(name, kernel):
     say(f"config {name}")
     wl = W.make_config_workload(name, device=DEV, poison=True)

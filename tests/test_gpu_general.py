@@ -53,6 +53,8 @@ CASES = [
     (3, 16, 4, 128, 32, (40, 700, 2000), (2, 4, 3), "fp8", 0, 0),
     (3, 16, 4, 128, 32, (40, 700, 2000), (2, 4, 3), "fp8", 3, 100),
     (2, 8, 2, 64, 16, (50, 400), (4, 2), "fp8", 1, 33),
+    (3, 16, 4, 128, 32, (40, 700, 2000), (2, 4, 3), "int8", 0, 0),
+    (2, 32, 8, 128, 16, (600, 3000), (4, 1), "int8", 8, 300),
 ]
 
 
@@ -66,7 +68,8 @@ def test_general_attention_matches_oracle(case):
 def test_every_variant_with_queries_and_a_window():
     """Every (D, BS, G, dtype) instantiation with the most queries it takes."""
     import itertools
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8), ("bf16", "fp8")):
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+                                          ("bf16", "fp8", "int8")):
         Hkv = 2
         q = 16 // G
         wl = build(3, Hkv * G, Hkv, D, BS, (q, BS + q + 3, 9 * BS + 5), (q, q, max(1, q // 2)),

@@ -3,8 +3,8 @@ the same seeded inputs.
 
 Bars: kv_append bit-exact over the whole cache (untouched bytes included);
 attention within |gpu - ref| <= 4e-3 + 8e-3 |ref| elementwise for a bf16
-cache and <= 3e-2 absolute for an fp8 cache (against the oracle's
-dequantised-fp8 result).
+or int8 cache and <= 3e-2 absolute for an fp8 cache (against the oracle on
+the dequantised codes).
 """
 from __future__ import annotations
 
@@ -87,6 +87,9 @@ SMALL = [
     (3, 32, 8, 128, 32, (2, 96, 3000), "fp8"),
     (2, 4, 4, 128, 16, (40, 700), "fp8"),
     (2, 8, 4, 64, 32, (64, 129), "fp8"),
+    (3, 16, 2, 128, 32, (1, 32, 1025), "int8"),
+    (2, 8, 2, 64, 16, (16, 977), "int8"),
+    (3, 32, 8, 128, 16, (2, 96, 3000), "int8"),
 ]
 
 
@@ -99,7 +102,8 @@ def test_step_matches_oracle_small(shape, kernel):
 
 def test_all_supported_variants_run(kernel):
     """Every (D, BS, G, dtype) instantiation against the oracle."""
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8), ("bf16", "fp8")):
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+                                          ("bf16", "fp8", "int8")):
         Hkv = 2
         wl = build(3, Hkv * G, Hkv, D, BS, (1, BS + 3, 9 * BS + 5), kv=kv, seed=D + BS + G)
         check_step(wl, f"D{D} BS{BS} G{G} {kv}")
@@ -196,7 +200,7 @@ def pick_sequences(wl: W.Workload, n=6):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b", "long_context", "mixed_70b", "fp8"])
+@pytest.mark.parametrize("name", ["llama3_8b", "long_context", "mixed_70b", "fp8", "int8"])
 def test_full_configuration_sampled(name, kernel):
     """The full-size configurations, in the launch configuration the benchmark
     times, checked on sampled sequences (first, last, longest, shortest and
