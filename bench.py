@@ -378,6 +378,23 @@ def main():
     part_med_us = float(np.median([x[1].elapsed_time(x[2]) for x in e])) * 1e3
     merge_us = float(np.median([x[2].elapsed_time(x[3]) for x in e])) * 1e3
 
+    # the RoPE-fused append at the same batch (rotating q into a scratch
+    # tensor and appending the rotated keys into the first cache copy), 50
+    # launches between events
+    q_rot = torch.empty_like(wl.q)
+    pos = (wl.context_lens - 1).to(torch.int32)
+    kc, vc, ks, vs = caches[0]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for i in range(60):
+            if i == 10:
+                r0.record(stream)
+            ops.rope_kv_append(wl.q, wl.k_new, wl.v_new, pos, wl.slot_mapping, kc, vc, ks, vs,
+                               q_out=q_rot, stream=stream)
+        r1.record(stream)
+    torch.cuda.synchronize()
+    rope_us = r0.elapsed_time(r1) * 1e3 / 50
+
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (part_avg_ms * 1e-3) / 1e9
     waves = ops.lib().pkv_attention_waves(wl.D, wl.BS, wl.G, kvd)
@@ -422,6 +439,7 @@ def main():
             "ms_per_step_" + ("two_call" if args.step == "fused" else "fused"):
                 round(ms_per_step_other, 5),
             "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
+            "rope_kv_append_us_mean": round(rope_us, 2),
             "persistent_waves": waves,
         },
     }

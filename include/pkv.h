@@ -98,6 +98,31 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
                   void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                   int N, int Hkv, int D, int BS, int NB, int kv_dtype, void* stream);
 
+/* RoPE fused with the append ("tiny-vllm part 5", the RoPE section: each
+ * head's pairs (x[2i], x[2i+1]) rotate by pos * f_i, f_i = theta^(-2i/D),
+ * with the Llama 3 frequency scaling of the page's table path: where the
+ * wavelength 2 pi / f_i exceeds original_max_len / low_freq_factor, f_i is
+ * divided by rope_factor; between that and original_max_len /
+ * high_freq_factor it is blended, (1 - a) f_i / rope_factor + a f_i with
+ * a = (original_max_len / wavelength - low_freq_factor) / (high_freq_factor
+ * - low_freq_factor).  rope_factor = 1 is plain RoPE.  The page's Llama 3
+ * setting is theta 500000, factor 32, 1, 4, 8192.)
+ * For each token i < N at position positions[i]:
+ *   q_out[i]  = RoPE(q[i])     [N, Hq, D] bf16 (q_out may be q itself)
+ *   k_rot     = RoPE(k_new[i]) [Hkv, D]
+ *   then exactly pkv_kv_append of (k_rot, v_new[i]) into slot_mapping[i]
+ *   (bf16 copy or fp8 / int8 codes, the same scale rule; a slot outside the
+ *   pool skips the append, q is rotated all the same).
+ * The angle, cos / sin and the rotation are fp64; each rotated element is
+ * rounded once to bf16 (nearest even).  Hkv <= 8; D in {64, 128}; pointers
+ * 4-byte aligned.  N == 0 is a no-op (pointers may then be NULL). */
+int pkv_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                       const int32_t* positions, const int32_t* slot_mapping, void* k_cache,
+                       void* v_cache, float* k_scale, float* v_scale, int N, int Hq, int Hkv,
+                       int D, int BS, int NB, int kv_dtype, double rope_theta,
+                       double rope_factor, double low_freq_factor, double high_freq_factor,
+                       double original_max_len, void* stream);
+
 /* Bytes of device workspace pkv_paged_decode_attention needs for these
  * sizes on the current device (it depends on the device's compute-unit
  * count).  Returns 0 for sizes the library does not support. */

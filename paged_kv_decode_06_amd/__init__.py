@@ -13,6 +13,8 @@ Two operations sit behind a C-ABI shared library (``libpkv.so``, declared in
 * ``paged_attention``: the generalised call -- several query tokens per
   sequence with the bottom-right causal mask, and an optional sliding window
   with attention sinks;
+* ``rope_kv_append``: the rotary embedding of q and of the new keys
+  (Llama 3 frequency scaling) fused with the append;
 * ``decode_step``: both in one call (the append runs inside the attention's
   partition kernel), bit-identical to the two calls in sequence.
 
@@ -26,6 +28,7 @@ from .ops import (  # noqa: F401
     PkvError,
     decode_step,
     kv_append,
+    rope_kv_append,
     paged_attention,
     attention_workspace_bytes,
     paged_decode_attention,

@@ -437,6 +437,40 @@ int pkv_decode_step_partition(const void* q, const void* k_new, const void* v_ne
                           workspace, workspace_bytes, stream, false);
 }
 
+int pkv_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                       const int32_t* positions, const int32_t* slot_mapping, void* k_cache,
+                       void* v_cache, float* k_scale, float* v_scale, int N, int Hq, int Hkv,
+                       int D, int BS, int NB, int kv_dtype, double rope_theta,
+                       double rope_factor, double low_freq_factor, double high_freq_factor,
+                       double original_max_len, void* stream) {
+  g_last_error.clear();
+  if (N < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || BS <= 0 || NB <= 0)
+    return fail(PKV_ERR_SHAPE, "sizes must be positive (N may be 0): N=%d Hq=%d Hkv=%d D=%d BS=%d NB=%d",
+                N, Hq, Hkv, D, BS, NB);
+  if ((D != 64 && D != 128) || (BS != 16 && BS != 32) || Hkv > 8 ||
+      (kv_dtype != PKV_KV_BF16 && kv_dtype != PKV_KV_FP8_E4M3FN && kv_dtype != PKV_KV_INT8))
+    return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d BS=%d Hkv=%d kv_dtype=%d", D, BS, Hkv, kv_dtype);
+  if (!(rope_theta > 1.0) || !(rope_factor > 0.0) || !(low_freq_factor > 0.0) ||
+      !(high_freq_factor > low_freq_factor) || !(original_max_len > 0.0))
+    return fail(PKV_ERR_SHAPE, "rope parameters: theta > 1, factor > 0, 0 < low_freq_factor < "
+                "high_freq_factor and original_max_len > 0 are required");
+  if (N == 0) return PKV_OK;   // nothing to do; pointers may be NULL
+  if (!q || !q_out || !k_new || !v_new || !positions || !slot_mapping || !k_cache || !v_cache)
+    return fail(PKV_ERR_NULL, "a required tensor pointer is NULL");
+  const bool q8 = kv_dtype != PKV_KV_BF16;
+  if (q8 && (!k_scale || !v_scale)) return fail(PKV_ERR_NULL, "fp8 / int8 cache needs k_scale and v_scale");
+  if (!q8 && (k_scale || v_scale)) return fail(PKV_ERR_SHAPE, "bf16 cache takes no scales");
+  if ((((uintptr_t)q) | ((uintptr_t)q_out) | ((uintptr_t)k_new) | ((uintptr_t)v_new) |
+       ((uintptr_t)k_cache) | ((uintptr_t)v_cache)) & 3u)
+    return fail(PKV_ERR_ALIGN, "q, q_out, k_new, v_new and the caches must be 4-byte aligned");
+  const pkv::RopeParams rp{rope_theta, rope_factor, low_freq_factor, high_freq_factor,
+                           original_max_len};
+  hipError_t e = pkv::launch_rope_append(q, q_out, k_new, v_new, positions, slot_mapping,
+                                         k_cache, v_cache, k_scale, v_scale, N, Hq, Hkv, D, BS,
+                                         NB, kv_dtype, rp, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "rope_kv_append kernel launch");
+}
+
 int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                   void* k_cache, void* v_cache, float* k_scale, float* v_scale, int N, int Hkv,
                   int D, int BS, int NB, int kv_dtype, void* stream) {

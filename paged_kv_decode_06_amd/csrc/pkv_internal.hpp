@@ -105,6 +105,20 @@ std::atomic<int>& path_flag();
 
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
 
+// Rotary embedding parameters (the Llama 3 scaled frequencies; factor 1:
+// plain RoPE).
+struct RopeParams {
+  double theta, factor, low_freq_factor, high_freq_factor, original_max;
+};
+
+// RoPE of q (into q_out) and of the new keys, then the append of the rotated
+// keys and the values into `slots` (see rope_append.hip).  Hkv <= 8.
+hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                              const int32_t* positions, const int32_t* slots, void* k_cache,
+                              void* v_cache, float* k_scale, float* v_scale, int N, int Hq,
+                              int Hkv, int D, int BS, int NB, int kind, const RopeParams& rp,
+                              hipStream_t stream);
+
 // One-token append.  With `slots` NULL the slot of token i is derived from
 // the block table instead: position context_lens[i] - 1 of sequence i
 // (block_tables is [N, MBS]); a length outside [1, MBS * BS] skips the token.

@@ -1,0 +1,178 @@
+// RoPE fused with the one-token KV append.
+//
+// "tiny-vllm part 5", section "RoPE: one current position, recomputed on
+// every call": each head's pairs (x[2i], x[2i+1]) are rotated by the angle
+// pos * f_i, with f_i = theta^(-2i/D) and the Llama 3 scaling of the table
+// path (frequencies whose wavelength 2 pi / f exceeds original_max /
+// low_freq_factor are divided by `factor`; between that and original_max /
+// high_freq_factor they are blended linearly in original_max / wavelength).
+// The page notes that its decode path recomputes unscaled angles while its
+// prefill table is scaled; here one rule serves both (factor = 1 turns the
+// scaling off).
+//
+// One workgroup per token: it rotates the token's query heads into q_out and
+// its new key heads into LDS, then appends the rotated key and the value row
+// exactly as the stand-alone append does (bf16 copy, or fp8 / int8 codes
+// with a per-(block, kv head) scale).  The angle, cos / sin and the rotation
+// are computed in fp64 and the result is rounded once, straight from fp64
+// to bf16 (nearest even): each rotated element is the nearest bf16 to the
+// fp64 rotation.
+
+#include "pkv_device.hpp"
+#include "pkv_internal.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kRopeThreads = 256;
+
+// f_i of pair i (fp64), every operation a separately rounded IEEE one (no
+// contraction), so only pow itself can differ from another fp64 evaluation
+// of the same formula.  The blend is continuous at both band edges.
+__device__ __forceinline__ double rope_freq(int i, int D, const RopeParams& rp) {
+  const double base = __ddiv_rn(1.0, pow(rp.theta, __ddiv_rn(2.0 * i, (double)D)));
+  const double w = __ddiv_rn(2.0 * 3.14159265358979323846, base);   // wavelength
+  const double lw = __ddiv_rn(rp.original_max, rp.low_freq_factor);
+  const double hw = __ddiv_rn(rp.original_max, rp.high_freq_factor);
+  if (w > lw) return __ddiv_rn(base, rp.factor);
+  if (w >= hw) {
+    const double a = __ddiv_rn(__dsub_rn(__ddiv_rn(rp.original_max, w), rp.low_freq_factor),
+                               __dsub_rn(rp.high_freq_factor, rp.low_freq_factor));
+    return __dadd_rn(__dmul_rn(__dsub_rn(1.0, a), __ddiv_rn(base, rp.factor)),
+                     __dmul_rn(a, base));
+  }
+  return base;
+}
+
+// Nearest-even rounding of a double straight to bf16 (8 significant bits):
+// round the double's 52-bit significand at bit 45, then the value is exact
+// in binary32 and its top 16 bits are the bf16.  (Finite values in the
+// normal range; rotated activations are.)
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long lsb = (u >> 45) & 1ull;
+  u += (1ull << 44) - 1ull + lsb;
+  u &= ~((1ull << 45) - 1ull);
+  const float f = (float)__longlong_as_double((long long)u);   // exact
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// Rotate one pair; bf16 bits in, bf16 bits out.
+__device__ __forceinline__ void rotate_pair(uint32_t pair, double angle, uint16_t& r0,
+                                            uint16_t& r1) {
+  const double x0 = (double)bf16_lo(pair), x1 = (double)bf16_hi(pair);
+  double s, c;
+  sincos(angle, &s, &c);
+  // two rounded products and a rounded sum each, no fused multiply-add
+  r0 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x0, c), __dmul_rn(x1, s)));
+  r1 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x0, s), __dmul_rn(x1, c)));
+}
+
+template <int D, int KIND>
+__global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
+    const uint32_t* q, uint32_t* q_out, const uint32_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int32_t* __restrict__ positions,
+    const int32_t* __restrict__ slots, unsigned char* k_cache, unsigned char* v_cache,
+    float* k_scale, float* v_scale, int Hq, int Hkv, int BS, int NB, const RopeParams rp) {
+  constexpr int HP = D / 2;                   // pairs per head
+  __shared__ uint32_t k_rot[8 * HP];          // the token's rotated key heads (Hkv <= 8)
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const double pos = (double)positions[i];
+  // (the angle pos * f is one rounded fp64 product, as in the oracle)
+
+  // query heads -> q_out (in place allowed: each pair is read, then written)
+  for (int t = tid; t < Hq * HP; t += kRopeThreads) {
+    const int64_t e = (int64_t)i * Hq * HP + t;
+    uint16_t r0, r1;
+    rotate_pair(q[e], __dmul_rn(pos, rope_freq(t % HP, D, rp)), r0, r1);
+    q_out[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+  }
+  // key heads -> LDS
+  for (int t = tid; t < Hkv * HP; t += kRopeThreads) {
+    uint16_t r0, r1;
+    rotate_pair(k_new[(int64_t)i * Hkv * HP + t], __dmul_rn(pos, rope_freq(t % HP, D, rp)), r0,
+                r1);
+    k_rot[t] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+  }
+  __syncthreads();
+
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= (int64_t)NB * BS) return;
+  const int64_t row = slot * Hkv * D;         // element offset of the slot's row
+  if constexpr (KIND == kKvBf16) {
+    uint32_t* kd = reinterpret_cast<uint32_t*>(k_cache) + row / 2;
+    uint32_t* vd = reinterpret_cast<uint32_t*>(v_cache) + row / 2;
+    const uint32_t* vs = reinterpret_cast<const uint32_t*>(v_new) + (int64_t)i * Hkv * HP;
+    for (int t = tid; t < Hkv * HP; t += kRopeThreads) {
+      kd[t] = k_rot[t];
+      vd[t] = vs[t];
+    }
+  } else {
+    // one wave per (kv head, K or V); lane l holds elements l, l + 64, ...
+    constexpr int PER = D / kWave;
+    const int lane = tid & (kWave - 1);
+    const int64_t blk = slot / BS;
+    const bool opens = slot % BS == 0;
+    for (int job = tid >> 6; job < 2 * Hkv; job += kRopeThreads / kWave) {
+      const int g = job >> 1;
+      const bool is_v = job & 1;
+      float x[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + k * kWave;
+        const uint32_t bits = is_v ? (uint32_t)v_new[((int64_t)i * Hkv + g) * D + d]
+                                   : (k_rot[g * HP + d / 2] >> (16 * (d & 1))) & 0xffffu;
+        x[k] = __uint_as_float(bits << 16);
+      }
+      float* scale_slot = (is_v ? v_scale : k_scale) + blk * Hkv + g;
+      float sc;
+      if (opens) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) amax = fmaxf(amax, __builtin_fabsf(x[k]));
+        amax = wave_max(amax);
+        sc = KIND == kKvInt8 ? int8_block_scale(amax) : fp8_block_scale(amax);
+        if (lane == 0) *scale_slot = sc;
+      } else {
+        sc = *scale_slot;
+      }
+      unsigned char* dst = (is_v ? v_cache : k_cache) + row + (int64_t)g * D;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        dst[lane + k * kWave] = (unsigned char)(KIND == kKvInt8 ? int8_encode_scaled(x[k], sc)
+                                                                : fp8_encode_scaled(x[k], sc));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                              const int32_t* positions, const int32_t* slots, void* k_cache,
+                              void* v_cache, float* k_scale, float* v_scale, int N, int Hq,
+                              int Hkv, int D, int BS, int NB, int kind, const RopeParams& rp,
+                              hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  if (Hkv > 8) return hipErrorInvalidValue;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(N), dim3(kRopeThreads), 0, stream, (const uint32_t*)q,
+                       (uint32_t*)q_out, (const uint32_t*)k_new, (const uint16_t*)v_new,
+                       positions, slots, (unsigned char*)k_cache, (unsigned char*)v_cache,
+                       k_scale, v_scale, Hq, Hkv, BS, NB, rp);
+  };
+  if (D == 128) {
+    if (kind == kKvBf16) go(rope_append_kernel<128, kKvBf16>);
+    else if (kind == kKvFp8) go(rope_append_kernel<128, kKvFp8>);
+    else go(rope_append_kernel<128, kKvInt8>);
+  } else if (D == 64) {
+    if (kind == kKvBf16) go(rope_append_kernel<64, kKvBf16>);
+    else if (kind == kKvFp8) go(rope_append_kernel<64, kKvFp8>);
+    else go(rope_append_kernel<64, kKvInt8>);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

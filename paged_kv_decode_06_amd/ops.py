@@ -61,6 +61,10 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = I
+        Dd = ctypes.c_double
+        lib.pkv_rope_kv_append.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                           Dd, Dd, Dd, Dd, Dd, P]
+        lib.pkv_rope_kv_append.restype = I
         lib.pkv_paged_attention.argtypes = [P, P, I, P, P, P, P, P, P, F, I, I, P, I, I, I, I,
                                             I, I, I, I, P, S, P]
         lib.pkv_paged_attention.restype = I
@@ -151,6 +155,43 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scal
                                _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB,
                                kvd, _stream(stream))
     _check("pkv_kv_append", st)
+
+
+LLAMA3_ROPE = dict(theta=500000.0, factor=32.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                   original_max_len=8192.0)
+
+
+def rope_kv_append(q, k_new, v_new, positions, slot_mapping, k_cache, v_cache, k_scale=None,
+                   v_scale=None, q_out=None, theta=500000.0, factor=32.0, low_freq_factor=1.0,
+                   high_freq_factor=4.0, original_max_len=8192.0, stream=None) -> None:
+    """pkv_rope_kv_append: rotate q (into q_out; in place when q_out is None)
+    and the new keys at `positions`, then append the rotated keys and the
+    values into their slots.  Defaults are the Llama 3 RoPE parameters."""
+    kvd = _kv_dtype(k_cache)
+    if q_out is None:
+        q_out = q
+    for t, name in ((q, "q"), (q_out, "q_out"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, name, torch.bfloat16, 3)
+    _need(positions, "positions", torch.int32, 1)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    _need(k_cache, "k_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    if kvd != KV_BF16:
+        _need(k_scale, "k_scale", torch.float32, 2)
+        _need(v_scale, "v_scale", torch.float32, 2)
+    N, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    NB, BS = k_cache.shape[0], k_cache.shape[1]
+    if (tuple(q_out.shape) != (N, Hq, D) or tuple(k_new.shape) != (N, Hkv, D)
+            or tuple(v_new.shape) != (N, Hkv, D) or positions.shape[0] != N
+            or slot_mapping.shape[0] != N or tuple(k_cache.shape) != (NB, BS, Hkv, D)):
+        raise ValueError("q, q_out, k_new, v_new, positions, slot_mapping and the caches disagree")
+    st = _load().pkv_rope_kv_append(
+        _ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(slot_mapping),
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), N, Hq, Hkv, D, BS, NB, kvd,
+        float(theta), float(factor), float(low_freq_factor), float(high_freq_factor),
+        float(original_max_len), _stream(stream))
+    _check("pkv_rope_kv_append", st)
 
 
 PARTITION_VALU = 0

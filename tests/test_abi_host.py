@@ -117,3 +117,16 @@ def test_decode_step_argument_checks(lib):
     assert step(D=96) == -3
     assert step(Hq=6, Hkv=4) == -2
     assert step(B=0, q=0, kn=0, vn=0) == 0         # empty batch: nothing to do
+
+
+def test_rope_kv_append_argument_checks(lib):
+    """Checked before any HIP call, so this runs without a GPU."""
+    f = lib.pkv_rope_kv_append
+    P = None
+    llama3 = (500000.0, 32.0, 1.0, 4.0, 8192.0)
+    assert f(P, P, P, P, P, P, P, P, P, P, 0, 8, 2, 64, 16, 4, 0, *llama3, P) == 0   # N = 0
+    assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 16, 64, 16, 4, 0, *llama3, P) == -3  # Hkv > 8
+    assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 2, 96, 16, 4, 0, *llama3, P) == -3   # D = 96
+    assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 2, 64, 16, 4, 0,
+             500000.0, 32.0, 4.0, 1.0, 8192.0, P) == -2                              # low >= high
+    assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 2, 64, 16, 4, 0, *llama3, P) == -1   # NULL tensors
