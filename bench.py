@@ -380,15 +380,21 @@ def main():
 
     # the RoPE-fused append at the same batch (rotating q into a scratch
     # tensor and appending the rotated keys into the first cache copy), 50
-    # launches between events
+    # launches between events.  A bounded spin on the stream first lets the
+    # host queue all 50 before the first runs, so the events time the GPU,
+    # not the launch rate of a few-microsecond kernel.
     q_rot = torch.empty_like(wl.q)
     pos = (wl.context_lens - 1).to(torch.int32)
     kc, vc, ks, vs = caches[0]
     r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        for i in range(60):
-            if i == 10:
-                r0.record(stream)
+        for i in range(10):
+            ops.rope_kv_append(wl.q, wl.k_new, wl.v_new, pos, wl.slot_mapping, kc, vc, ks, vs,
+                               q_out=q_rot, stream=stream)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)          # ~10 ms of GPU clock cycles
+        r0.record(stream)
+        for i in range(50):
             ops.rope_kv_append(wl.q, wl.k_new, wl.v_new, pos, wl.slot_mapping, kc, vc, ks, vs,
                                q_out=q_rot, stream=stream)
         r1.record(stream)

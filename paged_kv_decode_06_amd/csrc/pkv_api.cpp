@@ -463,8 +463,9 @@ int pkv_rope_kv_append(const void* q, void* q_out, const void* k_new, const void
   if ((((uintptr_t)q) | ((uintptr_t)q_out) | ((uintptr_t)k_new) | ((uintptr_t)v_new) |
        ((uintptr_t)k_cache) | ((uintptr_t)v_cache)) & 3u)
     return fail(PKV_ERR_ALIGN, "q, q_out, k_new, v_new and the caches must be 4-byte aligned");
-  const pkv::RopeParams rp{rope_theta, rope_factor, low_freq_factor, high_freq_factor,
-                           original_max_len};
+  pkv::RopeParams rp{rope_theta, rope_factor, low_freq_factor, high_freq_factor,
+                     original_max_len, {}};
+  pkv::rope_freqs(D, rp);
   hipError_t e = pkv::launch_rope_append(q, q_out, k_new, v_new, positions, slot_mapping,
                                          k_cache, v_cache, k_scale, v_scale, N, Hq, Hkv, D, BS,
                                          NB, kv_dtype, rp, static_cast<hipStream_t>(stream));

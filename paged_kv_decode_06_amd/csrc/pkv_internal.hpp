@@ -106,10 +106,12 @@ std::atomic<int>& path_flag();
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream);
 
 // Rotary embedding parameters (the Llama 3 scaled frequencies; factor 1:
-// plain RoPE).
+// plain RoPE) and the D / 2 frequencies they give (rope_freqs, host side).
 struct RopeParams {
   double theta, factor, low_freq_factor, high_freq_factor, original_max;
+  double freq[64];
 };
+void rope_freqs(int D, RopeParams& rp);
 
 // RoPE of q (into q_out) and of the new keys, then the append of the rotated
 // keys and the values into `slots` (see rope_append.hip).  Hkv <= 8.

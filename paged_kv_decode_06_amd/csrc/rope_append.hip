@@ -10,13 +10,18 @@
 // prefill table is scaled; here one rule serves both (factor = 1 turns the
 // scaling off).
 //
-// One workgroup per token: it rotates the token's query heads into q_out and
-// its new key heads into LDS, then appends the rotated key and the value row
-// exactly as the stand-alone append does (bf16 copy, or fp8 / int8 codes
+// The D / 2 frequencies are computed once per call on the host (they depend
+// only on D and the parameters) and passed in the kernel arguments.  Grid
+// (token, part): part 0 rotates the token's new key heads into LDS and
+// appends the rotated key and the value row exactly as the stand-alone
+// append does; parts 1.. rotate kQHeads query heads each into q_out.  Every
+// workgroup first tabulates the cos / sin of the token's D / 2 angles (bf16 copy, or fp8 / int8 codes
 // with a per-(block, kv head) scale).  The angle, cos / sin and the rotation
 // are computed in fp64 and the result is rounded once, straight from fp64
 // to bf16 (nearest even): each rotated element is the nearest bf16 to the
 // fp64 rotation.
+
+#include <cmath>
 
 #include "pkv_device.hpp"
 #include "pkv_internal.hpp"
@@ -25,24 +30,7 @@ namespace pkv {
 namespace {
 
 constexpr int kRopeThreads = 256;
-
-// f_i of pair i (fp64), every operation a separately rounded IEEE one (no
-// contraction), so only pow itself can differ from another fp64 evaluation
-// of the same formula.  The blend is continuous at both band edges.
-__device__ __forceinline__ double rope_freq(int i, int D, const RopeParams& rp) {
-  const double base = __ddiv_rn(1.0, pow(rp.theta, __ddiv_rn(2.0 * i, (double)D)));
-  const double w = __ddiv_rn(2.0 * 3.14159265358979323846, base);   // wavelength
-  const double lw = __ddiv_rn(rp.original_max, rp.low_freq_factor);
-  const double hw = __ddiv_rn(rp.original_max, rp.high_freq_factor);
-  if (w > lw) return __ddiv_rn(base, rp.factor);
-  if (w >= hw) {
-    const double a = __ddiv_rn(__dsub_rn(__ddiv_rn(rp.original_max, w), rp.low_freq_factor),
-                               __dsub_rn(rp.high_freq_factor, rp.low_freq_factor));
-    return __dadd_rn(__dmul_rn(__dsub_rn(1.0, a), __ddiv_rn(base, rp.factor)),
-                     __dmul_rn(a, base));
-  }
-  return base;
-}
+constexpr int kQHeads = 8;   // query heads per workgroup
 
 // Nearest-even rounding of a double straight to bf16 (8 significant bits):
 // round the double's 52-bit significand at bit 45, then the value is exact
@@ -57,12 +45,11 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
-// Rotate one pair; bf16 bits in, bf16 bits out.
-__device__ __forceinline__ void rotate_pair(uint32_t pair, double angle, uint16_t& r0,
+// Rotate one pair by the angle whose cosine and sine are c, s; bf16 bits in,
+// bf16 bits out.
+__device__ __forceinline__ void rotate_pair(uint32_t pair, double c, double s, uint16_t& r0,
                                             uint16_t& r1) {
   const double x0 = (double)bf16_lo(pair), x1 = (double)bf16_hi(pair);
-  double s, c;
-  sincos(angle, &s, &c);
   // two rounded products and a rounded sum each, no fused multiply-add
   r0 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x0, c), __dmul_rn(x1, s)));
   r1 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x0, s), __dmul_rn(x1, c)));
@@ -76,23 +63,38 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
     float* k_scale, float* v_scale, int Hq, int Hkv, int BS, int NB, const RopeParams rp) {
   constexpr int HP = D / 2;                   // pairs per head
   __shared__ uint32_t k_rot[8 * HP];          // the token's rotated key heads (Hkv <= 8)
+  __shared__ double cs[HP][2];                // cos, sin of pair j's angle (every head's)
   const int i = blockIdx.x;
+  const int part = blockIdx.y;
   const int tid = threadIdx.x;
   const double pos = (double)positions[i];
-  // (the angle pos * f is one rounded fp64 product, as in the oracle)
 
-  // query heads -> q_out (in place allowed: each pair is read, then written)
-  for (int t = tid; t < Hq * HP; t += kRopeThreads) {
-    const int64_t e = (int64_t)i * Hq * HP + t;
-    uint16_t r0, r1;
-    rotate_pair(q[e], __dmul_rn(pos, rope_freq(t % HP, D, rp)), r0, r1);
-    q_out[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+  // the angle pos * f_j is one rounded fp64 product, as in the oracle
+  for (int j = tid; j < HP; j += kRopeThreads) {
+    double sn, c;
+    sincos(__dmul_rn(pos, rp.freq[j]), &sn, &c);
+    cs[j][0] = c;
+    cs[j][1] = sn;
+  }
+  __syncthreads();
+
+  if (part > 0) {
+    // query heads h0 .. h0 + kQHeads - 1 -> q_out (in place allowed: each
+    // pair is read, then written)
+    const int h0 = (part - 1) * kQHeads;
+    const int n = min(kQHeads, Hq - h0) * HP;
+    for (int t = tid; t < n; t += kRopeThreads) {
+      const int64_t e = ((int64_t)i * Hq + h0) * HP + t;
+      uint16_t r0, r1;
+      rotate_pair(q[e], cs[t % HP][0], cs[t % HP][1], r0, r1);
+      q_out[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    }
+    return;
   }
   // key heads -> LDS
   for (int t = tid; t < Hkv * HP; t += kRopeThreads) {
     uint16_t r0, r1;
-    rotate_pair(k_new[(int64_t)i * Hkv * HP + t], __dmul_rn(pos, rope_freq(t % HP, D, rp)), r0,
-                r1);
+    rotate_pair(k_new[(int64_t)i * Hkv * HP + t], cs[t % HP][0], cs[t % HP][1], r0, r1);
     k_rot[t] = (uint32_t)r0 | ((uint32_t)r1 << 16);
   }
   __syncthreads();
@@ -148,6 +150,31 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
 
 }  // namespace
 
+// f_i of pair i < D / 2 (fp64, on the host), each operation a separately
+// rounded IEEE one in the order of the formula.  The blend is continuous at
+// both band edges.
+void rope_freqs(int D, RopeParams& rp) {
+  const double pi = 3.14159265358979323846;
+  const double lw = rp.original_max / rp.low_freq_factor;
+  const double hw = rp.original_max / rp.high_freq_factor;
+  for (int i = 0; i < D / 2; ++i) {
+    const volatile double e = (2.0 * i) / (double)D;   // (volatile: no contraction or reordering)
+    const double base = 1.0 / std::pow(rp.theta, (double)e);
+    const double w = 2.0 * pi / base;                   // wavelength
+    double f = base;
+    if (w > lw) {
+      f = base / rp.factor;
+    } else if (w >= hw) {
+      const volatile double a =
+          (rp.original_max / w - rp.low_freq_factor) / (rp.high_freq_factor - rp.low_freq_factor);
+      const volatile double t0 = (1.0 - a) * (base / rp.factor);
+      const volatile double t1 = a * base;
+      f = t0 + t1;
+    }
+    rp.freq[i] = f;
+  }
+}
+
 hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new,
                               const int32_t* positions, const int32_t* slots, void* k_cache,
                               void* v_cache, float* k_scale, float* v_scale, int N, int Hq,
@@ -155,8 +182,9 @@ hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, con
                               hipStream_t stream) {
   if (N == 0) return hipSuccess;
   if (Hkv > 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)N, 1u + (unsigned)((Hq + kQHeads - 1) / kQHeads));
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(N), dim3(kRopeThreads), 0, stream, (const uint32_t*)q,
+    hipLaunchKernelGGL(kernel, grid, dim3(kRopeThreads), 0, stream, (const uint32_t*)q,
                        (uint32_t*)q_out, (const uint32_t*)k_new, (const uint16_t*)v_new,
                        positions, slots, (unsigned char*)k_cache, (unsigned char*)v_cache,
                        k_scale, v_scale, Hq, Hkv, BS, NB, rp);
