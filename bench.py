@@ -403,7 +403,8 @@ def main():
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (part_avg_ms * 1e-3) / 1e9
-    waves = ops.lib().pkv_attention_waves(wl.D, wl.BS, wl.G, kvd)
+    waves = ops.attention_waves(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, kvd)
+    unit_heads = ops.decode_unit_heads(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, kvd)
     result = {
         "metric": "KV-read GB/s per decode-attention step (1 MI355X)",
         "value": round(value, 2),
@@ -447,6 +448,7 @@ def main():
             "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
             "rope_kv_append_us_mean": round(rope_us, 2),
             "persistent_waves": waves,
+            "kv_heads_per_wave": unit_heads,
         },
     }
     if not args.no_cpu:

@@ -240,9 +240,29 @@ const char* pkv_status_string(int status);
 /* Detail of the last failing call on this host thread ("" if none). */
 const char* pkv_last_error(void);
 
-/* Number of persistent waves the attention grid uses on the current device
- * (0 if the device cannot be queried).  Informational. */
-int pkv_attention_waves(int D, int BS, int G, int kv_dtype);
+/* Number of persistent waves the grid of a decode call (one query per
+ * sequence, no window) with these sizes uses on the current device, under
+ * the current selections (0 if unsupported or the device cannot be
+ * queried).  Informational. */
+int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
+
+/* Kv heads one wave of the MFMA partition kernel serves together in such a
+ * call (a unit of adjacent kv heads whose rows lie side by side in every
+ * cache row, so a wave streams one contiguous run of unit * D * elem bytes
+ * per token): 2 when Hkv is even and the wider kernel fits two workgroups
+ * on a compute unit, else 1; always 1 for the VALU kernel and for calls
+ * with several queries or a window.  The result does not depend on it
+ * beyond floating-point summation order.  0 if unsupported.
+ * Informational. */
+int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
+
+/* mode 0 (default): units as above; mode 1: one kv head per wave always.
+ * Process-wide, read at the start of every attention call and workspace
+ * query, like pkv_select_partition_kernel (switch only between calls, size
+ * the workspace after switching).  PKV_UNIT_HEADS=1 in the environment
+ * selects mode 1 when the library loads.  PKV_ERR_UNSUPPORTED for another
+ * value. */
+int pkv_select_unit_heads(int mode);
 
 /* Partition-kernel variants.  Both compute the same attention; MFMA (the
  * default) puts the GQA group on the matrix cores, VALU uses fp32 vector

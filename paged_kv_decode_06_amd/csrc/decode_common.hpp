@@ -17,17 +17,19 @@
 // block's tail cannot leak in).
 //
 // Work split (flash-decoding style split of the context).  The work axis is
-// every (sequence b, kv head g, page j) triple in that order: position
-// Hkv*pre[b] + g*n_b + j, where n_b = ceil(L_b / BS) and pre is the prefix
-// sum of n_b.  The axis is cut into consecutive pieces of equal page count
+// every (sequence b, unit u, page j) triple in that order: position
+// U*pre[b] + u*n_b + j, where n_b = ceil(L_b / BS) and pre is the prefix
+// sum of n_b.  A unit is the set of kv heads one wave serves together: one
+// kv head (U = Hkv units per sequence) or, in the MFMA kernel's decode
+// instantiations, HG adjacent kv heads (U = Hkv / HG).  The axis is cut into consecutive pieces of equal page count
 // for a persistent grid of W waves, so every wave streams the same number of
 // KV bytes whatever the length mix.  kPiecesPerWave pieces per wave are
 // taken from far apart on the axis; the default is one (measured: a second
 // or third piece costs more in per-piece setup than it recovers in balance).
 //
-// A (b, g) run that one piece covers completely is finished in place (out
+// A (b, u) run that one piece covers completely is finished in place (out
 // written as bf16); otherwise each piece that touches it leaves (m, l, o)
-// for its share in workspace row k + segment (segment = b*Hkv + g).  Both k
+// for its share in workspace row k + segment (segment = b*U + u).  Both k
 // and the segment grow along the axis, so the row is unique, and the rows
 // of one segment are consecutive for the merge kernel.  m is kept in the
 // exp2 domain (scores times scale*log2(e)).
@@ -102,12 +104,12 @@ __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
   __syncthreads();
 }
 
-// Last b in [0, B) with Hkv * pre[b] <= x (x < Hkv * pre[B]).
-__device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int Hkv, int x) {
+// Last b in [0, B) with U * pre[b] <= x (x < U * pre[B]).
+__device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int U, int x) {
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (Hkv * s_pre[mid] <= x)
+    if (U * s_pre[mid] <= x)
       lo = mid;
     else
       hi = mid - 1;
@@ -146,20 +148,20 @@ __device__ __forceinline__ void run_split(const WorkSplit& s, int wave, Body&& b
   }
 }
 
-// One wave's share of a (sequence, kv head) run: pages [j0, j1) of run
-// (b, g), whose first page sits at `run_start` on the work axis.
+// One wave's share of a (sequence, unit) run: pages [j0, j1) of run
+// (b, u), whose first page sits at `run_start` on the work axis.
 struct Piece {
-  int b, g, n_b, run_start, j0, j1;
+  int b, u, n_b, run_start, j0, j1;
 };
 
-__device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int Hkv, int x,
+__device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int U, int x,
                                               int x_end) {
   Piece pc;
-  pc.b = find_sequence(s_pre, B, Hkv, x);
+  pc.b = find_sequence(s_pre, B, U, x);
   pc.n_b = s_pre[pc.b + 1] - s_pre[pc.b];
-  const int seg_start = Hkv * s_pre[pc.b];
-  pc.g = (x - seg_start) / pc.n_b;
-  pc.run_start = seg_start + pc.g * pc.n_b;
+  const int seg_start = U * s_pre[pc.b];
+  pc.u = (x - seg_start) / pc.n_b;
+  pc.run_start = seg_start + pc.u * pc.n_b;
   pc.j0 = x - pc.run_start;
   pc.j1 = min(pc.n_b, x_end - pc.run_start);
   return pc;

@@ -6,8 +6,10 @@
 // keys the query sees in that piece.  With M = max_p m_p:
 //   out = sum_p exp2(m_p - M) o_p / sum_p exp2(m_p - M) l_p,
 // which is the softmax over every key the query sees (0 if it sees none).
-// Output rows are (b, i, h) for query i < q_len_b; the share column of
-// query i, head h = g G + jj is i G + jj.
+// Output rows are (b, i, h) for query i < q_len_b.  The partition kernel's
+// shares are per (sequence, unit) with a unit of hg adjacent kv heads (the
+// UG = hg G query heads u UG .. u UG + UG - 1); the share column of query i,
+// head h = u UG + jj is i UG + jj.
 
 #include <float.h>
 
@@ -17,7 +19,7 @@ namespace pkv {
 namespace {
 
 // Merge: one wave per (sequence, query head), four per workgroup.  The
-// rows of a (b, g) run are k + segment for the consecutive pieces k0..k1
+// rows of a (b, u) run are k + segment for the consecutive pieces k0..k1
 // that cover it.  A row is D floats; TPR lanes take 4 dims each, so
 // the wave reads RPW rows per step, and the unrolled loop keeps several
 // steps of independent loads in flight; the RPW row groups are summed with
@@ -35,13 +37,14 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
   const int qi = (int)(bqh / p.Hq % p.max_q);
   const int h = (int)(bqh % p.Hq);
   if (qi >= seq_queries(p, b)) return;
-  const int g = h / G;
-  const int col = qi * G + h % G;
+  const int UG = p.hg * G;
+  const int u = h / UG;
+  const int col = qi * UG + h % UG;
   const int C = p.cols;
-  const int Hkv = p.Hkv;
+  const int U = p.Hkv / p.hg;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
-  const int total = Hkv * pre_B;
+  const int total = U * pre_B;
   const int n_b = pre_b1 - pre_b;
   const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
   uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D;
@@ -50,11 +53,11 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
     return;
   }
   const WorkSplit split = make_split(total, p.total_waves);
-  const int start = Hkv * pre_b + g * n_b;
+  const int start = U * pre_b + u * n_b;
   const int k0 = piece_of(split, start);
   const int k1 = piece_of(split, start + n_b - 1);
   if (k0 == k1) return;                        // finished by the partition kernel
-  const int seg = b * Hkv + g;
+  const int seg = b * U + u;
   const int P = k1 - k0 + 1;
   const int64_t rok0 = (int64_t)k0 + seg;
   const float* __restrict__ ml = p.ws_ml;
@@ -112,13 +115,14 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   const int qi = (int)(bqh / p.Hq % p.max_q);
   const int h = (int)(bqh % p.Hq);
   if (qi >= seq_queries(p, b)) return;
-  const int g = h / G;
-  const int col = qi * G + h % G;
+  const int UG = p.hg * G;
+  const int u = h / UG;
+  const int col = qi * UG + h % UG;
   const int C = p.cols;
-  const int Hkv = p.Hkv;
+  const int U = p.Hkv / p.hg;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
-  const int total = Hkv * pre_B;
+  const int total = U * pre_B;
   const int n_b = pre_b1 - pre_b;
   const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
   uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D;
@@ -127,11 +131,11 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
     return;
   }
   const WorkSplit split = make_split(total, p.total_waves);
-  const int start = Hkv * pre_b + g * n_b;
+  const int start = U * pre_b + u * n_b;
   const int k0 = piece_of(split, start);
   const int k1 = piece_of(split, start + n_b - 1);
   if (k0 == k1) return;
-  const int seg = b * Hkv + g;
+  const int seg = b * U + u;
   const int P = k1 - k0 + 1;
   const int64_t row0 = (int64_t)k0 + seg;
   const float* __restrict__ ml = p.ws_ml;

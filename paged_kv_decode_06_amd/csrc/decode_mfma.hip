@@ -7,28 +7,30 @@
 //   scores  S^T[t][h] = sum_d K[t][d] q[h][d]       16x16x32 bf16 MFMA,
 //           A = a 16-token x 32-dim slice of the K tile, B = the group's q
 //           (columns past G are zero)
-//   output  O[h][d] += sum_t P[h][t] V[t][d]          16x16x16 bf16 MFMA,
-//           A = P in exactly the register layout S^T came out in,
-//           B = four tokens of one head dim of the V tile
+//   output  O^T[d][h] += sum_t V[t][d] P[h][t]        16x16x16 bf16 MFMA,
+//           A = four tokens of one head dim of the V tile, B = P^T in
+//           exactly the register layout S^T came out in
 //
 // Lane l (n = l % 16, r = l / 16) ends a score step holding S^T for tokens
-// 4r..4r+3 of the tile and head n, which is the A-operand layout of the
-// 16x16x16 product, so P never leaves its registers.
+// 4r..4r+3 of the tile and column n, which is the B-operand layout of the
+// 16x16x16 product, so P never leaves its registers; O^T comes out with
+// column n in the same lanes, so the softmax rescale of O needs no shuffle.
+// In the decode instantiations a wave may serve a unit of HG adjacent kv
+// heads at once (their HG * G query heads are the columns; see the kernel).
 //
 // Data path per 16-token tile: K and V rows are read from HBM with 16-byte
-// non-temporal loads laid out as whole 256-byte runs of consecutive lanes
-// (the layout that streams best through the memory system), then staged in
-// one LDS buffer per wave as bf16 rows with a padded pitch: K first (read
+// non-temporal loads laid out as whole runs of consecutive lanes per unit
+// row (the layout that streams best through the memory system), then staged
+// in one LDS buffer per wave as bf16 rows with a padded pitch: K first (read
 // back as the A operands, 16 bytes a lane), then V over it (read back with
 // the gfx950 transposing LDS read, which hands each lane four tokens of one
-// head dim, the B operand of the PV product).  fp8 and int8 codes are widened to
-// bf16 exactly on the way into LDS; the per-(block, kv head) K scale then
+// head dim, the A operand of the PV product).  fp8 and int8 codes are widened
+// to bf16 exactly on the way into LDS; the per-(block, kv head) K scale then
 // multiplies the scores and the V scale is folded into P.
 //
-// Online softmax: one running max per head (kept by the lanes of column
-// n), raised only when a tile brings a larger score; the rescale of O is
-// then a wave-uniform branch.  The work split over waves is described in
-// decode_common.hpp.
+// Online softmax: one running max per column, raised only when a tile
+// brings a larger score; the rescale of O is then a wave-uniform branch.
+// The work split over waves is described in decode_common.hpp.
 //
 // Decode step: with k_new set, the kernel also performs the one-token append
 // of each sequence (see park_new_rows), so a step is this kernel plus the merge.
@@ -49,25 +51,36 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-template <int D_, int BS_, int G_, int KIND_>
+// HG: kv heads one wave serves together (a unit).  Their rows sit side by
+// side in every cache row, so a unit row is one contiguous run of HG * RB
+// bytes; the HG * G query heads of the unit fill the 16 MFMA columns.
+template <int D_, int BS_, int G_, int KIND_, int HG_ = 1>
 struct MfmaShape {
   static constexpr int D = D_;
   static constexpr int BS = BS_;
   static constexpr int G = G_;
+  static constexpr int HG = HG_;
+  static constexpr int UG = HG * G;           // query heads of a unit (columns used)
   static constexpr bool Q8 = KIND_ != kKvBf16;    // one-byte codes with per-block scales
   static constexpr bool INT8 = KIND_ == kKvInt8;  // (else fp8 e4m3fn when Q8)
   static constexpr int EB = Q8 ? 1 : 2;         // bytes per cache element
   static constexpr int RB = D * EB;           // bytes of one token's head row in the cache
-  static constexpr int LPR = RB / 16;         // lanes per row (16 bytes each)
+  static constexpr int URB = HG * RB;         // bytes of one token's unit row
+  static constexpr int LPR = URB / 16;        // lanes per unit row (16 bytes each)
   static constexpr int RPI = kWave / LPR;     // rows per wave-wide load
   static constexpr int NI = 16 / RPI;         // wave-wide loads per 16-token tile
   static constexpr int NKK = D / 32;          // score k-steps (16x16x32)
   static constexpr int NBN = D / 16;          // output n-blocks (16x16x16)
   static constexpr int SUB = BS / 16;         // 16-token tiles per page
-  static constexpr int PITCH = 2 * D + 32;    // LDS row pitch (bytes) of a bf16 tile
-  static constexpr bool KV_TOGETHER = 16 * RB <= 2048;   // issue a tile's K and V loads at once
-  static_assert(G >= 1 && G <= 16, "the group is the 16-wide N dimension");
-  static_assert(NI >= 1 && BS % 16 == 0, "shape");
+  static constexpr int PITCH = HG * 2 * D + 32;   // LDS row pitch (bytes) of a bf16 tile
+  static constexpr bool KV_TOGETHER = 16 * URB <= 2048;   // issue a tile's K and V loads at once
+  // waves per SIMD: a unit of several heads keeps several times the bytes
+  // of a one-head tile in flight per wave, and two such waves per SIMD
+  // measured faster than three (bf16 D = 128, two heads: 107 vs 111 us on
+  // a B64 step), although the registers would fit three
+  static constexpr int WPE = HG > 1 ? 2 : PKV_MFMA_WAVES_PER_EU;
+  static_assert(UG >= 1 && UG <= 16, "the unit's heads are the 16-wide N dimension");
+  static_assert(LPR <= kWave && NI >= 1 && BS % 16 == 0, "shape");
 };
 
 __device__ __forceinline__ short bf16_bits(float x) {
@@ -110,16 +123,26 @@ __device__ __forceinline__ void q8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16x
     fp8x16_to_bf16(c, lo, hi);
 }
 
-// Streaming 16-byte load: every KV byte is read once, so it is marked
-// non-temporal (probe measurements on this layout: ~10% more bandwidth).
-__device__ __forceinline__ uint4 load_nt(const unsigned char* p) {
-  const uint32_t* a = reinterpret_cast<const uint32_t*>(p);
-  uint4 v;
-  v.x = __builtin_nontemporal_load(a + 0);
-  v.y = __builtin_nontemporal_load(a + 1);
-  v.z = __builtin_nontemporal_load(a + 2);
-  v.w = __builtin_nontemporal_load(a + 3);
-  return v;
+// Tile loads: buffer loads off a descriptor for the tile's first byte
+// (wave-uniform), a 32-bit per-lane offset and a per-load scalar offset, so
+// a tile costs one vector register of addressing however many loads it
+// takes.  Every KV byte is read once, so the loads are non-temporal (probe
+// measurements on this layout: ~10% more bandwidth).  Descriptor: stride 0,
+// 2^31 - 1 bytes of range (a tile spans 16 cache rows), 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const unsigned char* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, 0x7fffffff, 0x00020000);
+}
+
+constexpr int kCachePolicyNT = 2;   // the non-temporal bit of the buffer instructions
+
+__device__ __forceinline__ uint4 load_tile_chunk(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -151,20 +174,21 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
 }
 
 // Decode-step append inside the partition kernel.  The tile holding
-// position L - 1 of a (sequence, kv head) is read by exactly one wave, the
+// position L - 1 of a (sequence, unit) run is read by exactly one wave, the
 // one whose piece holds the run's last page.  That wave stores the step's
-// new row in the cache and writes the same values over that row of its
-// staged tile in LDS (after the tile's own rows: LDS writes of a wave land
-// in order), so it attends to what an append before the call would have
-// left; no other wave reads the row.  All the work is done early: the new
-// rows are loaded beside q at the start of the run, and when the first tile
-// of the chunk holding the last page has its loads in flight, the rows are
-// encoded (fp8 / int8), stored to the cache and parked in the wave's LDS slot in
-// tile format, hidden behind that tile's load latency; the tile holding
-// position L - 1 then only copies two rows within LDS.
-// fp8 / int8: a token at offset 0 opens its block and sets the block's scale
-// to amax / 448 (fp8) or amax / 127 (int8) first; otherwise the block keeps
-// its scale (the same arithmetic as the stand-alone append).
+// new rows (the unit's HG kv heads) in the cache and writes the same values
+// over that row of its staged tile in LDS (after the tile's own rows: LDS
+// writes of a wave land in order), so it attends to what an append before
+// the call would have left; no other wave reads the row.  All the work is
+// done early: the new rows are loaded beside q at the start of the run, and
+// when the first tile of the chunk holding the last page has its loads in
+// flight, the rows are encoded (fp8 / int8), stored to the cache and parked
+// in the wave's LDS slot in tile format, hidden behind that tile's load
+// latency; the tile holding position L - 1 then only copies two unit rows
+// within LDS.
+// fp8 / int8: a token at offset 0 opens its block and sets the block's
+// per-head scales to amax / 448 (fp8) or amax / 127 (int8) first; otherwise
+// the block keeps its scales (the same arithmetic as the stand-alone append).
 
 // 8 int8 codes -> 8 bf16 (exact).
 __device__ __forceinline__ bf16x8_t i8x8_to_bf16(const uint2 c) {
@@ -193,78 +217,145 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const uint2 c) {
   return r;
 }
 
-// Park the new K and V rows of kv head g in the wave's LDS slot `rows`
-// ([K | V], 2 D bytes each, tile format) and store them in the cache rows
-// `kdst` / `vdst`.  Lane l < D / 4 holds `part`, the bf16 elements
-// 8 l' .. 8 l' + 7 of the K row (l < D / 8, l' = l) or of the V row
-// (l' = l - D / 8).  fp8 / int8: `sk` / `sv` come in as the block's scales and
-// leave as the scales after the append (set from the rows when `opens`;
-// lane 0 then stores them at `skw` / `svw`).
+// The new rows of a unit as 16-byte bf16 chunks: chunks [0, CH) are the K
+// rows of its HG kv heads (D / 8 chunks each, in head order), [CH, 2 CH) the
+// V rows; lane l holds chunks l, l + 64, ... (NP of them).
 template <class S>
-__device__ __forceinline__ void park_new_rows(const uint4 part, int lane, unsigned char* rows,
-                                              unsigned char* kdst, unsigned char* vdst,
-                                              bool opens, float& sk, float& sv, float* skw,
-                                              float* svw) {
-  constexpr int D = S::D;
-  const bool is_k = lane < D / 8;
-  const bool mine = lane < D / 4;
-  const int c = is_k ? lane : lane - D / 8;
+struct NewRows {
+  static constexpr int CH = S::HG * S::D / 8;
+  static constexpr int NP = (2 * CH + kWave - 1) / kWave;
+};
+
+// Park the unit's new K and V rows in the wave's LDS slot `rows` ([K | V],
+// 2 CH chunks, tile format) and store them in the cache unit rows `kdst` /
+// `vdst`.  fp8 / int8: `ks` / `vs` are the block's scales of the unit's heads
+// (read when the token lands inside the block), `ksw` / `vsw` the same
+// slots for writing (when it opens the block, lane 0 stores the scales set
+// from the rows); `sk` / `sv` leave as the scales of head `mem` after the
+// append.
+template <class S>
+__device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP], int lane,
+                                              int mem, unsigned char* rows, unsigned char* kdst,
+                                              unsigned char* vdst, bool opens, float& sk,
+                                              float& sv, const float* ks, const float* vs,
+                                              float* ksw, float* vsw) {
+  constexpr int HG = S::HG, CH = NewRows<S>::CH, NP = NewRows<S>::NP;
+  constexpr int CPH = S::D / 8;   // chunks per head row
   if constexpr (S::Q8) {
-    float x[8];
-    unpack8(part, x);   // lanes past the rows hold zeros
     auto block_scale = [](float amax) {
       return S::INT8 ? int8_block_scale(amax) : fp8_block_scale(amax);
     };
     auto enc = [](float v, float sc) {
       return S::INT8 ? int8_encode_scaled(v, sc) : fp8_encode_scaled(v, sc);
     };
-    if (opens) {
-      float am = 0.0f;
+    float x[NP][8];
+    int grp[NP];   // scale group of chunk i: K of head j -> j, V of head j -> HG + j; -1: none
 #pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, __builtin_fabsf(x[e]));
-      const float amk = wave_max(is_k ? am : 0.0f);
-      const float amv = wave_max(is_k ? 0.0f : am);
-      sk = block_scale(amk);
-      sv = block_scale(amv);
+    for (int i = 0; i < NP; ++i) {
+      const int q = lane + kWave * i;
+      unpack8(part[i], x[i]);
+      grp[i] = q < CH ? q / CPH : (q < 2 * CH ? HG + (q - CH) / CPH : -1);
+    }
+    float gsc[2 * HG];   // the groups' scales after the append (wave-uniform)
+    if (opens) {
+      float amc[NP];     // amax of chunk i
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        amc[i] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amc[i] = fmaxf(amc[i], __builtin_fabsf(x[i][e]));
+      }
+#pragma unroll
+      for (int gi = 0; gi < 2 * HG; ++gi) {
+        float am = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) am = fmaxf(am, grp[i] == gi ? amc[i] : 0.0f);
+        gsc[gi] = block_scale(wave_max(am));
+      }
       if (lane == 0) {
-        *skw = sk;
-        *svw = sv;
+#pragma unroll
+        for (int j = 0; j < HG; ++j) {
+          ksw[j] = gsc[j];
+          vsw[j] = gsc[HG + j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < HG; ++j) {
+        gsc[j] = ks[j];
+        gsc[HG + j] = vs[j];
       }
     }
-    const float sc = is_k ? sk : sv;
-    uint2 codes;
-    codes.x = enc(x[0], sc) | (enc(x[1], sc) << 8) | (enc(x[2], sc) << 16) | (enc(x[3], sc) << 24);
-    codes.y = enc(x[4], sc) | (enc(x[5], sc) << 8) | (enc(x[6], sc) << 16) | (enc(x[7], sc) << 24);
-    if (mine) {
-      *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes;
-      *reinterpret_cast<bf16x8_t*>(rows + 16 * lane) =
-          S::INT8 ? i8x8_to_bf16(codes) : fp8x8_to_bf16(codes);
+    sk = gsc[0];
+    sv = gsc[HG];
+#pragma unroll
+    for (int j = 1; j < HG; ++j) {
+      if (mem == j) {
+        sk = gsc[j];
+        sv = gsc[HG + j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      float sc = gsc[0];
+#pragma unroll
+      for (int gi = 1; gi < 2 * HG; ++gi)
+        if (grp[i] == gi) sc = gsc[gi];
+      if (grp[i] >= 0) {
+        const int q = lane + kWave * i;
+        const bool is_k = q < CH;
+        const int c = is_k ? q : q - CH;
+        uint2 codes;
+        codes.x = enc(x[i][0], sc) | (enc(x[i][1], sc) << 8) | (enc(x[i][2], sc) << 16) |
+                  (enc(x[i][3], sc) << 24);
+        codes.y = enc(x[i][4], sc) | (enc(x[i][5], sc) << 8) | (enc(x[i][6], sc) << 16) |
+                  (enc(x[i][7], sc) << 24);
+        *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes;
+        *reinterpret_cast<bf16x8_t*>(rows + 16 * q) =
+            S::INT8 ? i8x8_to_bf16(codes) : fp8x8_to_bf16(codes);
+      }
     }
   } else {
-    if (mine) {
-      *reinterpret_cast<uint4*>((is_k ? kdst : vdst) + 16 * c) = part;
-      *reinterpret_cast<uint4*>(rows + 16 * lane) = part;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int q = lane + kWave * i;
+      if (q < 2 * CH) {
+        const bool is_k = q < CH;
+        *reinterpret_cast<uint4*>((is_k ? kdst : vdst) + 16 * (is_k ? q : q - CH)) = part[i];
+        *reinterpret_cast<uint4*>(rows + 16 * q) = part[i];
+      }
     }
   }
 }
 
-// Copy a parked row (2 D bytes in tile format) over row `tr` of the tile.
+// Copy a parked unit row (HG * 2 D bytes in tile format) over row `tr` of
+// the tile.
 template <class S>
 __device__ __forceinline__ void take_new_row(const unsigned char* row, unsigned char* tile, int tr,
                                              int lane) {
-  if (lane < S::D / 8)
+  if (lane < NewRows<S>::CH)
     *reinterpret_cast<uint4*>(tile + tr * S::PITCH + 16 * lane) =
         *reinterpret_cast<const uint4*>(row + 16 * lane);
 }
 
 // GEN: the generalised call (several queries per sequence, a window); the
-// decode instantiations (GEN = false) carry none of its per-lane state.
+// decode instantiations (GEN = false) carry none of its per-lane state and
+// may serve several kv heads per wave (S::HG).
+//
+// Units of HG > 1 kv heads: the unit's HG * G query heads are the 16
+// columns, column n reading kv head `mem` = n / G of the unit.  The scores
+// run one MFMA chain per kv head of the unit (K of that head times every
+// column's q) and each column keeps its own head's chain; the output runs
+// O^T += V_j^T P_j^T per head j with P_j = P restricted to head j's columns,
+// so every column sums only its own head's values.
 template <class S, bool GEN>
-__global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WAVES_PER_EU, PKV_MFMA_WAVES_PER_EU)))
+__global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(S::WPE, S::WPE)))
 void mfma_partition_kernel(const AttnParams p) {
-  constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB;
+  constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB, HG = S::HG, UG = S::UG;
   constexpr int NI = S::NI, RPI = S::RPI, LPR = S::LPR;
   constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
+  constexpr int NP = NewRows<S>::NP, CH = NewRows<S>::CH;
+  static_assert(!GEN || HG == 1, "the generalised call serves one kv head per wave");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
@@ -272,7 +363,8 @@ void mfma_partition_kernel(const AttnParams p) {
   build_prefix(p, BS, s_pre, s_tmp);
 
   const int Hkv = p.Hkv;
-  const int total = Hkv * s_pre[p.B];
+  const int U = Hkv / HG;                  // units per sequence
+  const int total = U * s_pre[p.B];
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= p.B; i += blockDim.x) p.ws_pre[i] = s_pre[i];
   if (total == 0) return;
@@ -281,18 +373,22 @@ void mfma_partition_kernel(const AttnParams p) {
   const int wave_in_block = threadIdx.x >> 6;
   const int wave = blockIdx.x * kAttnWavesPerBlock + wave_in_block;
   const size_t pre_bytes = (sizeof(int32_t) * ((size_t)p.B + 1 + kAttnBlockThreads) + 15) & ~size_t(15);
-  constexpr int WAVE_LDS = 16 * PITCH + 4 * D;   // staged tile + the new K and V rows (bf16)
+  constexpr int WAVE_LDS = 16 * PITCH + 32 * CH;   // staged tile + the new K and V unit rows (bf16)
   unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * WAVE_LDS;
-  unsigned char* new_rows = tile + 16 * PITCH;     // [K row | V row], 2 D bytes each
+  unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
 
-  const int n = lane & 15;        // head column of S^T and O; K row of the A operand
-  const int r = lane >> 4;        // 4-token group of S^T rows; 4-head group of O rows
+  const int n = lane & 15;        // column of S^T and O^T (a query head); K row of the A operand
+  const int r = lane >> 4;        // 4-token group of S^T rows; 4-dim group of O^T rows
+  // kv head of the unit that column n reads (columns past the unit's UG
+  // heads, unused when UG < 16, take the last one: their loads stay in the unit)
+  const int mem = HG > 1 ? min(n / G, HG - 1) : 0;
   const WorkSplit split = make_split(total, p.total_waves);
   const int64_t row_bytes = (int64_t)Hkv * RB;
-  // this lane's 16-byte chunk of a token row, for the global loads
-  const int load_row = lane / LPR;
-  const int load_off = 16 * (lane % LPR);
-  // tile offsets of the operand reads
+  // this lane's 16-byte chunk of a unit row, for the global loads: a 32-bit
+  // offset from the tile's (wave-uniform) first byte, so the loads take the
+  // scalar-base + vector-offset form
+  const uint32_t lane_off = (uint32_t)((lane / LPR) * row_bytes + 16 * (lane % LPR));
+  // tile offsets of the operand reads (+ 2 D bytes per kv head of the unit)
   const int k_rd = n * PITCH + 16 * r;                               // + 64 kk
   const int v_rd = (4 * r + (n >> 2)) * PITCH + 8 * (n & 3);         // + 32 nb
   const unsigned char* __restrict__ kc = static_cast<const unsigned char*>(p.k_cache);
@@ -301,33 +397,42 @@ void mfma_partition_kernel(const AttnParams p) {
 
   run_split(split, wave, [&](int x, const int x_end, const int piece) {
   while (x < x_end) {
-    const Piece pc = locate_piece(s_pre, p.B, Hkv, x, x_end);
-    const int b = pc.b, g = pc.g;
+    Piece pc = locate_piece(s_pre, p.B, U, x, x_end);
+    // (wave-uniform: kept in scalar registers)
+    pc.b = __builtin_amdgcn_readfirstlane(pc.b);
+    pc.u = __builtin_amdgcn_readfirstlane(pc.u);
+    pc.n_b = __builtin_amdgcn_readfirstlane(pc.n_b);
+    pc.run_start = __builtin_amdgcn_readfirstlane(pc.run_start);
+    pc.j0 = __builtin_amdgcn_readfirstlane(pc.j0);
+    pc.j1 = __builtin_amdgcn_readfirstlane(pc.j1);
+    const int b = pc.b, g0 = pc.u * HG;   // the unit's first kv head
     const int L_in = p.context_lens[b];
     const int L = min(max(L_in, 0), p.MBS * BS);
     // a length outside [1, MBS * BS] breaks the contract: no append then
     // (the decode step is one query per sequence: never the GEN instantiation)
     const bool append = !GEN && p.k_new != nullptr && L == L_in && L >= 1;
     const int32_t* bt_row = p.block_tables + (int64_t)b * p.MBS;
-    const int64_t head_off = (int64_t)g * RB + load_off;
-    // query tokens: column n of S^T / row n of O is query n / G, head n % G
+    const int64_t head_off = (int64_t)g0 * RB;
+    // column n: query token n / UG of the sequence, query head g0 G + n % UG
+    // (GEN: UG = G; decode: one query, the unit's UG heads)
     const int ql = GEN ? seq_queries(p, b) : 1;
-    const int ncol = G * ql;
+    const int ncol = UG * ql;
+    const int col_q = n / UG, col_h = g0 * G + n % UG;
     const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;   // first q / out row
     const SeqRange sr = GEN ? seq_range(L, ql, p.sinks, p.window, BS) : SeqRange{0, 0, 0};
     auto table_page = [&](int j) { return !GEN || j < sr.ps ? j : j + sr.gap; };
     // keys column n sees: j <= lim_n (bottom-right causal), and with a window
     // j >= lo_n or j < sinks
-    const int lim_n = n < ncol ? L - ql + n / G : -1;
+    const int lim_n = n < ncol ? L - ql + col_q : -1;
     const int lo_n = lim_n - p.window + 1;
     const bool windowed = GEN && p.window > 0;
     const int gap_end = L - ql - p.window + 1;    // keys in [sinks, gap_end) no query sees
 
-    // q of the group as the B operand: element i of k-step kk is head dim
+    // q of the columns as the B operand: element i of k-step kk is head dim
     // 32 kk + 8 r + i, the same dims the K operand's element i holds
     bf16x8_t qB[NKK];
     {
-      const uint16_t* qrow = qp + ((int64_t)(r0 + n / G) * p.Hq + g * G + n % G) * D + 8 * r;
+      const uint16_t* qrow = qp + ((int64_t)(r0 + col_q) * p.Hq + col_h) * D + 8 * r;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -336,22 +441,27 @@ void mfma_partition_kernel(const AttnParams p) {
       }
     }
     // The decode step's new rows when this piece holds the run's last page
-    // (loaded beside q; lane l < D / 4 takes 16 bytes of [K row | V row]).
+    // (loaded beside q; see NewRows for the chunks a lane takes).
     const bool has_new = append && pc.j1 == pc.n_b;
-    uint4 new_part = make_uint4(0, 0, 0, 0);
-    if (has_new && lane < D / 4) {
-      const int64_t src = ((int64_t)b * Hkv + g) * D;
-      new_part = lane < D / 8
-                     ? *reinterpret_cast<const uint4*>(p.k_new + src + 8 * lane)
-                     : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (lane - D / 8));
+    uint4 new_part[NP];
+    {
+      const int64_t src = ((int64_t)b * Hkv + g0) * D;
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int q = lane + kWave * i;
+        new_part[i] = make_uint4(0, 0, 0, 0);
+        if (has_new && q < 2 * CH)
+          new_part[i] = q < CH ? *reinterpret_cast<const uint4*>(p.k_new + src + 8 * q)
+                               : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (q - CH));
+      }
     }
-    float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: the last block's scales after the append
+    float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: head mem's last-block scales after the append
 
-    float4_t O[NBN];
+    float4_t O[NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
 #pragma unroll
     for (int nb = 0; nb < NBN; ++nb) O[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -FLT_MAX;   // running max of head n (exp2 domain)
-    float l_run = 0.0f;       // this lane's share of head n's sum
+    float m_run = -FLT_MAX;   // running max of column n (exp2 domain)
+    float l_run = 0.0f;       // this lane's share of column n's sum
 
     for (int jc = pc.j0; jc < pc.j1; jc += kWave) {
       const int nchunk = min(kWave, pc.j1 - jc);
@@ -374,46 +484,59 @@ void mfma_partition_kernel(const AttnParams p) {
       // (fp8 / int8, or D = 64) issue K and V together (~3% faster than in turn).
       // The other waves of the CU overlap their compute with the waits;
       // issuing the next tile early does not pay for the registers it costs.
-      auto tile_base = [&](int u) {
+      auto tile_base = [&](int u) {   // (wave-uniform)
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
-        return ((int64_t)phys * BS + sb * 16 + load_row) * row_bytes + head_off;
+        return ((int64_t)phys * BS + sb * 16) * row_bytes + head_off;
       };
       auto issue = [&](const unsigned char* __restrict__ src, int64_t base, uint4 (&ch)[NI]) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(src + base);
 #pragma unroll
-        for (int s = 0; s < NI; ++s) ch[s] = load_nt(src + base + (int64_t)s * RPI * row_bytes);
+        for (int s = 0; s < NI; ++s)
+          ch[s] = load_tile_chunk(rs, lane_off, (uint32_t)(s * RPI * row_bytes));
       };
-      const int nunits = nchunk * SUB;
+      // tiles of the chunk; in the run's last page only those holding a
+      // position below L (a tile past the history would add nothing)
+      int nunits = nchunk * SUB;
+      if (jc + nchunk == pc.n_b) {
+        const int last_pos = table_page(pc.n_b - 1) * BS;   // first position of the last page
+        nunits -= SUB - (L - last_pos + 15) / 16;
+      }
       for (int u = 0; u < nunits; ++u) {
         const int k = u / SUB, sb = u % SUB;
         const int tok0 = table_page(jc + k) * BS + sb * 16;   // position of the tile's first token
         const int live = L - tok0;                  // rows of the tile inside the history
         // the decode step's new token goes to row live - 1 of this tile
         const bool new_tile = new_here && k == k_last && live >= 1 && live <= 16;
+        if constexpr (S::Q8) {   // the tile's scales: scalar loads, then column n's head
+          const int phys = __builtin_amdgcn_readlane(phys_l, k);
+          const float* ks = p.k_scale + (int64_t)phys * Hkv + g0;
+          const float* vs = p.v_scale + (int64_t)phys * Hkv + g0;
+          ksc = ks[0];
+          vsc = vs[0];
+#pragma unroll
+          for (int j = 1; j < HG; ++j) {
+            const float kj = ks[j], vj = vs[j];
+            if (mem == j) {
+              ksc = kj;
+              vsc = vj;
+            }
+          }
+        }
         const int64_t base = tile_base(u);
         issue(kc, base, kb);
         if constexpr (S::KV_TOGETHER) issue(vc, base, vb);
         if (new_here && u == 0) {   // park the new rows while this tile's loads fly
           const int blk = __builtin_amdgcn_readlane(phys_l, k_last);
           const int off = (L - 1) % BS;
-          const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g * RB;
-          const int64_t sslot = (int64_t)blk * Hkv + g;
-          if constexpr (S::Q8) {
-            if (off != 0) {
-              new_ksc = p.k_scale[sslot];
-              new_vsc = p.v_scale[sslot];
-            }
-          }
-          park_new_rows<S>(new_part, lane, new_rows, p.k_cache_w + row, p.v_cache_w + row,
-                           off == 0, new_ksc, new_vsc, p.k_scale_w + sslot, p.v_scale_w + sslot);
-        }
-        if constexpr (S::Q8) {
-          const int phys = __builtin_amdgcn_readlane(phys_l, k);
-          ksc = p.k_scale[(int64_t)phys * Hkv + g];
-          vsc = p.v_scale[(int64_t)phys * Hkv + g];
+          const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g0 * RB;
+          const int64_t sslot = (int64_t)blk * Hkv + g0;
+          park_new_rows<S>(new_part, lane, mem, new_rows, p.k_cache_w + row, p.v_cache_w + row,
+                           off == 0, new_ksc, new_vsc, p.k_scale + sslot, p.v_scale + sslot,
+                           p.k_scale_w + sslot, p.v_scale_w + sslot);
         }
 
-        // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 heads)
+        // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 columns)
         stage_tile<S>(tile, kb, lane, live, false);
         if (new_tile) {
           take_new_row<S>(new_rows, tile, live - 1, lane);
@@ -426,11 +549,23 @@ void mfma_partition_kernel(const AttnParams p) {
           __builtin_amdgcn_sched_barrier(0);   // keep the V loads behind the K wait
           issue(vc, base, vb);
         }
-        float4_t s = {0.f, 0.f, 0.f, 0.f};
+        float4_t s;
+        {
+          float4_t sh[HG];   // one chain per kv head of the unit
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(tile + k_rd + 64 * kk);
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], s, 0, 0, 0);
+          for (int j = 0; j < HG; ++j) sh[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+            for (int j = 0; j < HG; ++j) {
+              const bf16x8_t a =
+                  *reinterpret_cast<const bf16x8_t*>(tile + k_rd + 2 * D * j + 64 * kk);
+              sh[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], sh[j], 0, 0, 0);
+            }
+          s = sh[0];
+#pragma unroll
+          for (int j = 1; j < HG; ++j)
+            if (mem == j) s = sh[j];
         }
         const float c = S::Q8 ? p.scale_log2 * ksc : p.scale_log2;
         // rows past a_rel are in column n's future (decode: past the history)
@@ -447,7 +582,7 @@ void mfma_partition_kernel(const AttnParams p) {
             if (4 * r + i < lo_rel && 4 * r + i >= sk_rel) s[i] = -INFINITY;
         }
 
-        // online softmax, one max per head (column n)
+        // online softmax, one max per column n
         float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         pm = fmaxf(pm, __shfl_xor(pm, 16));
         pm = fmaxf(pm, __shfl_xor(pm, 32));
@@ -456,35 +591,40 @@ void mfma_partition_kernel(const AttnParams p) {
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
           l_run *= alpha;
-          // O rows are heads 4r + i: fetch their factors from columns 4r + i
+          // O^T columns are this lane's column: its own factor
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = __shfl(alpha, 4 * r + i);
+          for (int nb = 0; nb < NBN; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < NBN; ++nb) O[nb][i] *= a;
-          }
+            for (int i = 0; i < 4; ++i) O[nb][i] *= alpha;
         }
-        short4_t pa;
+        // P^T as the B operand: lane (n, r) holds column n, tokens 4r..4r+3,
+        // the layout S^T came out in
+        short4_t pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pr = fast_exp2(s[i] - m_run);
           l_run += pr;
-          pa[i] = bf16_bits(S::Q8 ? pr * vsc : pr);
+          pb[i] = bf16_bits(S::Q8 ? pr * vsc : pr);
         }
 
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
-        // order within a wave) -> transposed B operands, O += P V
+        // order within a wave) -> transposed A operands, O^T += V^T P^T
         if (windowed)
           stage_tile<S>(tile, vb, lane, live, true, p.sinks - tok0, gap_end - tok0);
         else
           stage_tile<S>(tile, vb, lane, live, true);
-        if (new_tile) take_new_row<S>(new_rows + 2 * D, tile, live - 1, lane);
+        if (new_tile) take_new_row<S>(new_rows + 16 * CH, tile, live - 1, lane);
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb) {
-          // (C-style cast: generic -> LDS address space)
-          const short4_t vB =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(tile + v_rd + 32 * nb));
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vB, O[nb], 0, 0, 0);
+        for (int j = 0; j < HG; ++j) {
+          short4_t pj = pb;
+          if (HG > 1 && mem != j) pj = short4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb) {
+            // (C-style cast: generic -> LDS address space)
+            const short4_t vA = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_short4_t*)(tile + v_rd + 2 * D * j + 32 * nb));
+            O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pj, O[nb], 0, 0, 0);
+          }
         }
       }
     }
@@ -492,36 +632,28 @@ void mfma_partition_kernel(const AttnParams p) {
     // ---- finish the piece ---------------------------------------------------
     float l_tot = l_run;
     l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);            // head n's sum, in every row group
-    float l_row[4];                             // sums of the O rows 4r + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l_row[i] = __shfl(l_tot, 4 * r + i);
-    const int seg = b * Hkv + g;
+    l_tot += __shfl_xor(l_tot, 32);            // column n's sum, in every row group
+    const int seg = b * U + pc.u;
     if (pc.j0 == 0 && pc.j1 == pc.n_b) {
-      uint16_t* op = static_cast<uint16_t*>(p.out);
+      if (n < ncol) {
+        // (a query that sees no key gets 0)
+        const float inv = !GEN || l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t* orow =
+            static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + col_q) * p.Hq + col_h) * D + 4 * r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 4 * r + i;   // O row: query c / G, head c % G
-        if (c < ncol) {
-          // (a query that sees no key gets 0)
-          const float inv = !GEN || l_row[i] > 0.0f ? 1.0f / l_row[i] : 0.0f;
-          uint16_t* orow = op + ((int64_t)(r0 + c / G) * p.Hq + g * G + c % G) * D + n;
-#pragma unroll
-          for (int nb = 0; nb < NBN; ++nb)
-            orow[16 * nb] = (uint16_t)f32_to_bf16_rne(O[nb][i] * inv);
-        }
+        for (int nb = 0; nb < NBN; ++nb)
+          *reinterpret_cast<uint2*>(orow + 16 * nb) =
+              make_uint2(pack_bf16x2(O[nb][0] * inv, O[nb][1] * inv),
+                         pack_bf16x2(O[nb][2] * inv, O[nb][3] * inv));
       }
     } else {
       const int64_t row = (int64_t)piece + seg;
       const int C = p.cols;
+      if (n < ncol) {
+        float* orow = p.ws_o + (row * C + n) * D + 4 * r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 4 * r + i;
-        if (c < ncol) {
-          float* orow = p.ws_o + (row * C + c) * D + n;
-#pragma unroll
-          for (int nb = 0; nb < NBN; ++nb) orow[16 * nb] = O[nb][i];
-        }
+        for (int nb = 0; nb < NBN; ++nb)
+          *reinterpret_cast<float4*>(orow + 16 * nb) = make_float4(O[nb][0], O[nb][1], O[nb][2], O[nb][3]);
       }
       if (lane < ncol)
         *reinterpret_cast<float2*>(p.ws_ml + (row * C + lane) * 2) = make_float2(m_run, l_tot);
@@ -531,44 +663,92 @@ void mfma_partition_kernel(const AttnParams p) {
   });
 }
 
+// Calls f(MfmaShape<D, BS, G, kind, hg>{}) for the combination given at run
+// time: hg = 1, or hg = kUnitHeads(G) (the decode instantiations only).
+// Two heads per wave measured best on every decode workload (B64 / B4 /
+// B256 / B128 bf16, fp8 and int8 shapes): 2-4% faster steps than one head
+// (fp8: 6%), while four heads lost on bf16 D = 128 G = 4 (3% slower steps:
+// the wider partial rows and the 2-waves-per-SIMD grid cost more than the
+// 1 KB runs gain).
+constexpr int kUnitHeads(int G) { return G <= 8 ? 2 : 1; }
+
+template <int D_, int BS_, int G_, int K_>
+struct ShapeKey {
+  static constexpr int D = D_, BS = BS_, G = G_, K = K_;
+};
+
+template <class F>
+bool dispatch_mfma(int D, int BS, int G, int kind, int hg, F&& f) {
+  bool ok = false;
+  dispatch_shapes<ShapeKey>(D, BS, G, kind, [&](auto key) {
+    using Kt = decltype(key);
+    constexpr int H = kUnitHeads(Kt::G);
+    if (hg == 1) {
+      f(MfmaShape<Kt::D, Kt::BS, Kt::G, Kt::K, 1>{});
+      ok = true;
+    } else if (hg == H) {
+      f(MfmaShape<Kt::D, Kt::BS, Kt::G, Kt::K, H>{});
+      ok = true;
+    }
+  });
+  return ok;
+}
+
 }  // namespace
 
-size_t mfma_stage_lds_bytes(int D) {
-  return (size_t)kAttnWavesPerBlock * (16 * (2 * D + 32) + 4 * D);
+int mfma_unit_heads(int G) { return kUnitHeads(G); }
+
+size_t mfma_stage_lds_bytes(int D, int hg) {
+  return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + 4 * hg * D);
 }
 
-static size_t mfma_lds_total(int B, int D) {
-  return ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D);
+// Units of several kv heads run at two workgroups (8 waves) per CU: each
+// workgroup reserves at least this much LDS, so a third one never fits
+// (three waves per SIMD measured slower for them: see MfmaShape::WPE).
+constexpr size_t kUnitLdsFloor = 56 * 1024;
+
+static size_t mfma_lds_total(int B, int D, int hg) {
+  const size_t t = ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg);
+  return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
 
-// Occupancy of the decode instantiation; the generalised one is held to the
+// hg = 1: the decode and the generalised instantiations are held to the
 // same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves both.
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B) {
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg) {
   int blocks = 0, blocks_gen = 0;
-  const size_t lds = mfma_lds_total(B, D);
-  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, kind, [&](auto s) {
+  const size_t lds = mfma_lds_total(B, D, hg);
+  const bool ok = dispatch_mfma(D, BS, G, kind, hg, [&](auto s) {
     using S = decltype(s);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S, false>,
-                                                     kAttnBlockThreads, lds) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
                                                      kAttnBlockThreads, lds) != hipSuccess)
-      blocks = blocks_gen = 0;
+      blocks = 0;
+    blocks_gen = blocks;
+    if constexpr (S::HG == 1) {
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
+                                                       kAttnBlockThreads, lds) != hipSuccess)
+        blocks_gen = 0;
+    }
   });
   return ok ? (blocks < blocks_gen ? blocks : blocks_gen) : 0;
 }
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
-  const size_t lds = mfma_lds_total(p.B, D);
+  const size_t lds = mfma_lds_total(p.B, D, p.hg);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
-  const bool ok = dispatch_shapes<MfmaShape>(D, BS, G, kind, [&](auto s) {
+  if (gen && p.hg != 1) return hipErrorInvalidValue;
+  if (p.hg < 1 || p.Hkv % p.hg != 0) return hipErrorInvalidValue;
+  const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);
-    if (gen)
-      hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks), dim3(kAttnBlockThreads),
-                         lds, stream, p);
-    else
-      hipLaunchKernelGGL((mfma_partition_kernel<S, false>), dim3(blocks), dim3(kAttnBlockThreads),
-                         lds, stream, p);
+    if constexpr (S::HG == 1) {
+      if (gen) {
+        hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks),
+                           dim3(kAttnBlockThreads), lds, stream, p);
+        return;
+      }
+    }
+    hipLaunchKernelGGL((mfma_partition_kernel<S, false>), dim3(blocks), dim3(kAttnBlockThreads),
+                       lds, stream, p);
   });
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

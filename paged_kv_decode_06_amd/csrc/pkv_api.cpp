@@ -60,10 +60,12 @@ int cu_count(int dev) {
 }
 
 // LDS of the partition kernel grows with B; occupancy is looked up for B
-// rounded up to a multiple of 1024 so that the cache stays small.
-int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B) {
+// rounded up to a multiple of 1024 so that the cache stays small.  hg: kv
+// heads per wave (MFMA only).
+int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)dev << 40) | ((unsigned long long)path << 36) |
+  const unsigned long long key = ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
+                                 ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
                                  ((unsigned long long)G << 16) | ((unsigned long long)kind << 12) |
                                  (unsigned long long)(Bq / 1024);
@@ -73,7 +75,7 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, i
     auto it = c.blocks.find(key);
     if (it != c.blocks.end()) return it->second;
   }
-  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq)
+  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg)
                                              : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
@@ -87,12 +89,35 @@ bool supported(int D, int BS, int G, int kv_dtype) {
 }
 
 // Persistent grid: every workgroup that fits at once on every CU.
-int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B) {
+int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B, int hg) {
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
-  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B);
+  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg);
   return ncu * per_cu;
+}
+
+// Largest unit (kv heads per partition wave) the decode-shaped calls may
+// use: 0 = the kernel's own (pkv::mfma_unit_heads), 1 = one kv head.
+std::atomic<int>& unit_heads_flag() {
+  static std::atomic<int> flag([] {
+    const char* e = std::getenv("PKV_UNIT_HEADS");
+    return (e && std::string(e) == "1") ? 1 : 0;
+  }());
+  return flag;
+}
+
+// A wave of the MFMA kernel serves hg adjacent kv heads when the call is
+// decode-shaped (one query per sequence, no window), hg divides Hkv and the
+// wider instantiation still fits two workgroups on a CU; otherwise one.
+int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, int B, bool gen) {
+  if (path != pkv::AttnPath::kMfma || gen || unit_heads_flag().load(std::memory_order_relaxed) == 1)
+    return 1;
+  const int hg = pkv::mfma_unit_heads(G);
+  if (hg <= 1 || Hkv % hg != 0) return 1;
+  int dev;
+  if (current_device(&dev) != 0) return 1;
+  return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg) >= 2 ? hg : 1;
 }
 
 struct AttnCall {
@@ -164,11 +189,13 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (q8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
   const pkv::AttnPath path = path_for(opts);
-  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B);
+  const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
+  const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen);
+  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
-  const int cols = G * opts.max_q;
-  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv, cols, D, waves);
+  const int cols = hg * G * opts.max_q;
+  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv / hg, cols, D, waves);
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, lay.total);
@@ -194,6 +221,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.cols = cols;
   p.sinks = opts.sinks;
   p.window = opts.window;
+  p.hg = hg;
   p.total_waves = waves;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
@@ -259,9 +287,26 @@ int pkv_select_partition_kernel(int variant) {
 
 int pkv_partition_kernel(void) { return (int)pkv::attn_path(); }
 
-int pkv_attention_waves(int D, int BS, int G, int kv_dtype) {
+int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
+  if (B < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || B > pkv::kMaxBatch) return 0;
+  const int G = Hq / Hkv;
   if (!supported(D, BS, G, kv_dtype)) return 0;
-  return attention_blocks(pkv::attn_path(), D, BS, G, kv_dtype, 1) * pkv::kAttnWavesPerBlock;
+  const pkv::AttnPath path = pkv::attn_path();
+  const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, false);
+  return attention_blocks(path, D, BS, G, kv_dtype, B, hg) * pkv::kAttnWavesPerBlock;
+}
+
+int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
+  if (B < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || B > pkv::kMaxBatch) return 0;
+  const int G = Hq / Hkv;
+  if (!supported(D, BS, G, kv_dtype)) return 0;
+  return unit_heads(pkv::attn_path(), D, BS, G, Hkv, kv_dtype, B, false);
+}
+
+int pkv_select_unit_heads(int mode) {
+  if (mode != 0 && mode != 1) return fail(PKV_ERR_UNSUPPORTED, "unit-heads mode %d is not 0 or 1", mode);
+  unit_heads_flag().store(mode, std::memory_order_relaxed);
+  return PKV_OK;
 }
 
 }  // extern "C"
@@ -274,10 +319,20 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
   if (!supported(D, BS, G, kv_dtype) || B > pkv::kMaxBatch || G * max_q > kMaxCols) return 0;
   QueryOpts o;
   o.general = general;
-  const int blocks = attention_blocks(path_for(o), D, BS, G, kv_dtype, B);
-  if (blocks <= 0) return 0;
-  const int waves = blocks * pkv::kAttnWavesPerBlock;
-  return pkv::workspace_layout(B, Hkv, G * max_q, D, waves).total;
+  const pkv::AttnPath path = path_for(o);
+  // the general call is decode-shaped or not depending on q_start and the
+  // window: size for both unit choices
+  size_t need = 0;
+  for (int gen = general ? 1 : 0; gen >= 0; --gen) {
+    if (gen == 0 && max_q > 1) continue;
+    const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0);
+    const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
+    if (blocks <= 0) return 0;
+    const int waves = blocks * pkv::kAttnWavesPerBlock;
+    const size_t t = pkv::workspace_layout(B, Hkv / hg, hg * G * max_q, D, waves).total;
+    if (t > need) need = t;
+  }
+  return need;
 }
 }  // namespace
 

@@ -27,12 +27,17 @@ struct AttnParams {
   int B, Hq, Hkv, NB, MBS;
   // Query tokens (bottom-right causal, see decode_common.hpp): sequence b
   // owns q/out rows q_start[b] .. q_start[b+1]-1 (q_start NULL: row b only);
-  // at most max_q of them, G * max_q <= 16.  cols = G * max_q columns per
-  // share row.  window > 0 hides keys more than window - 1 positions behind a
+  // at most max_q of them, G * max_q <= 16.  cols = hg * G * max_q columns
+  // per share row.  window > 0 hides keys more than window - 1 positions behind a
   // query except the first `sinks` positions.
   const int32_t* q_start;
   int max_q, cols;
   int sinks, window;
+  // kv heads one partition wave serves together (a unit of adjacent kv
+  // heads): the work axis runs over (sequence, unit, page), U = Hkv / hg
+  // units per sequence.  Above 1 only for one query per sequence and no
+  // window (then cols = hg * G); the VALU kernel always takes 1.
+  int hg;
   int total_waves;      // persistent waves of the partition grid
   // workspace (see workspace_layout)
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
@@ -63,11 +68,12 @@ struct WorkspaceLayout {
 #endif
 constexpr int kPiecesPerWave = PKV_PIECES_PER_WAVE;
 
-// `cols` = G * (query tokens per sequence, at most).
-inline WorkspaceLayout workspace_layout(int B, int Hkv, int cols, int D, int total_waves) {
+// `U` = units per sequence (Hkv / hg), `cols` = hg * G * (query tokens per
+// sequence, at most).
+inline WorkspaceLayout workspace_layout(int B, int U, int cols, int D, int total_waves) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
-  w.rows = kPiecesPerWave * total_waves + B * Hkv;
+  w.rows = kPiecesPerWave * total_waves + B * U;
   w.pre_off = 0;
   w.ml_off = w.pre_off + up(sizeof(int32_t) * (size_t)(B + 1));
   w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * cols);
@@ -92,11 +98,16 @@ hipError_t launch_partition_valu(const AttnParams& p, int D, int BS, int G, int 
                                  hipStream_t stream);
 int valu_blocks_per_cu(int D, int BS, int G, int kind, int B);
 // (the VALU variant handles one query per sequence and no window only)
+// (the MFMA launch takes the unit size from p.hg)
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream);
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B);
+// hg = 1: the occupancy both instantiations (decode and generalised) reach;
+// hg > 1: that of the decode instantiation with hg kv heads per wave (0 if
+// there is none: mfma_unit_heads(G) is the one hg above 1 that exists).
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg);
+int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
-size_t mfma_stage_lds_bytes(int D);
+size_t mfma_stage_lds_bytes(int D, int hg);
 
 // Variant used by the attention calls: MFMA unless PKV_ATTN_KERNEL=valu is
 // set when the library loads, or pkv_select_partition_kernel changes it.

@@ -78,8 +78,12 @@ def _load():
         lib.pkv_status_string.restype = ctypes.c_char_p
         lib.pkv_last_error.argtypes = []
         lib.pkv_last_error.restype = ctypes.c_char_p
-        lib.pkv_attention_waves.argtypes = [I, I, I, I]
+        lib.pkv_attention_waves.argtypes = [I, I, I, I, I, I]
         lib.pkv_attention_waves.restype = I
+        lib.pkv_decode_unit_heads.argtypes = [I, I, I, I, I, I]
+        lib.pkv_decode_unit_heads.restype = I
+        lib.pkv_select_unit_heads.argtypes = [I]
+        lib.pkv_select_unit_heads.restype = I
         lib.pkv_select_partition_kernel.argtypes = [I]
         lib.pkv_select_partition_kernel.restype = I
         lib.pkv_partition_kernel.argtypes = []
@@ -206,6 +210,28 @@ def select_partition_kernel(variant: int) -> None:
 
 def partition_kernel() -> int:
     return int(_load().pkv_partition_kernel())
+
+
+UNITS_AUTO = 0
+UNITS_ONE_HEAD = 1
+
+
+def select_unit_heads(mode: int) -> None:
+    """pkv_select_unit_heads: 0 = several kv heads per MFMA wave where the
+    call allows it, 1 = one kv head per wave (process-wide; resize
+    workspaces afterwards)."""
+    _check("pkv_select_unit_heads", _load().pkv_select_unit_heads(int(mode)))
+
+
+def decode_unit_heads(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:
+    """Kv heads per partition wave a decode call with these sizes uses
+    (kv_dtype: KV_BF16, KV_FP8 or KV_INT8)."""
+    return int(_load().pkv_decode_unit_heads(B, Hq, Hkv, D, BS, int(kv_dtype)))
+
+
+def attention_waves(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:
+    """Persistent waves of a decode call's partition grid with these sizes."""
+    return int(_load().pkv_attention_waves(B, Hq, Hkv, D, BS, int(kv_dtype)))
 
 
 def workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:

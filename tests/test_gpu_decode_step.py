@@ -18,17 +18,16 @@ import torch
 from paged_kv_decode_06_amd import ops
 from paged_kv_decode_06_amd import workloads as W
 from tests import gpu_support as GS
-from tests.test_gpu_parity import DEV, KERNELS, SMALL, build, say
+from tests.test_gpu_parity import DEV, KERNELS, SMALL, build, default_kernel, say, use_kernel
 
 pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(params=list(KERNELS))
 def kernel(request):
-    ops.select_partition_kernel(KERNELS[request.param])
-    say(f"partition kernel: {request.param}")
+    use_kernel(request.param)
     yield request.param
-    ops.select_partition_kernel(ops.PARTITION_MFMA)
+    default_kernel()
 
 
 def derived_slots(wl: W.Workload) -> np.ndarray:
@@ -90,7 +89,7 @@ def test_step_equals_two_calls_every_variant(kernel):
     others put it mid-block and on the last offset of a block."""
     for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
                                           ("bf16", "fp8", "int8")):
-        Hkv = 2
+        Hkv = 4
         wl = build(5, Hkv * G, Hkv, D, BS, (1, BS + 1, 2 * BS, 9 * BS + 5, 3 * BS - 1), kv=kv,
                    seed=D + BS + G + 7)
         assert_same_as_two_calls(wl, f"D{D} BS{BS} G{G} {kv}")

@@ -27,16 +27,31 @@ def say(*a):
     print(*a, flush=True)
 
 
-KERNELS = {"mfma": ops.PARTITION_MFMA, "valu": ops.PARTITION_VALU}
+# partition-kernel variant and unit mode: "mfma" serves several kv heads per
+# wave where the call allows it (the default), "mfma1" one kv head per wave
+KERNELS = {"mfma": (ops.PARTITION_MFMA, ops.UNITS_AUTO),
+           "mfma1": (ops.PARTITION_MFMA, ops.UNITS_ONE_HEAD),
+           "valu": (ops.PARTITION_VALU, ops.UNITS_AUTO)}
+
+
+def use_kernel(name: str) -> None:
+    variant, units = KERNELS[name]
+    ops.select_partition_kernel(variant)
+    ops.select_unit_heads(units)
+    say(f"partition kernel: {name}")
+
+
+def default_kernel() -> None:
+    ops.select_partition_kernel(ops.PARTITION_MFMA)
+    ops.select_unit_heads(ops.UNITS_AUTO)
 
 
 @pytest.fixture(params=list(KERNELS))
 def kernel(request):
-    """Run the test with each partition-kernel variant (the default, MFMA, last)."""
-    ops.select_partition_kernel(KERNELS[request.param])
-    say(f"partition kernel: {request.param}")
+    """Run the test with each partition-kernel variant (the default last)."""
+    use_kernel(request.param)
     yield request.param
-    ops.select_partition_kernel(ops.PARTITION_MFMA)
+    default_kernel()
 
 
 def build(B, Hq, Hkv, D, BS, lengths, kv="bf16", seed=0, poison=True, NB=None, scale=None):
@@ -101,10 +116,11 @@ def test_step_matches_oracle_small(shape, kernel):
 
 
 def test_all_supported_variants_run(kernel):
-    """Every (D, BS, G, dtype) instantiation against the oracle."""
+    """Every (D, BS, G, dtype) instantiation against the oracle (Hkv = 4: the
+    decode call serves 2 kv heads per wave, or one with "mfma1")."""
     for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
                                           ("bf16", "fp8", "int8")):
-        Hkv = 2
+        Hkv = 4
         wl = build(3, Hkv * G, Hkv, D, BS, (1, BS + 3, 9 * BS + 5), kv=kv, seed=D + BS + G)
         check_step(wl, f"D{D} BS{BS} G{G} {kv}")
 
