@@ -146,6 +146,23 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{len(times)} run(s), mean {t:.3f} s per step"}
 
 
+def settle(runs, seconds: float) -> int:
+    """Keep the GPU busy with the workload's own steps for `seconds` of wall
+    time before the warmup steps: clocks ramp under load, and a timed region
+    started from idle read up to 3% slow for its first tens of milliseconds
+    (the first of two step kinds timed back to back was the one to suffer).
+    Returns the steps run; none of them is timed."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            for run in runs:
+                run(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def general_result(args, cfg, wl, dev, nbytes):
     """Several query tokens per sequence and/or a sliding window: a step is
     the append of every new token (kv_append, in position order) followed by
@@ -189,6 +206,7 @@ def general_result(args, cfg, wl, dev, nbytes):
         att()
 
     with torch.cuda.stream(stream):
+        settled = settle([run], args.settle)
         for i in range(Wm):
             run(i)
         torch.cuda.synchronize()
@@ -232,6 +250,7 @@ def general_result(args, cfg, wl, dev, nbytes):
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
             "attention_call_us_mean": round(att_ms * 1e3, 2),
             "query_rows_heads_per_s": round(int(wl.q_start_np[-1]) * wl.Hq / (ms_per_step * 1e-3), 1),
+            "settle_steps_untimed": settled,
         },
     }
     return result
@@ -242,6 +261,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warmup (clock settling)")
     ap.add_argument("--config", default="llama3_8b")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies cycled (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -324,6 +345,7 @@ def main():
     K, Wm = args.steps, args.warmup
     main_run, other_run = (run_fused, run_split) if args.step == "fused" else (run_split, run_fused)
     with torch.cuda.stream(stream):
+        settled = settle([main_run, other_run], args.settle)
         for i in range(Wm):
             other_run(i)
         for i in range(Wm):
@@ -448,6 +470,7 @@ def main():
             "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
             "rope_kv_append_us_mean": round(rope_us, 2),
             "persistent_waves": waves,
+            "settle_steps_untimed": settled,
             "kv_heads_per_wave": unit_heads,
         },
     }
