@@ -477,13 +477,14 @@ void mfma_partition_kernel(const AttnParams p) {
       const bool new_here = has_new && k_last < nchunk && ((valid >> k_last) & 1);
       uint4 kb[NI], vb[NI];
       float ksc = 1.0f, vsc = 1.0f;
-      // one unit = one 16-token tile: page k of the chunk, tile sb.  Bytes
-      // in flight per wave: a 4 KB half tile (bf16, D = 128) is enough on
-      // its own, so its V loads are issued only once the K loads have
-      // landed (issuing both at once measured ~7% slower); 2 KB halves
-      // (fp8 / int8, or D = 64) issue K and V together (~3% faster than in turn).
-      // The other waves of the CU overlap their compute with the waits;
-      // issuing the next tile early does not pay for the registers it costs.
+      // u indexes the chunk's 16-token tiles: page k of the chunk, tile sb.
+      // Bytes in flight per wave: a half tile of 4 KB or more (bf16, D =
+      // 128) is enough on its own, so its V loads are issued only once the K
+      // loads have landed (issuing both at once measured ~7% slower with one
+      // head per wave, 2-3% with two); 2 KB halves (one head, fp8 / int8 or
+      // D = 64) issue K and V together (~3% faster than in turn).  The other
+      // waves of the CU overlap their compute with the waits; issuing the
+      // next tile's K early measured 3-7% slower.
       auto tile_base = [&](int u) {   // (wave-uniform)
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
@@ -531,9 +532,12 @@ void mfma_partition_kernel(const AttnParams p) {
           const int off = (L - 1) % BS;
           const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g0 * RB;
           const int64_t sslot = (int64_t)blk * Hkv + g0;
+          // (bf16 caches have no scales: null pointers then)
           park_new_rows<S>(new_part, lane, mem, new_rows, p.k_cache_w + row, p.v_cache_w + row,
-                           off == 0, new_ksc, new_vsc, p.k_scale + sslot, p.v_scale + sslot,
-                           p.k_scale_w + sslot, p.v_scale_w + sslot);
+                           off == 0, new_ksc, new_vsc, S::Q8 ? p.k_scale + sslot : nullptr,
+                           S::Q8 ? p.v_scale + sslot : nullptr,
+                           S::Q8 ? p.k_scale_w + sslot : nullptr,
+                           S::Q8 ? p.v_scale_w + sslot : nullptr);
         }
 
         // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 columns)

@@ -259,6 +259,25 @@ def test_many_rows_small_lengths(kernel):
     check_step(wl, "B64 Hq16")
 
 
+@pytest.mark.parametrize("D,kv", [(64, "bf16"), (128, "fp8")])
+def test_largest_batch(D, kv, kernel):
+    """B = 8192 (the largest batch: the sequence prefix sums fill their LDS),
+    lengths 1..40, so every thread of the prefix scan sums 32 sequences and
+    most runs are finished in place; then every 7th sequence emptied (L = 0:
+    no pages, output 0) and the rest still within the bar of the oracle."""
+    L = np.random.default_rng(23).integers(1, 41, 8192)
+    L[:4] = (1, 16, 17, 40)
+    wl = build(8192, 4, 2, D, 16, L, kv=kv, seed=23, poison=True)
+    _, ref = check_step(wl, f"B8192 D{D} {kv}")
+    wl.context_lens[::7] = 0
+    out0 = GS.gpu_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert (out0[::7] == 0).all()
+    keep = np.ones(8192, dtype=bool)
+    keep[::7] = False
+    GS.assert_attention_close(GS.bf16_to_f64(out0)[keep], ref[keep], wl.kv_dtype, "emptied")
+
+
 def test_edge_cases_empty_full_and_skipped():
     """B = 0 and N = 0 do nothing; a sequence that fills its block table
     exactly (L = MBS * BS); a negative slot writes nothing."""
