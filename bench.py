@@ -310,7 +310,10 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": ops.KV_INT8}[wl.kv_dtype]
-    ws = torch.zeros(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
+    # (also large enough for the RoPE step, which always runs the MFMA kernel)
+    ws = torch.zeros(max(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
+                         ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS,
+                                                       kvd, 1)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(wl.q)
     caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
@@ -423,6 +426,32 @@ def main():
     torch.cuda.synchronize()
     rope_us = r0.elapsed_time(r1) * 1e3 / 50
 
+    # The decode step with RoPE: one call (rotation inside the partition
+    # kernel) against RoPE append + attention, K steps each, wall clock.
+    rope_fused = [ops.PreparedStep(wl.q, wl.k_new, wl.v_new, kc_, vc_, wl.block_tables,
+                                   wl.context_lens, wl.scale, out, ks_, vs_, ws, stream=stream,
+                                   rope={})
+                  for kc_, vc_, ks_, vs_ in caches]
+    rope_att = [ops.PreparedAttention(q_rot, kc_, vc_, wl.block_tables, wl.context_lens,
+                                      wl.scale, out, ks_, vs_, ws, stream=stream)
+                for kc_, vc_, ks_, vs_ in caches]
+
+    def run_rope_fused(i):
+        rope_fused[i % copies]()
+
+    def run_rope_split(i):
+        kc_, vc_, ks_, vs_ = caches[i % copies]
+        ops.rope_kv_append(wl.q, wl.k_new, wl.v_new, pos, wl.slot_mapping, kc_, vc_, ks_, vs_,
+                           q_out=q_rot, stream=stream)
+        rope_att[i % copies]()
+
+    with torch.cuda.stream(stream):
+        for i in range(Wm):
+            run_rope_fused(i)
+            run_rope_split(i)
+        rope_step_ms = timed(run_rope_fused, Wm)
+        rope_split_ms = timed(run_rope_split, Wm)
+
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (part_avg_ms * 1e-3) / 1e9
     waves = ops.attention_waves(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, kvd)
@@ -469,6 +498,8 @@ def main():
                 round(ms_per_step_other, 5),
             "seq_heads_per_s": round(wl.B * wl.Hq / (ms_per_step * 1e-3), 1),
             "rope_kv_append_us_mean": round(rope_us, 2),
+            "decode_step_rope_us": round(rope_step_ms * 1e3, 2),
+            "rope_append_then_attention_us": round(rope_split_ms * 1e3, 2),
             "persistent_waves": waves,
             "settle_steps_untimed": settled,
             "kv_heads_per_wave": unit_heads,

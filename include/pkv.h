@@ -223,6 +223,26 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* The decode step with RoPE ("tiny-vllm part 5", the RoPE section, with the
+ * frequencies and parameters of pkv_rope_kv_append): q and k_new arrive
+ * unrotated; exactly equivalent to
+ *   pkv_rope_kv_append(q, q_rot, k_new, v_new, pos, slot, ...);
+ *   pkv_paged_decode_attention(q_rot, ...);
+ * with pos[b] = context_lens[b] - 1 and slot[b] as for pkv_decode_step:
+ * caches, scales and out bit-identical to those two calls (q itself is not
+ * changed).  Always runs the MFMA partition kernel, which rotates q in
+ * registers and the new key rows before it stores them, so the step is two
+ * launches; size the workspace with pkv_paged_attention_workspace_bytes
+ * (max_q_len = 1).  D in {64, 128}; other arguments as for pkv_decode_step.
+ * Bad rope parameters give PKV_ERR_SHAPE.  B == 0 is a no-op. */
+int pkv_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         double rope_theta, double rope_factor, double low_freq_factor,
+                         double high_freq_factor, double original_max_len, void* out, int B,
+                         int Hq, int Hkv, int D, int BS, int NB, int MBS, int kv_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* The first half of pkv_decode_step (the append and the partition kernel),
  * same arguments; following it with pkv_paged_decode_merge on the same
  * stream and workspace is exactly pkv_decode_step.  Exposed so that the

@@ -27,6 +27,7 @@ from .ops import (  # noqa: F401
     KV_FP8,
     PkvError,
     decode_step,
+    decode_step_rope,
     kv_append,
     rope_kv_append,
     paged_attention,

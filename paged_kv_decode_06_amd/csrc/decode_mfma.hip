@@ -338,9 +338,59 @@ __device__ __forceinline__ void take_new_row(const unsigned char* row, unsigned 
         *reinterpret_cast<const uint4*>(row + 16 * lane);
 }
 
+// RoPE inside the decode step: rotate the columns' q (the B operands) and,
+// when this piece appends, the unit's new K rows, at position `pos`.  Lane
+// j < D / 2 computes the cosine and sine of pair j's angle (pos * f_j, one
+// rounded fp64 product; rope_sincos) into the wave's tile buffer, which is free until the
+// first tile is staged (LDS accesses of a wave run in order); each lane then
+// rotates its pairs with the fp64 arithmetic of the RoPE append kernel, so
+// the rotated values are bit for bit those of that kernel.  The q lane (n, r)
+// holds dims 32 kk + 8 r .. + 7, pairs 16 kk + 4 r + t; a K chunk c of a
+// head row holds dims 8 c .. 8 c + 7, pairs 4 c + t.
+template <class S>
+__device__ __forceinline__ void rope_rotate(const AttnParams& p, int pos, int lane, int r,
+                                            unsigned char* scratch, bf16x8_t (&qB)[S::NKK],
+                                            uint4 (&new_part)[NewRows<S>::NP], bool has_new) {
+  constexpr int HP = S::D / 2, CH = NewRows<S>::CH, CPH = S::D / 8;
+  double2* cs = reinterpret_cast<double2*>(scratch);
+  if (lane < HP) {
+    double sn, c;
+    rope_sincos(__dmul_rn((double)pos, p.rope_freq[lane]), &sn, &c);
+    cs[lane] = make_double2(c, sn);
+  }
+#pragma unroll
+  for (int kk = 0; kk < S::NKK; ++kk) {
+    uint4 w = __builtin_bit_cast(uint4, qB[kk]);
+    uint32_t* e = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const double2 a = cs[16 * kk + 4 * r + t];
+      e[t] = rotate_pair(e[t], a.x, a.y);
+    }
+    qB[kk] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  if (has_new) {
+#pragma unroll
+    for (int i = 0; i < NewRows<S>::NP; ++i) {
+      const int q = lane + kWave * i;
+      if (q < CH) {   // a K chunk
+        const int c = q % CPH;
+        uint32_t* e = reinterpret_cast<uint32_t*>(&new_part[i]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const double2 a = cs[4 * c + t];
+          e[t] = rotate_pair(e[t], a.x, a.y);
+        }
+      }
+    }
+  }
+}
+
 // GEN: the generalised call (several queries per sequence, a window); the
 // decode instantiations (GEN = false) carry none of its per-lane state and
-// may serve several kv heads per wave (S::HG).
+// may serve several kv heads per wave (S::HG).  ROPE: the decode step with
+// RoPE (instantiated apart, so that the other kernels do not carry its
+// registers).
 //
 // Units of HG > 1 kv heads: the unit's HG * G query heads are the 16
 // columns, column n reading kv head `mem` = n / G of the unit.  The scores
@@ -348,7 +398,7 @@ __device__ __forceinline__ void take_new_row(const unsigned char* row, unsigned 
 // column's q) and each column keeps its own head's chain; the output runs
 // O^T += V_j^T P_j^T per head j with P_j = P restricted to head j's columns,
 // so every column sums only its own head's values.
-template <class S, bool GEN>
+template <class S, bool GEN, bool ROPE = false>
 __global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(S::WPE, S::WPE)))
 void mfma_partition_kernel(const AttnParams p) {
   constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB, HG = S::HG, UG = S::UG;
@@ -356,6 +406,7 @@ void mfma_partition_kernel(const AttnParams p) {
   constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
   constexpr int NP = NewRows<S>::NP, CH = NewRows<S>::CH;
   static_assert(!GEN || HG == 1, "the generalised call serves one kv head per wave");
+  static_assert(!(GEN && ROPE), "RoPE is fused into the decode step only");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
@@ -455,6 +506,9 @@ void mfma_partition_kernel(const AttnParams p) {
                                : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (q - CH));
       }
     }
+    // (placed here, before the run's first page-table load: inside the
+    // chunk or tile loop it raised the loop's registers and measured slower)
+    if constexpr (ROPE) rope_rotate<S>(p, L_in - 1, lane, r, tile, qB, new_part, has_new);
     float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: head mem's last-block scales after the append
 
     float4_t O[NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
@@ -473,6 +527,7 @@ void mfma_partition_kernel(const AttnParams p) {
         phys_l = valid_l ? v : 0;
       }
       const uint64_t valid = __builtin_amdgcn_ballot_w64(valid_l);   // pages with a real block id
+
       const int k_last = pc.n_b - 1 - jc;             // the run's last page in this chunk, if < nchunk
       const bool new_here = has_new && k_last < nchunk && ((valid >> k_last) & 1);
       uint4 kb[NI], vb[NI];
@@ -740,7 +795,7 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
                                  hipStream_t stream) {
   const size_t lds = mfma_lds_total(p.B, D, p.hg);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
-  if (gen && p.hg != 1) return hipErrorInvalidValue;
+  if (gen && (p.hg != 1 || p.rope)) return hipErrorInvalidValue;
   if (p.hg < 1 || p.Hkv % p.hg != 0) return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);
@@ -751,8 +806,12 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
         return;
       }
     }
-    hipLaunchKernelGGL((mfma_partition_kernel<S, false>), dim3(blocks), dim3(kAttnBlockThreads),
-                       lds, stream, p);
+    if (p.rope)
+      hipLaunchKernelGGL((mfma_partition_kernel<S, false, true>), dim3(blocks),
+                         dim3(kAttnBlockThreads), lds, stream, p);
+    else
+      hipLaunchKernelGGL((mfma_partition_kernel<S, false>), dim3(blocks),
+                         dim3(kAttnBlockThreads), lds, stream, p);
   });
   if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();

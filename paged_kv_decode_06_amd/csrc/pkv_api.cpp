@@ -233,6 +233,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.v_cache_w = nullptr;
   p.k_scale_w = nullptr;
   p.v_scale_w = nullptr;
+  p.rope = 0;
   call->path = path;
   call->D = D;
   call->BS = BS;
@@ -432,21 +433,30 @@ namespace {
 
 // The decode step's launches: the first half (append + partition) and, when
 // `merge`, the log-sum-exp merge.
+// rope != NULL: the decode step with RoPE of q and the new keys inside the
+// partition kernel (always the MFMA kernel).
 int decode_step_impl(const void* q, const void* k_new, const void* v_new, void* k_cache,
                      void* v_cache, float* k_scale, float* v_scale, const int32_t* block_tables,
                      const int32_t* context_lens, float scale, void* out, int B, int Hq, int Hkv,
                      int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
-                     size_t workspace_bytes, void* stream, bool merge) {
+                     size_t workspace_bytes, void* stream, bool merge,
+                     const pkv::RopeParams* rope = nullptr) {
   AttnCall call;
+  QueryOpts opts;
+  opts.general = rope != nullptr;
   int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
                              scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
-                             workspace_bytes, &call, true, k_new, v_new);
+                             workspace_bytes, &call, true, k_new, v_new, opts);
   if (st != PKV_OK) return st;
   if (B == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (call.path == pkv::AttnPath::kMfma) {
     pkv::AttnParams& p = call.p;
+    if (rope) {
+      p.rope = 1;
+      for (int i = 0; i < 64; ++i) p.rope_freq[i] = rope->freq[i];
+    }
     p.k_new = static_cast<const uint16_t*>(k_new);
     p.v_new = static_cast<const uint16_t*>(v_new);
     p.k_cache_w = static_cast<unsigned char*>(k_cache);
@@ -490,6 +500,27 @@ int pkv_decode_step_partition(const void* q, const void* k_new, const void* v_ne
   return decode_step_impl(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
                           context_lens, scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype,
                           workspace, workspace_bytes, stream, false);
+}
+
+int pkv_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, float* k_scale, float* v_scale,
+                         const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         double rope_theta, double rope_factor, double low_freq_factor,
+                         double high_freq_factor, double original_max_len, void* out, int B,
+                         int Hq, int Hkv, int D, int BS, int NB, int MBS, int kv_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!(rope_theta > 1.0) || !(rope_factor > 0.0) || !(low_freq_factor > 0.0) ||
+      !(high_freq_factor > low_freq_factor) || !(original_max_len > 0.0))
+    return fail(PKV_ERR_SHAPE, "rope parameters: theta > 1, factor > 0, 0 < low_freq_factor < "
+                "high_freq_factor and original_max_len > 0 are required");
+  if (D != 64 && D != 128) return fail(PKV_ERR_UNSUPPORTED, "unsupported D=%d", D);
+  pkv::RopeParams rp{rope_theta, rope_factor, low_freq_factor, high_freq_factor,
+                     original_max_len, {}};
+  pkv::rope_freqs(D, rp);
+  return decode_step_impl(q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables,
+                          context_lens, scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype,
+                          workspace, workspace_bytes, stream, true, &rp);
 }
 
 int pkv_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new,

@@ -151,4 +151,82 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- rotary embedding --------------------------------------------------------
+
+// Nearest-even rounding of a double straight to bf16 (8 significant bits):
+// round the double's 52-bit significand at bit 45, then the value is exact
+// in binary32 and its top 16 bits are the bf16.  (Finite values in the
+// normal range; rotated activations are.)
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  unsigned long long u = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long lsb = (u >> 45) & 1ull;
+  u += (1ull << 44) - 1ull + lsb;
+  u &= ~((1ull << 45) - 1ull);
+  const float f = (float)__longlong_as_double((long long)u);   // exact
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// Cosine and sine of an fp64 angle, for RoPE angles (a position times a
+// frequency <= 1).  Cody-Waite reduction x = k pi/2 + r, |r| <= pi/4, with
+// pi/2 split in three parts whose first two carry 33 significant bits, so
+// that k times each is exact for |k| < 2^20 (|x| < 2^19 here); then the
+// Taylor series of sin r to the r^19 term and of cos r to the r^18 term
+// (the first omitted terms are below 2^-70 for |r| <= pi/4), evaluated with
+// correctly rounded fused multiply-adds; the quadrant k mod 4 swaps and
+// negates.  Every operation is spelled out (no contraction left to the
+// compiler), so the two kernels that use it get identical bits.  Larger
+// angles take the library's sincos.
+__device__ __forceinline__ void rope_sincos(double x, double* s, double* c) {
+  if (!(__builtin_fabs(x) < 524288.0)) {
+    sincos(x, s, c);
+    return;
+  }
+  constexpr double kTwoOverPi = 0.6366197723675814;
+  constexpr double kP1 = 1.5707963267341256;        // 0x1.921fb544p+0
+  constexpr double kP2 = 6.077100506303966e-11;     // 0x1.0b4611a6p-34
+  constexpr double kP3 = 2.0222662487959506e-21;    // 0x1.3198a2e037073p-69
+  const double k = __builtin_rint(__dmul_rn(x, kTwoOverPi));
+  double r = __fma_rn(-k, kP1, x);
+  r = __fma_rn(-k, kP2, r);
+  r = __fma_rn(-k, kP3, r);
+  const double z = __dmul_rn(r, r);
+  // sin r = r (1 - z/3! + z^2/5! - ... - z^9/19!), cos r = 1 - z/2! + ... + z^9/18!
+  double ps = -8.22063524662433e-18;                 // -1/19!
+  ps = __fma_rn(ps, z, 2.8114572543455206e-15);      //  1/17!
+  ps = __fma_rn(ps, z, -7.647163731819816e-13);      // -1/15!
+  ps = __fma_rn(ps, z, 1.6059043836821613e-10);      //  1/13!
+  ps = __fma_rn(ps, z, -2.505210838544172e-08);      // -1/11!
+  ps = __fma_rn(ps, z, 2.7557319223985893e-06);      //  1/9!
+  ps = __fma_rn(ps, z, -0.0001984126984126984);      // -1/7!
+  ps = __fma_rn(ps, z, 0.008333333333333333);        //  1/5!
+  ps = __fma_rn(ps, z, -0.16666666666666666);        // -1/3!
+  const double sr = __fma_rn(__dmul_rn(ps, z), r, r);
+  double pc = 1.5619206968586225e-16;                //  1/18!
+  pc = __fma_rn(pc, z, -4.779477332387385e-14);      // -1/16!
+  pc = __fma_rn(pc, z, 1.1470745597729725e-11);      //  1/14!
+  pc = __fma_rn(pc, z, -2.08767569878681e-09);       // -1/12!
+  pc = __fma_rn(pc, z, 2.755731922398589e-07);       //  1/10!
+  pc = __fma_rn(pc, z, -2.48015873015873e-05);       // -1/8!
+  pc = __fma_rn(pc, z, 0.001388888888888889);        //  1/6!
+  pc = __fma_rn(pc, z, -0.041666666666666664);       // -1/4!
+  pc = __fma_rn(pc, z, 0.5);                         //  1/2!  (subtracted below)
+  const double cr = __fma_rn(-pc, z, 1.0);
+  const int q = (int)((long long)k & 3);
+  const double sv = (q & 1) ? cr : sr;
+  const double cv = (q & 1) ? sr : cr;
+  *s = (q & 2) ? -sv : sv;
+  *c = ((q + 1) & 2) ? -cv : cv;
+}
+
+// Rotate one pair (x[2i], x[2i+1]), two bf16 in a word, by the angle whose
+// cosine and sine are c, s: two separately rounded fp64 products and a
+// rounded sum or difference each, no fused multiply-add, then one rounding
+// to bf16.  Returns the rotated pair in the same packing.
+__device__ __forceinline__ uint32_t rotate_pair(uint32_t pair, double c, double s) {
+  const double x0 = (double)bf16_lo(pair), x1 = (double)bf16_hi(pair);
+  const uint32_t r0 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x0, c), __dmul_rn(x1, s)));
+  const uint32_t r1 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x0, s), __dmul_rn(x1, c)));
+  return r0 | (r1 << 16);
+}
+
 }  // namespace pkv

@@ -53,6 +53,12 @@ struct AttnParams {
   unsigned char* v_cache_w;
   float* k_scale_w;
   float* v_scale_w;
+  // RoPE inside the decode step (MFMA kernel, one query per sequence): when
+  // rope is set, q and the new keys arrive unrotated and each wave rotates
+  // them at position context_lens[b] - 1 with the D / 2 frequencies
+  // rope_freq (see RopeParams), as the RoPE append kernel does.
+  int rope;
+  double rope_freq[64];
 };
 
 struct WorkspaceLayout {

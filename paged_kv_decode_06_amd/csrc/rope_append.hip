@@ -14,12 +14,13 @@
 // only on D and the parameters) and passed in the kernel arguments.  Grid
 // (token, part): part 0 rotates the token's new key heads into LDS and
 // appends the rotated key and the value row exactly as the stand-alone
-// append does; parts 1.. rotate kQHeads query heads each into q_out.  Every
-// workgroup first tabulates the cos / sin of the token's D / 2 angles (bf16 copy, or fp8 / int8 codes
-// with a per-(block, kv head) scale).  The angle, cos / sin and the rotation
-// are computed in fp64 and the result is rounded once, straight from fp64
-// to bf16 (nearest even): each rotated element is the nearest bf16 to the
-// fp64 rotation.
+// append does (a bf16 copy, or fp8 / int8 codes with a per-(block, kv head)
+// scale); parts 1.. rotate kQHeads query heads each into q_out.  Every
+// workgroup first tabulates the cos / sin of the token's D / 2 angles in LDS
+// (rope_sincos, pkv_device.hpp; the decode step with RoPE uses the same
+// function, so the two paths agree bit for bit).  The angle, cos / sin and
+// the rotation are computed in fp64 and the result is rounded once, straight
+// from fp64 to bf16 (nearest even).
 
 #include <cmath>
 
@@ -31,29 +32,6 @@ namespace {
 
 constexpr int kRopeThreads = 256;
 constexpr int kQHeads = 8;   // query heads per workgroup
-
-// Nearest-even rounding of a double straight to bf16 (8 significant bits):
-// round the double's 52-bit significand at bit 45, then the value is exact
-// in binary32 and its top 16 bits are the bf16.  (Finite values in the
-// normal range; rotated activations are.)
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-  unsigned long long u = (unsigned long long)__double_as_longlong(x);
-  const unsigned long long lsb = (u >> 45) & 1ull;
-  u += (1ull << 44) - 1ull + lsb;
-  u &= ~((1ull << 45) - 1ull);
-  const float f = (float)__longlong_as_double((long long)u);   // exact
-  return (uint16_t)(__float_as_uint(f) >> 16);
-}
-
-// Rotate one pair by the angle whose cosine and sine are c, s; bf16 bits in,
-// bf16 bits out.
-__device__ __forceinline__ void rotate_pair(uint32_t pair, double c, double s, uint16_t& r0,
-                                            uint16_t& r1) {
-  const double x0 = (double)bf16_lo(pair), x1 = (double)bf16_hi(pair);
-  // two rounded products and a rounded sum each, no fused multiply-add
-  r0 = f64_to_bf16_rne(__dsub_rn(__dmul_rn(x0, c), __dmul_rn(x1, s)));
-  r1 = f64_to_bf16_rne(__dadd_rn(__dmul_rn(x0, s), __dmul_rn(x1, c)));
-}
 
 template <int D, int KIND>
 __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
@@ -72,7 +50,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
   // the angle pos * f_j is one rounded fp64 product, as in the oracle
   for (int j = tid; j < HP; j += kRopeThreads) {
     double sn, c;
-    sincos(__dmul_rn(pos, rp.freq[j]), &sn, &c);
+    rope_sincos(__dmul_rn(pos, rp.freq[j]), &sn, &c);
     cs[j][0] = c;
     cs[j][1] = sn;
   }
@@ -85,17 +63,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
     const int n = min(kQHeads, Hq - h0) * HP;
     for (int t = tid; t < n; t += kRopeThreads) {
       const int64_t e = ((int64_t)i * Hq + h0) * HP + t;
-      uint16_t r0, r1;
-      rotate_pair(q[e], cs[t % HP][0], cs[t % HP][1], r0, r1);
-      q_out[e] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+      q_out[e] = rotate_pair(q[e], cs[t % HP][0], cs[t % HP][1]);
     }
     return;
   }
   // key heads -> LDS
   for (int t = tid; t < Hkv * HP; t += kRopeThreads) {
-    uint16_t r0, r1;
-    rotate_pair(k_new[(int64_t)i * Hkv * HP + t], cs[t % HP][0], cs[t % HP][1], r0, r1);
-    k_rot[t] = (uint32_t)r0 | ((uint32_t)r1 << 16);
+    k_rot[t] = rotate_pair(k_new[(int64_t)i * Hkv * HP + t], cs[t % HP][0], cs[t % HP][1]);
   }
   __syncthreads();
 

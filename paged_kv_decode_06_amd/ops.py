@@ -74,6 +74,10 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
             fn.restype = I
+        Dbl = ctypes.c_double
+        lib.pkv_decode_step_rope.argtypes = ([P] * 9 + [F] + [Dbl] * 5 + [P] + [I] * 8
+                                             + [P, S, P])
+        lib.pkv_decode_step_rope.restype = I
         lib.pkv_status_string.argtypes = [I]
         lib.pkv_status_string.restype = ctypes.c_char_p
         lib.pkv_last_error.argtypes = []
@@ -379,18 +383,42 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, s
     _check("pkv_decode_step", _load().pkv_decode_step(*args))
 
 
+def _rope_args(rope) -> tuple:
+    r = dict(LLAMA3_ROPE)
+    r.update(rope or {})
+    return tuple(float(r[k]) for k in ("theta", "factor", "low_freq_factor", "high_freq_factor",
+                                       "original_max_len"))
+
+
+def decode_step_rope(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                     k_scale=None, v_scale=None, workspace=None, stream=None, rope=None) -> None:
+    """pkv_decode_step_rope: the decode step with RoPE of q and the new keys
+    at position context_lens[b] - 1 inside the partition kernel (q is not
+    changed).  `rope`: overrides of LLAMA3_ROPE.  Size the workspace with
+    attention_workspace_bytes(..., max_q_len=1)."""
+    a = _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                   k_scale, v_scale, workspace, stream)
+    _check("pkv_decode_step_rope",
+           _load().pkv_decode_step_rope(*(a[:10] + _rope_args(rope) + a[10:])))
+
+
 class PreparedStep:
-    """decode_step with its arguments marshalled once (see PreparedAttention)."""
+    """decode_step (or, with `rope`, decode_step_rope) with its arguments
+    marshalled once (see PreparedAttention)."""
 
     def __init__(self, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
-                 k_scale=None, v_scale=None, workspace=None, stream=None):
+                 k_scale=None, v_scale=None, workspace=None, stream=None, rope=None):
         self._args = _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
                                 scale, out, k_scale, v_scale, workspace, stream)
         a = self._args
         self._merge_args = (a[0],) + a[3:]     # the attention call's arguments
         self._lib = _load()
+        self._rope_args = None if rope is None else a[:10] + _rope_args(rope) + a[10:]
 
     def __call__(self):
+        if self._rope_args is not None:
+            _check("pkv_decode_step_rope", self._lib.pkv_decode_step_rope(*self._rope_args))
+            return
         _check("pkv_decode_step", self._lib.pkv_decode_step(*self._args))
 
     def partition(self):

@@ -130,3 +130,17 @@ def test_rope_kv_append_argument_checks(lib):
     assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 2, 64, 16, 4, 0,
              500000.0, 32.0, 4.0, 1.0, 8192.0, P) == -2                              # low >= high
     assert f(P, P, P, P, P, P, P, P, P, P, 1, 8, 2, 64, 16, 4, 0, *llama3, P) == -1   # NULL tensors
+
+
+def test_decode_step_rope_argument_checks(lib):
+    """Rope parameters and D are checked before any HIP call (no GPU needed)."""
+    f = lib.pkv_decode_step_rope
+    P = None
+    args = lambda theta, factor, low, high, orig, D=64: f(   # noqa: E731
+        P, P, P, P, P, P, P, P, P, 0.125, theta, factor, low, high, orig, P,
+        2, 8, 2, D, 16, 4, 4, 0, P, 0, P)
+    assert args(1.0, 32.0, 1.0, 4.0, 8192.0) == -2               # theta must exceed 1
+    assert args(500000.0, 0.0, 1.0, 4.0, 8192.0) == -2           # factor > 0
+    assert args(500000.0, 32.0, 4.0, 1.0, 8192.0) == -2          # low < high
+    assert args(500000.0, 32.0, 1.0, 4.0, 0.0) == -2             # original_max_len > 0
+    assert args(500000.0, 32.0, 1.0, 4.0, 8192.0, D=96) == -3    # D in {64, 128}
