@@ -445,12 +445,25 @@ def main():
                            q_out=q_rot, stream=stream)
         rope_att[i % copies]()
 
+    # The two are timed in alternating blocks of 5 steps (wall clock around
+    # each block), so that a drift of the GPU's clocks over the run weighs on
+    # both alike.
     with torch.cuda.stream(stream):
         for i in range(Wm):
             run_rope_fused(i)
             run_rope_split(i)
-        rope_step_ms = timed(run_rope_fused, Wm)
-        rope_split_ms = timed(run_rope_split, Wm)
+        spent = {run_rope_fused: 0.0, run_rope_split: 0.0}
+        n_blocks = max(1, K // 5)
+        for blk in range(n_blocks):
+            for run in (run_rope_fused, run_rope_split):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for i in range(5):
+                    run(Wm + 5 * blk + i)
+                torch.cuda.synchronize()
+                spent[run] += time.perf_counter() - t0
+        rope_step_ms = spent[run_rope_fused] * 1e3 / (5 * n_blocks)
+        rope_split_ms = spent[run_rope_split] * 1e3 / (5 * n_blocks)
 
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (part_avg_ms * 1e-3) / 1e9

@@ -506,8 +506,12 @@ void mfma_partition_kernel(const AttnParams p) {
                                : *reinterpret_cast<const uint4*>(p.v_new + src + 8 * (q - CH));
       }
     }
-    // (placed here, before the run's first page-table load: inside the
-    // chunk or tile loop it raised the loop's registers and measured slower)
+    // the page-table entries of the run's first chunk (lane l: page j0 + l),
+    // loaded beside q and the new rows
+    int bt_first = -1;
+    if (lane < min(kWave, pc.j1 - pc.j0)) bt_first = bt_row[table_page(pc.j0 + lane)];
+    // (RoPE here, with those loads in flight: inside the chunk or tile loop
+    // it raised the loop's registers and measured slower)
     if constexpr (ROPE) rope_rotate<S>(p, L_in - 1, lane, r, tile, qB, new_part, has_new);
     float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: head mem's last-block scales after the append
 
@@ -519,13 +523,13 @@ void mfma_partition_kernel(const AttnParams p) {
 
     for (int jc = pc.j0; jc < pc.j1; jc += kWave) {
       const int nchunk = min(kWave, pc.j1 - jc);
-      int phys_l = 0;
-      bool valid_l = false;
-      if (lane < nchunk) {
-        const int v = bt_row[table_page(jc + lane)];
-        valid_l = (unsigned)v < (unsigned)p.NB;
-        phys_l = valid_l ? v : 0;
+      int v = bt_first;
+      if (jc != pc.j0) {
+        v = -1;
+        if (lane < nchunk) v = bt_row[table_page(jc + lane)];
       }
+      const bool valid_l = (unsigned)v < (unsigned)p.NB;   // (-1: past the chunk)
+      const int phys_l = valid_l ? v : 0;
       const uint64_t valid = __builtin_amdgcn_ballot_w64(valid_l);   // pages with a real block id
 
       const int k_last = pc.n_b - 1 - jc;             // the run's last page in this chunk, if < nchunk
