@@ -681,13 +681,16 @@ void mfma_partition_kernel(const AttnParams p) {
         for (int j = 0; j < HG; ++j) {
           short4_t pj = pb;
           if (HG > 1 && mem != j) pj = short4_t{0, 0, 0, 0};
+          // every V operand of this kv head first, then the products (the
+          // reads stay pipelined whatever the register pressure elsewhere)
+          short4_t vA[NBN];
 #pragma unroll
-          for (int nb = 0; nb < NBN; ++nb) {
-            // (C-style cast: generic -> LDS address space)
-            const short4_t vA = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          for (int nb = 0; nb < NBN; ++nb)   // (C-style cast: generic -> LDS address space)
+            vA[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_short4_t*)(tile + v_rd + 2 * D * j + 32 * nb));
-            O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA, pj, O[nb], 0, 0, 0);
-          }
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj, O[nb], 0, 0, 0);
         }
       }
     }

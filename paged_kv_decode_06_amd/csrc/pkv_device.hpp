@@ -167,20 +167,19 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 }
 
 // Cosine and sine of an fp64 angle, for RoPE angles (a position times a
-// frequency <= 1).  Cody-Waite reduction x = k pi/2 + r, |r| <= pi/4, with
-// pi/2 split in three parts whose first two carry 33 significant bits, so
-// that k times each is exact for |k| < 2^20 (|x| < 2^19 here); then the
-// Taylor series of sin r to the r^19 term and of cos r to the r^18 term
-// (the first omitted terms are below 2^-70 for |r| <= pi/4), evaluated with
-// correctly rounded fused multiply-adds; the quadrant k mod 4 swaps and
-// negates.  Every operation is spelled out (no contraction left to the
-// compiler), so the two kernels that use it get identical bits.  Larger
-// angles take the library's sincos.
+// frequency <= 1, so |x| < 2^31).  Cody-Waite reduction x = k pi/2 + r,
+// |r| <= pi/4, with pi/2 split in three parts (the first two with 33
+// significant bits), each subtracted with a fused multiply-add: the product
+// k * part is exact inside the fma, so each step rounds once, on a result
+// that shrinks by 2^-33 per step, and r is accurate to far below an ulp of
+// sin for any such k.  Then the Taylor series of sin r to the r^19 term and
+// of cos r to the r^18 term (the first omitted terms are below 2^-70 for
+// |r| <= pi/4), evaluated with correctly rounded fused multiply-adds; the
+// quadrant k mod 4 swaps and negates.  Every operation is spelled out (no
+// contraction left to the compiler), so the two kernels that use it get
+// identical bits; and it calls no library routine, whose registers would
+// weigh on the kernels that inline it.
 __device__ __forceinline__ void rope_sincos(double x, double* s, double* c) {
-  if (!(__builtin_fabs(x) < 524288.0)) {
-    sincos(x, s, c);
-    return;
-  }
   constexpr double kTwoOverPi = 0.6366197723675814;
   constexpr double kP1 = 1.5707963267341256;        // 0x1.921fb544p+0
   constexpr double kP2 = 6.077100506303966e-11;     // 0x1.0b4611a6p-34
