@@ -66,6 +66,7 @@ extern "C" {
 #define PKV_ERR_WORKSPACE (-4)   /* workspace NULL or smaller than required */
 #define PKV_ERR_HIP (-5)         /* a HIP runtime call failed; see pkv_last_error() */
 #define PKV_ERR_ALIGN (-6)       /* a tensor pointer is not 16-byte aligned */
+#define PKV_ERR_INPUT (-7)       /* device-resident input breaks the contract (pkv_validate_inputs) */
 
 /* KV cache element types */
 #define PKV_KV_BF16 0
@@ -253,6 +254,21 @@ int pkv_decode_step_partition(const void* q, const void* k_new, const void* v_ne
                               float scale, void* out, int B, int Hq, int Hkv, int D, int BS,
                               int NB, int MBS, int kv_dtype, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* Debug check of the device-resident inputs of pkv_paged_decode_attention
+ * (same arguments; the attention calls trust them): every context length in
+ * [1, MBS * BS], the block ids of the pages each history uses
+ * (j < ceil(L_b / BS), "Decode Phase Attention Forward Pass", sections 2-3)
+ * in [0, NB), and for fp8 / int8 caches the K and V scales of those blocks
+ * positive and finite.  Runs the host checks of the attention call, one
+ * check kernel on `stream` (using the workspace's first 8 bytes), then
+ * SYNCHRONISES the stream.  Returns PKV_OK, or PKV_ERR_INPUT with the first
+ * violation (lowest sequence, then kind, then page) in pkv_last_error(). */
+int pkv_validate_inputs(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, void* out, int B, int Hq,
+                        int Hkv, int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* pkv_status_string(int status);

@@ -35,6 +35,7 @@ from .ops import (  # noqa: F401
     paged_decode_attention,
     paged_decode_merge,
     paged_decode_partition,
+    validate_inputs,
     workspace_bytes,
     library_path,
 )

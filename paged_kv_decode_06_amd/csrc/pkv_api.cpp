@@ -273,6 +273,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace too small";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_ALIGN: return "misaligned pointer";
+    case PKV_ERR_INPUT: return "device-resident input breaks the contract";
     default: return "unknown status";
   }
 }
@@ -425,6 +426,47 @@ int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   e = pkv::launch_merge(call.p, call.D, call.G, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+}
+
+int pkv_validate_inputs(const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, float scale, void* out, int B, int Hq,
+                        int Hkv, int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  AttnCall call;
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, workspace,
+                             workspace_bytes, &call);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // (the workspace's first word; the attention call rewrites it)
+  auto* first = static_cast<unsigned long long*>(workspace);
+  const bool q8 = kv_dtype != PKV_KV_BF16;
+  hipError_t e = pkv::launch_validate(block_tables, context_lens, q8 ? k_scale : nullptr,
+                                      q8 ? v_scale : nullptr, B, Hkv, BS, NB, MBS, first, s);
+  if (e != hipSuccess) return hip_fail(e, "validation kernel launch");
+  unsigned long long key = 0;
+  e = hipMemcpyAsync(&key, first, sizeof(key), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "validation readback");
+  if (key == ~0ull) return PKV_OK;
+  const int b = (int)(key >> 32), kind = (int)((key >> 28) & 0xf), j = (int)(key & 0xfffffff);
+  int32_t val = 0;
+  const int32_t* src = kind == 0 ? context_lens + b : block_tables + (long long)b * MBS + j;
+  e = hipMemcpy(&val, src, sizeof(val), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "validation readback");
+  switch (kind) {
+    case 0:
+      return fail(PKV_ERR_INPUT, "sequence %d: context length %d outside [1, MBS*BS = %lld]", b,
+                  val, (long long)MBS * BS);
+    case 1:
+      return fail(PKV_ERR_INPUT, "sequence %d, page %d: block id %d outside [0, NB = %d)", b, j,
+                  val, NB);
+    default:
+      return fail(PKV_ERR_INPUT, "sequence %d, page %d (block %d): a %s scale of the block is "
+                  "not a positive finite number", b, j, val, kind == 2 ? "K" : "V");
+  }
 }
 
 }  // extern "C"

@@ -138,6 +138,13 @@ hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, con
                               int Hkv, int D, int BS, int NB, int kind, const RopeParams& rp,
                               hipStream_t stream);
 
+// The check of pkv_validate_inputs (validate.hip): the first violation of
+// the device-resident contract, as b << 32 | kind << 28 | page, or ~0 for
+// none, is left in *first (a word of device memory).
+hipError_t launch_validate(const int32_t* block_tables, const int32_t* context_lens,
+                           const float* k_scale, const float* v_scale, int B, int Hkv, int BS,
+                           int NB, int MBS, unsigned long long* first, hipStream_t stream);
+
 // One-token append.  With `slots` NULL the slot of token i is derived from
 // the block table instead: position context_lens[i] - 1 of sequence i
 // (block_tables is [N, MBS]); a length outside [1, MBS * BS] skips the token.

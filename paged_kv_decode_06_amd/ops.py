@@ -57,7 +57,7 @@ def _load():
         lib.pkv_paged_decode_workspace_bytes.restype = S
         attn_args = [P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
         for name in ("pkv_paged_decode_attention", "pkv_paged_decode_partition",
-                     "pkv_paged_decode_merge"):
+                     "pkv_paged_decode_merge", "pkv_validate_inputs"):
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = I
@@ -277,6 +277,17 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
                       v_scale, workspace, stream)
     _check("pkv_paged_decode_attention", _load().pkv_paged_decode_attention(*args))
+
+
+def validate_inputs(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                    k_scale=None, v_scale=None, workspace=None, stream=None) -> None:
+    """pkv_validate_inputs: check the device-resident inputs of
+    paged_decode_attention (lengths, block ids of the used pages, fp8 / int8
+    scales of those blocks); synchronises the stream; raises PkvError
+    (PKV_ERR_INPUT) naming the first violation."""
+    args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
+                      v_scale, workspace, stream)
+    _check("pkv_validate_inputs", _load().pkv_validate_inputs(*args))
 
 
 def paged_decode_partition(q, k_cache, v_cache, block_tables, context_lens, scale, out,

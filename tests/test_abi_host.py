@@ -144,3 +144,13 @@ def test_decode_step_rope_argument_checks(lib):
     assert args(500000.0, 32.0, 4.0, 1.0, 8192.0) == -2          # low < high
     assert args(500000.0, 32.0, 1.0, 4.0, 0.0) == -2             # original_max_len > 0
     assert args(500000.0, 32.0, 1.0, 4.0, 8192.0, D=96) == -3    # D in {64, 128}
+
+
+def test_validate_inputs_host_checks(lib):
+    """The validation call runs the attention call's host checks first (no GPU needed)."""
+    f = lib.pkv_validate_inputs
+    P = None
+    assert f(P, P, P, P, P, P, P, 0.125, P, 0, 8, 2, 64, 16, 4, 4, 0, P, 0, P) == 0    # B = 0
+    assert f(P, P, P, P, P, P, P, 0.125, P, 2, 8, 2, 64, 16, 4, 4, 0, P, 0, P) == -1   # NULL q
+    assert f(P, P, P, P, P, P, P, 0.125, P, 2, 8, 2, 96, 16, 4, 4, 0, P, 0, P) == -3   # D = 96
+    assert lib.pkv_status_string(-7).decode() == "device-resident input breaks the contract"
