@@ -20,9 +20,8 @@ namespace {
 
 // Merge: one wave per (sequence, query head), four per workgroup.  The
 // rows of a (b, u) run are k + segment for the consecutive pieces k0..k1
-// that cover it.  A row is D floats; TPR lanes take 4 dims each, so
-// the wave reads RPW rows per step, and the unrolled loop keeps several
-// steps of independent loads in flight; the RPW row groups are summed with
+// that cover it.  A row is D floats; TPR lanes take 4 dims each, so the
+// wave reads RPW rows per step; the RPW row groups are combined with
 // cross-lane shuffles at the end.
 template <int D>
 __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnParams p, int G) {
@@ -63,23 +62,59 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
   const float* __restrict__ ml = p.ws_ml;
   const float* __restrict__ po = p.ws_o;
 
-  float M = -FLT_MAX;
-  for (int i = lane; i < P; i += kWave) M = fmaxf(M, ml[((rok0 + i) * C + col) * 2]);
-  M = wave_max(M);
-
+  // One pass: row group `sub` takes shares sub, sub + RPW, ..., kBatch at a
+  // time, loading their (m, l) and o together (one wait on memory per
+  // batch); it keeps its own running max Mg and rescales what it has summed
+  // when a batch brings a larger m.  The groups are then brought to the
+  // wave's max and summed.
+  constexpr int kBatch = 4;
+  float Mg = -FLT_MAX;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
-#pragma unroll 8
-  for (int i = sub; i < P; i += RPW) {
-    const int64_t row = (rok0 + i) * C + col;
-    const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
-    const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
-    const float w = fast_exp2(mlv.x - M);
-    den = fmaf(w, mlv.y, den);
-    acc.x = fmaf(w, o.x, acc.x);
-    acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z);
-    acc.w = fmaf(w, o.w, acc.w);
+  for (int i0 = sub; i0 < P; i0 += RPW * kBatch) {
+    float2 mlv[kBatch];
+    float4 o[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = i0 + t * RPW;
+      mlv[t] = make_float2(-FLT_MAX, 0.0f);
+      o[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < P) {
+        const int64_t row = (rok0 + i) * C + col;
+        mlv[t] = *reinterpret_cast<const float2*>(ml + row * 2);
+        o[t] = *reinterpret_cast<const float4*>(po + row * D + d4);
+      }
+    }
+    float mb = Mg;
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) mb = fmaxf(mb, mlv[t].x);
+    const float a = fast_exp2(Mg - mb);
+    den *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const float w = fast_exp2(mlv[t].x - mb);
+      den = fmaf(w, mlv[t].y, den);
+      acc.x = fmaf(w, o[t].x, acc.x);
+      acc.y = fmaf(w, o[t].y, acc.y);
+      acc.z = fmaf(w, o[t].z, acc.z);
+      acc.w = fmaf(w, o[t].w, acc.w);
+    }
+    Mg = mb;
+  }
+  float M = Mg;
+#pragma unroll
+  for (int off = TPR; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  {
+    const float a = fast_exp2(Mg - M);
+    den *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
   }
 #pragma unroll
   for (int off = TPR; off < kWave; off <<= 1) {
