@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnPara
 
 // Merge for few rows with many shares each (long contexts): one workgroup
 // per (sequence, query head); thread t owns 4 head dims of every NGRP-th
-// share, so NGRP shares are read at once, and the groups are summed
+// share, so NGRP shares are read at once, and the groups are combined
 // through LDS.
 template <int D>
 __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const AttnParams p, int G) {
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   constexpr int NGRP = kAttnBlockThreads / TPR;
   __shared__ float s_acc[NGRP][D];
   __shared__ float s_den[NGRP];
-  __shared__ float s_max[kAttnWavesPerBlock];
+  __shared__ float s_max[NGRP];
   const int t = threadIdx.x;
   const int grp = t / TPR;
   const int d4 = (t % TPR) * 4;
@@ -176,43 +176,68 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   const float* __restrict__ ml = p.ws_ml;
   const float* __restrict__ po = p.ws_o;
 
-  float m_loc = -FLT_MAX;
-  for (int i = t; i < P; i += kAttnBlockThreads) m_loc = fmaxf(m_loc, ml[((row0 + i) * C + col) * 2]);
-  m_loc = wave_max(m_loc);
-  if ((t & (kWave - 1)) == 0) s_max[t >> 6] = m_loc;
-  __syncthreads();
-  float M = s_max[0];
-#pragma unroll
-  for (int w = 1; w < kAttnWavesPerBlock; ++w) M = fmaxf(M, s_max[w]);
-
+  // One pass, as in merge_kernel: group `grp` takes shares grp, grp + NGRP,
+  // ..., kBatch at a time, with its own running max; the groups meet in LDS,
+  // where each is brought to the common max.
+  constexpr int kBatch = 4;
+  float Mg = -FLT_MAX;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
-#pragma unroll 4
-  for (int i = grp; i < P; i += NGRP) {
-    const int64_t row = (row0 + i) * C + col;
-    const float2 mlv = *reinterpret_cast<const float2*>(ml + row * 2);
-    const float4 o = *reinterpret_cast<const float4*>(po + row * D + d4);
-    const float w = fast_exp2(mlv.x - M);
-    den = fmaf(w, mlv.y, den);
-    acc.x = fmaf(w, o.x, acc.x);
-    acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z);
-    acc.w = fmaf(w, o.w, acc.w);
+  for (int i0 = grp; i0 < P; i0 += NGRP * kBatch) {
+    float2 mlv[kBatch];
+    float4 o[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k * NGRP;
+      mlv[k] = make_float2(-FLT_MAX, 0.0f);
+      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < P) {
+        const int64_t row = (row0 + i) * C + col;
+        mlv[k] = *reinterpret_cast<const float2*>(ml + row * 2);
+        o[k] = *reinterpret_cast<const float4*>(po + row * D + d4);
+      }
+    }
+    float mb = Mg;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, mlv[k].x);
+    const float a = fast_exp2(Mg - mb);
+    den *= a;
+    acc.x *= a;
+    acc.y *= a;
+    acc.z *= a;
+    acc.w *= a;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = fast_exp2(mlv[k].x - mb);
+      den = fmaf(w, mlv[k].y, den);
+      acc.x = fmaf(w, o[k].x, acc.x);
+      acc.y = fmaf(w, o[k].y, acc.y);
+      acc.z = fmaf(w, o[k].z, acc.z);
+      acc.w = fmaf(w, o[k].w, acc.w);
+    }
+    Mg = mb;
   }
   *reinterpret_cast<float4*>(&s_acc[grp][d4]) = acc;
-  if (d4 == 0) s_den[grp] = den;
+  if (d4 == 0) {
+    s_den[grp] = den;
+    s_max[grp] = Mg;
+  }
   __syncthreads();
   if (t < TPR) {
+    float M = s_max[0];
+#pragma unroll
+    for (int q = 1; q < NGRP; ++q) M = fmaxf(M, s_max[q]);
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
     float dsum = 0.0f;
 #pragma unroll
     for (int q = 0; q < NGRP; ++q) {
+      const float a = fast_exp2(s_max[q] - M);
       const float4 v = *reinterpret_cast<const float4*>(&s_acc[q][d4]);
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
-      dsum += s_den[q];
+      sum.x = fmaf(a, v.x, sum.x);
+      sum.y = fmaf(a, v.y, sum.y);
+      sum.z = fmaf(a, v.z, sum.z);
+      sum.w = fmaf(a, v.w, sum.w);
+      dsum = fmaf(a, s_den[q], dsum);
     }
     const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;   // 0: the query sees no key
     *reinterpret_cast<uint2*>(op + d4) =
