@@ -73,7 +73,10 @@ struct MfmaShape {
   static constexpr int NBN = D / 16;          // output n-blocks (16x16x16)
   static constexpr int SUB = BS / 16;         // 16-token tiles per page
   static constexpr int PITCH = HG * 2 * D + 32;   // LDS row pitch (bytes) of a bf16 tile
-  static constexpr bool KV_TOGETHER = 16 * URB <= 2048;   // issue a tile's K and V loads at once
+  // issue a tile's K and V loads at once: when a half tile is 2 KB or less,
+  // and for int8 units of several heads (4 KB halves; measured 2% faster on
+  // a B128 BS32 step, while the same order made fp8 2.5% slower)
+  static constexpr bool KV_TOGETHER = 16 * URB <= 2048 || (INT8 && HG > 1);
   // waves per SIMD: a unit of several heads keeps several times the bytes
   // of a one-head tile in flight per wave, and two such waves per SIMD
   // measured faster than three (bf16 D = 128, two heads: 107 vs 111 us on
@@ -541,9 +544,10 @@ void mfma_partition_kernel(const AttnParams p) {
       // 128) is enough on its own, so its V loads are issued only once the K
       // loads have landed (issuing both at once measured ~7% slower with one
       // head per wave, 2-3% with two); 2 KB halves (one head, fp8 / int8 or
-      // D = 64) issue K and V together (~3% faster than in turn).  The other
-      // waves of the CU overlap their compute with the waits; issuing the
-      // next tile's K early measured 3-7% slower.
+      // D = 64) issue K and V together (~3% faster than in turn), and so do
+      // int8 units (see KV_TOGETHER).  The other waves of the CU overlap
+      // their compute with the waits; issuing the next tile's K early
+      // measured 3-7% slower.
       auto tile_base = [&](int u) {   // (wave-uniform)
         const int k = u / SUB, sb = u % SUB;
         const int phys = __builtin_amdgcn_readlane(phys_l, k);
