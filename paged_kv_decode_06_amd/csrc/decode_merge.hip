@@ -18,117 +18,85 @@
 namespace pkv {
 namespace {
 
-// Merge: one wave per (sequence, query head), four per workgroup.  The
-// rows of a (b, u) run are k + segment for the consecutive pieces k0..k1
-// that cover it.  A row is D floats; TPR lanes take 4 dims each, so the
-// wave reads RPW rows per step; the RPW row groups are combined with
-// cross-lane shuffles at the end.
+// Merge, one workgroup per (sequence, unit) run: the run's shares are rows
+// k0 + seg .. k1 + seg, each holding the unit's `cols` columns.  Thread t
+// owns dims 4 (t % TPR) .. + 3 of column t / TPR and folds in every share of
+// the run itself, kBatch at a time: each share's (m, l) and o are loaded
+// together (one wait on memory per batch) and the running max is rescaled
+// when a batch brings a larger m.  The run's prefix sums and split are read
+// once for all its columns.
 template <int D>
-__global__ __launch_bounds__(kAttnBlockThreads) void merge_kernel(const AttnParams p, int G) {
-  constexpr int TPR = D / 4;                   // lanes per row (4 dims each)
-  constexpr int RPW = kWave / TPR;             // rows per wave step
-  const int lane = threadIdx.x & (kWave - 1);
-  const int sub = lane / TPR;
-  const int d4 = (lane % TPR) * 4;
-  const int64_t bqh = (int64_t)blockIdx.x * kAttnWavesPerBlock + (threadIdx.x >> 6);
-  if (bqh >= (int64_t)p.B * p.max_q * p.Hq) return;
-  const int b = (int)(bqh / ((int64_t)p.max_q * p.Hq));
-  const int qi = (int)(bqh / p.Hq % p.max_q);
-  const int h = (int)(bqh % p.Hq);
-  if (qi >= seq_queries(p, b)) return;
-  const int UG = p.hg * G;
-  const int u = h / UG;
-  const int col = qi * UG + h % UG;
-  const int C = p.cols;
+__global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams p, int G) {
+  constexpr int TPR = D / 4;                   // threads per column (4 dims each)
+  constexpr int kBatch = 8;
   const int U = p.Hkv / p.hg;
+  const int seg = blockIdx.x;                  // b U + u
+  const int b = seg / U, u = seg % U;
+  const int n = threadIdx.x / TPR;             // column
+  const int d4 = (threadIdx.x % TPR) * 4;
+  const int C = p.cols;
+  const int UG = p.hg * G;
+  const int qi = n / UG;
+  if (n >= C || qi >= seq_queries(p, b)) return;
+  const int h = u * UG + n % UG;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
-  const int total = U * pre_B;
   const int n_b = pre_b1 - pre_b;
   const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
-  uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D;
+  uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D + d4;
   if (n_b == 0) {                              // empty history: defined as 0
-    if (lane < TPR) *reinterpret_cast<uint2*>(op + d4) = make_uint2(0, 0);
+    *reinterpret_cast<uint2*>(op) = make_uint2(0, 0);
     return;
   }
-  const WorkSplit split = make_split(total, p.total_waves);
+  const WorkSplit split = make_split(U * pre_B, p.total_waves);
   const int start = U * pre_b + u * n_b;
   const int k0 = piece_of(split, start);
   const int k1 = piece_of(split, start + n_b - 1);
   if (k0 == k1) return;                        // finished by the partition kernel
-  const int seg = b * U + u;
   const int P = k1 - k0 + 1;
-  const int64_t rok0 = (int64_t)k0 + seg;
+  const int64_t row0 = (int64_t)k0 + seg;
   const float* __restrict__ ml = p.ws_ml;
   const float* __restrict__ po = p.ws_o;
 
-  // One pass: row group `sub` takes shares sub, sub + RPW, ..., kBatch at a
-  // time, loading their (m, l) and o together (one wait on memory per
-  // batch); it keeps its own running max Mg and rescales what it has summed
-  // when a batch brings a larger m.  The groups are then brought to the
-  // wave's max and summed.
-  constexpr int kBatch = 4;
-  float Mg = -FLT_MAX;
+  float M = -FLT_MAX;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
-  for (int i0 = sub; i0 < P; i0 += RPW * kBatch) {
+  for (int i0 = 0; i0 < P; i0 += kBatch) {
     float2 mlv[kBatch];
     float4 o[kBatch];
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const int i = i0 + t * RPW;
-      mlv[t] = make_float2(-FLT_MAX, 0.0f);
-      o[t] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i < P) {
-        const int64_t row = (rok0 + i) * C + col;
-        mlv[t] = *reinterpret_cast<const float2*>(ml + row * 2);
-        o[t] = *reinterpret_cast<const float4*>(po + row * D + d4);
+    for (int k = 0; k < kBatch; ++k) {
+      mlv[k] = make_float2(-FLT_MAX, 0.0f);
+      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i0 + k < P) {
+        const int64_t row = (row0 + i0 + k) * C + n;
+        mlv[k] = *reinterpret_cast<const float2*>(ml + row * 2);
+        o[k] = *reinterpret_cast<const float4*>(po + row * D + d4);
       }
     }
-    float mb = Mg;
+    float mb = M;
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) mb = fmaxf(mb, mlv[t].x);
-    const float a = fast_exp2(Mg - mb);
+    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, mlv[k].x);
+    const float a = fast_exp2(M - mb);
     den *= a;
     acc.x *= a;
     acc.y *= a;
     acc.z *= a;
     acc.w *= a;
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const float w = fast_exp2(mlv[t].x - mb);
-      den = fmaf(w, mlv[t].y, den);
-      acc.x = fmaf(w, o[t].x, acc.x);
-      acc.y = fmaf(w, o[t].y, acc.y);
-      acc.z = fmaf(w, o[t].z, acc.z);
-      acc.w = fmaf(w, o[t].w, acc.w);
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = fast_exp2(mlv[k].x - mb);
+      den = fmaf(w, mlv[k].y, den);
+      acc.x = fmaf(w, o[k].x, acc.x);
+      acc.y = fmaf(w, o[k].y, acc.y);
+      acc.z = fmaf(w, o[k].z, acc.z);
+      acc.w = fmaf(w, o[k].w, acc.w);
     }
-    Mg = mb;
+    M = mb;
   }
-  float M = Mg;
-#pragma unroll
-  for (int off = TPR; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-  {
-    const float a = fast_exp2(Mg - M);
-    den *= a;
-    acc.x *= a;
-    acc.y *= a;
-    acc.z *= a;
-    acc.w *= a;
-  }
-#pragma unroll
-  for (int off = TPR; off < kWave; off <<= 1) {
-    acc.x += __shfl_xor(acc.x, off);
-    acc.y += __shfl_xor(acc.y, off);
-    acc.z += __shfl_xor(acc.z, off);
-    acc.w += __shfl_xor(acc.w, off);
-    den += __shfl_xor(den, off);
-  }
-  if (lane < TPR) {
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // 0: the query sees no key
-    *reinterpret_cast<uint2*>(op + d4) =
-        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
-  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // 0: the query sees no key
+  *reinterpret_cast<uint2*>(op) =
+      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
 }
 
 // Merge for few rows with many shares each (long contexts): one workgroup
@@ -176,7 +144,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   const float* __restrict__ ml = p.ws_ml;
   const float* __restrict__ po = p.ws_o;
 
-  // One pass, as in merge_kernel: group `grp` takes shares grp, grp + NGRP,
+  // One pass, as in merge_seg_kernel: group `grp` takes shares grp, grp + NGRP,
   // ..., kBatch at a time, with its own running max; the groups meet in LDS,
   // where each is brought to the common max.
   constexpr int kBatch = 4;
@@ -248,7 +216,8 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
 }  // namespace
 
 // Fewer (sequence, query head) rows than this get a workgroup each (they
-// are few and have many shares: long contexts); more get a wave each.
+// are few and have many shares: long contexts); more are merged a run at a
+// time.
 constexpr int64_t kWideMergeRows = 1024;
 
 hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
@@ -265,11 +234,13 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((rows + kAttnWavesPerBlock - 1) / kAttnWavesPerBlock));
+  // (a workgroup per run: cols <= 16 columns of D / 4 threads)
+  const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)));
+  if (p.cols < 1 || p.cols > 16) return hipErrorInvalidValue;
   if (D == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kAttnBlockThreads), 0, stream, p, G);
+    hipLaunchKernelGGL(merge_seg_kernel<128>, grid, dim3(p.cols * 32), 0, stream, p, G);
   else if (D == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kAttnBlockThreads), 0, stream, p, G);
+    hipLaunchKernelGGL(merge_seg_kernel<64>, grid, dim3(p.cols * 16), 0, stream, p, G);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

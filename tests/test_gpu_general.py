@@ -154,7 +154,7 @@ def test_full_configuration_sampled(name):
     ref = host.attention()
     gpu = GS.bf16_to_f64(out)[host.rows]
     GS.assert_attention_close(gpu, ref, wl.kv_dtype, name)
-    say(name, GS.error_report(gpu, ref))
+    say(name, GS.error_report(gpu, ref, wl.kv_dtype))
 
 
 def test_unsupported_query_counts_are_rejected():

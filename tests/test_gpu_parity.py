@@ -234,7 +234,7 @@ def test_full_configuration_sampled(name, kernel):
     ref = host.attention()
     gpu = GS.bf16_to_f64(out)[seqs]
     GS.assert_attention_close(gpu, ref, wl.kv_dtype, name)
-    say(name, GS.error_report(gpu, ref))
+    say(name, GS.error_report(gpu, ref, wl.kv_dtype))
     assert torch.isfinite(out.float()).all()
 
 
