@@ -146,8 +146,9 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
 
   // One pass, as in merge_seg_kernel: group `grp` takes shares grp, grp + NGRP,
   // ..., kBatch at a time, with its own running max; the groups meet in LDS,
-  // where each is brought to the common max.
-  constexpr int kBatch = 4;
+  // where each is brought to the common max.  (Few workgroups: registers for
+  // a deep batch are free, and 16 covers a 128-share row in one trip.)
+  constexpr int kBatch = 16;
   float Mg = -FLT_MAX;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
