@@ -312,8 +312,8 @@ def main():
     kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": ops.KV_INT8}[wl.kv_dtype]
     # (also large enough for the RoPE step, which always runs the MFMA kernel)
     ws = torch.zeros(max(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
-                         ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS,
-                                                       kvd, 1)),
+                         ops.decode_step_rope_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS,
+                                                              wl.MBS, kvd)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(wl.q)
     caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]

@@ -233,9 +233,22 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
  * caches, scales and out bit-identical to those two calls (q itself is not
  * changed).  Always runs the MFMA partition kernel, which rotates q in
  * registers and the new key rows before it stores them, so the step is two
- * launches; size the workspace with pkv_paged_attention_workspace_bytes
- * (max_q_len = 1).  D in {64, 128}; other arguments as for pkv_decode_step.
- * Bad rope parameters give PKV_ERR_SHAPE.  B == 0 is a no-op. */
+ * launches.  Size the workspace with pkv_decode_step_rope_workspace_bytes.
+ * When the call serves one kv head per partition wave (odd Hkv, or
+ * pkv_select_unit_heads(1)) and Hkv <= 8, the step runs
+ * as exactly those two calls instead (three launches; the rotated q goes to
+ * the end of the workspace), which is faster there; a workspace of only
+ * pkv_paged_attention_workspace_bytes(max_q_len = 1) bytes leaves no room
+ * for it and keeps the fused kernel.  The bits are the same either way.
+ * D in {64, 128}; other arguments as for pkv_decode_step.  Bad rope
+ * parameters give PKV_ERR_SHAPE.  B == 0 is a no-op. */
+/* Workspace bytes for pkv_decode_step_rope: those of
+ * pkv_paged_attention_workspace_bytes(..., max_q_len = 1) plus room for a
+ * rotated copy of q (B * Hq * D bf16, rounded up to 256 bytes).  0 for an
+ * unsupported shape. */
+size_t pkv_decode_step_rope_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                            int kv_dtype);
+
 int pkv_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, float* k_scale, float* v_scale,
                          const int32_t* block_tables, const int32_t* context_lens, float scale,

@@ -124,8 +124,15 @@ struct AttnCall {
   pkv::AttnParams p;
   pkv::AttnPath path;
   int D, BS, G, blocks;
-  int kind;   // pkv::KvKind (= kv_dtype)
+  int kind;          // pkv::KvKind (= kv_dtype)
+  size_t ws_used;    // workspace bytes the call's layout takes (a multiple of 256)
 };
+
+// Room for a rotated copy of q ([B, Hq, D] bf16) at the end of a decode step
+// with RoPE's workspace.
+size_t rope_q_room(int B, int Hq, int D) {
+  return ((size_t)B * Hq * D * 2 + 255) & ~size_t(255);
+}
 
 // Options beyond one query per sequence; the defaults are the decode call.
 struct QueryOpts {
@@ -240,6 +247,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   call->G = G;
   call->kind = kv_dtype;
   call->blocks = blocks;
+  call->ws_used = lay.total;
   return PKV_OK;
 }
 
@@ -348,6 +356,12 @@ size_t pkv_paged_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, i
 size_t pkv_paged_attention_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
                                            int kv_dtype, int max_q_len) {
   return workspace_bytes_for(B, Hq, Hkv, D, BS, MBS, kv_dtype, max_q_len, true);
+}
+
+size_t pkv_decode_step_rope_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                            int kv_dtype) {
+  const size_t n = workspace_bytes_for(B, Hq, Hkv, D, BS, MBS, kv_dtype, 1, true);
+  return n == 0 ? 0 : n + rope_q_room(B, Hq, D);
 }
 
 int pkv_paged_attention(const void* q, const int32_t* q_start, int max_q_len,
@@ -493,6 +507,27 @@ int decode_step_impl(const void* q, const void* k_new, const void* v_new, void* 
   if (B == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // RoPE with one kv head per wave (odd Hkv, say): the fused kernel's
+  // one-head instantiation is slower than the two calls the step is defined
+  // to equal (129.9 vs 112.5 us on a B64 Hq32 Hkv8 step), so when the
+  // workspace has room for the rotated q, those two calls are what runs:
+  // the RoPE append at each sequence's last position, then the attention.
+  if (rope && call.path == pkv::AttnPath::kMfma && call.p.hg == 1 && Hkv <= 8) {
+    const size_t room = rope_q_room(B, Hq, D);
+    if (workspace_bytes >= call.ws_used + room) {
+      void* q_rot = static_cast<char*>(workspace) + ((workspace_bytes - room) & ~size_t(255));
+      e = pkv::launch_rope_append(q, q_rot, k_new, v_new, nullptr, nullptr, k_cache, v_cache,
+                                  k_scale, v_scale, B, Hq, Hkv, D, BS, NB, call.kind, *rope, s,
+                                  context_lens, block_tables, MBS);
+      if (e != hipSuccess) return hip_fail(e, "rope_kv_append kernel launch");
+      call.p.q = q_rot;
+      e = launch_partition(call, s);
+      if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+      if (!merge) return PKV_OK;
+      e = pkv::launch_merge(call.p, call.D, call.G, s);
+      return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+    }
+  }
   if (call.path == pkv::AttnPath::kMfma) {
     pkv::AttnParams& p = call.p;
     if (rope) {

@@ -131,12 +131,16 @@ struct RopeParams {
 void rope_freqs(int D, RopeParams& rp);
 
 // RoPE of q (into q_out) and of the new keys, then the append of the rotated
-// keys and the values into `slots` (see rope_append.hip).  Hkv <= 8.
+// keys and the values into `slots` (see rope_append.hip).  Hkv <= 8.  With
+// positions and slots both NULL, token i is sequence i's new token: position
+// context_lens[i] - 1, slot from block_tables ([N, MBS]), as the decode step
+// places it.
 hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new,
                               const int32_t* positions, const int32_t* slots, void* k_cache,
                               void* v_cache, float* k_scale, float* v_scale, int N, int Hq,
                               int Hkv, int D, int BS, int NB, int kind, const RopeParams& rp,
-                              hipStream_t stream);
+                              hipStream_t stream, const int32_t* context_lens = nullptr,
+                              const int32_t* block_tables = nullptr, int MBS = 0);
 
 // The check of pkv_validate_inputs (validate.hip): the first violation of
 // the device-resident contract, as b << 32 | kind << 28 | page, or ~0 for

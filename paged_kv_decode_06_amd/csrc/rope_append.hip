@@ -37,15 +37,21 @@ template <int D, int KIND>
 __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
     const uint32_t* q, uint32_t* q_out, const uint32_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ positions,
-    const int32_t* __restrict__ slots, unsigned char* k_cache, unsigned char* v_cache,
-    float* k_scale, float* v_scale, int Hq, int Hkv, int BS, int NB, const RopeParams rp) {
+    const int32_t* __restrict__ slots, const int32_t* __restrict__ context_lens,
+    const int32_t* __restrict__ block_tables, int MBS, unsigned char* k_cache,
+    unsigned char* v_cache, float* k_scale, float* v_scale, int Hq, int Hkv, int BS, int NB,
+    const RopeParams rp) {
   constexpr int HP = D / 2;                   // pairs per head
   __shared__ uint32_t k_rot[8 * HP];          // the token's rotated key heads (Hkv <= 8)
   __shared__ double cs[HP][2];                // cos, sin of pair j's angle (every head's)
   const int i = blockIdx.x;
   const int part = blockIdx.y;
   const int tid = threadIdx.x;
-  const double pos = (double)positions[i];
+  // positions / slots NULL: token i is the new token of sequence i, at
+  // position context_lens[i] - 1 of the sequence ([N, MBS] block table); a
+  // length outside [1, MBS * BS] skips its append (q is still rotated)
+  const int L = positions == nullptr ? context_lens[i] : 0;
+  const double pos = positions != nullptr ? (double)positions[i] : (double)L - 1.0;
 
   // the angle pos * f_j is one rounded fp64 product, as in the oracle
   for (int j = tid; j < HP; j += kRopeThreads) {
@@ -73,7 +79,13 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
   }
   __syncthreads();
 
-  const int64_t slot = slots[i];
+  int64_t slot = -1;
+  if (slots != nullptr) {
+    slot = slots[i];
+  } else if (L >= 1 && L <= MBS * BS) {
+    const int t = L - 1;
+    slot = (int64_t)block_tables[(int64_t)i * MBS + t / BS] * BS + t % BS;
+  }
   if (slot < 0 || slot >= (int64_t)NB * BS) return;
   const int64_t row = slot * Hkv * D;         // element offset of the slot's row
   if constexpr (KIND == kKvBf16) {
@@ -153,15 +165,20 @@ hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, con
                               const int32_t* positions, const int32_t* slots, void* k_cache,
                               void* v_cache, float* k_scale, float* v_scale, int N, int Hq,
                               int Hkv, int D, int BS, int NB, int kind, const RopeParams& rp,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* context_lens,
+                              const int32_t* block_tables, int MBS) {
   if (N == 0) return hipSuccess;
   if (Hkv > 8) return hipErrorInvalidValue;
+  if ((positions == nullptr) != (slots == nullptr)) return hipErrorInvalidValue;
+  if (positions == nullptr && (context_lens == nullptr || block_tables == nullptr || MBS < 1))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)N, 1u + (unsigned)((Hq + kQHeads - 1) / kQHeads));
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, dim3(kRopeThreads), 0, stream, (const uint32_t*)q,
                        (uint32_t*)q_out, (const uint32_t*)k_new, (const uint16_t*)v_new,
-                       positions, slots, (unsigned char*)k_cache, (unsigned char*)v_cache,
-                       k_scale, v_scale, Hq, Hkv, BS, NB, rp);
+                       positions, slots, context_lens, block_tables, MBS,
+                       (unsigned char*)k_cache, (unsigned char*)v_cache, k_scale, v_scale, Hq,
+                       Hkv, BS, NB, rp);
   };
   if (D == 128) {
     if (kind == kKvBf16) go(rope_append_kernel<128, kKvBf16>);

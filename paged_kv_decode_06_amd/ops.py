@@ -70,6 +70,8 @@ def _load():
         lib.pkv_paged_attention.restype = I
         lib.pkv_paged_attention_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
         lib.pkv_paged_attention_workspace_bytes.restype = S
+        lib.pkv_decode_step_rope_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+        lib.pkv_decode_step_rope_workspace_bytes.restype = S
         for name in ("pkv_decode_step", "pkv_decode_step_partition"):
             fn = getattr(lib, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, P, F, P, I, I, I, I, I, I, I, I, P, S, P]
@@ -306,6 +308,10 @@ def paged_decode_merge(q, k_cache, v_cache, block_tables, context_lens, scale, o
     _check("pkv_paged_decode_merge", _load().pkv_paged_decode_merge(*args))
 
 
+def decode_step_rope_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:
+    return int(_load().pkv_decode_step_rope_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype))
+
+
 def attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16, max_q_len=1) -> int:
     return int(_load().pkv_paged_attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype,
                                                            max_q_len))
@@ -406,7 +412,7 @@ def decode_step_rope(q, k_new, v_new, k_cache, v_cache, block_tables, context_le
     """pkv_decode_step_rope: the decode step with RoPE of q and the new keys
     at position context_lens[b] - 1 inside the partition kernel (q is not
     changed).  `rope`: overrides of LLAMA3_ROPE.  Size the workspace with
-    attention_workspace_bytes(..., max_q_len=1)."""
+    decode_step_rope_workspace_bytes."""
     a = _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
                    k_scale, v_scale, workspace, stream)
     _check("pkv_decode_step_rope",

@@ -35,18 +35,22 @@ def _restore():
     default_kernel()
 
 
-def workspace(wl):
+def workspace(wl, q_room=True):
+    """The RoPE step's workspace; without the room for a rotated q (the
+    attention call's size) a one-head call keeps the fused kernel."""
     kvd = GS.KV_KIND[wl.kv_dtype]
     n = max(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
             ops.attention_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd, 1))
+    if q_room:
+        n = ops.decode_step_rope_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd)
     return torch.zeros(n, dtype=torch.uint8, device=DEV)
 
 
-def fused(wl, rope=None):
+def fused(wl, rope=None, q_room=True):
     out = torch.empty_like(wl.q)
     ops.decode_step_rope(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, wl.block_tables,
-                         wl.context_lens, wl.scale, out, wl.k_scale, wl.v_scale, workspace(wl),
-                         rope=rope)
+                         wl.context_lens, wl.scale, out, wl.k_scale, wl.v_scale,
+                         workspace(wl, q_room), rope=rope)
     return out
 
 
@@ -65,10 +69,10 @@ def two_calls(wl, rope=None):
     return out
 
 
-def assert_fused_equals_two_calls(wl, what, rope=None):
+def assert_fused_equals_two_calls(wl, what, rope=None, q_room=True):
     other = twin(wl)
     q0 = wl.q.clone()
-    a = fused(wl, rope)
+    a = fused(wl, rope, q_room)
     b = two_calls(other, rope)
     torch.cuda.synchronize()
     assert torch.equal(wl.q, q0), f"{what}: q changed"
@@ -93,13 +97,28 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("q_room", [True, False], ids=["room", "noroom"])
 @pytest.mark.parametrize("units", ["mfma", "mfma1"])
 @pytest.mark.parametrize("case", CASES, ids=lambda s: f"Hq{s[1]}Hkv{s[2]}D{s[3]}BS{s[4]}{s[6]}")
-def test_fused_rope_step_equals_the_two_calls(case, units):
+def test_fused_rope_step_equals_the_two_calls(case, units, q_room):
+    """With one kv head per wave (mfma1, or the odd Hkv) the step runs the two
+    calls themselves when the workspace has room for the rotated q, and the
+    fused one-head kernel otherwise; both must give the two calls' bits."""
     B, Hq, Hkv, D, BS, lengths, kv = case
     use_kernel(units)
     wl = build(B, Hq, Hkv, D, BS, lengths, kv=kv, seed=B + Hq + D + BS)
-    assert_fused_equals_two_calls(wl, f"{case} {units}")
+    assert_fused_equals_two_calls(wl, f"{case} {units} q_room={q_room}", q_room=q_room)
+
+
+def test_rope_step_workspace_query():
+    """The RoPE step's workspace is the attention call's plus a rotated q."""
+    for B, Hq, Hkv, D, BS, MBS, kvd in [(4, 32, 8, 128, 16, 64, ops.KV_BF16),
+                                        (3, 20, 5, 64, 32, 40, ops.KV_FP8),
+                                        (64, 32, 8, 128, 16, 256, ops.KV_INT8)]:
+        room = (B * Hq * D * 2 + 255) // 256 * 256
+        assert ops.decode_step_rope_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kvd) == \
+            ops.attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kvd, 1) + room
+    assert ops.decode_step_rope_workspace_bytes(4, 32, 8, 96, 16, 64, ops.KV_BF16) == 0
 
 
 def test_fused_rope_step_plain_rope_parameters():
