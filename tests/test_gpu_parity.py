@@ -9,6 +9,7 @@ the dequantised codes).
 from __future__ import annotations
 
 import itertools
+import re
 
 import numpy as np
 import pytest
@@ -195,14 +196,29 @@ def test_zero_length_sequence_gives_zero(kernel):
 
 
 def test_workspace_too_small_is_rejected():
+    """The query is an upper bound (a small call's grid can be smaller than
+    the persistent one); the call names what it needs, rejects 16 bytes
+    less and accepts exactly that."""
     wl = build(2, 8, 2, 64, 16, (5, 40), seed=2, poison=False)
     ws = GS.workspace_for(wl)
-    small = ws[: ws.numel() - 256]
-    with pytest.raises(ops.PkvError) as e:
+
+    def call(n):
         ops.paged_decode_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables,
                                    wl.context_lens, wl.scale, torch.empty_like(wl.q),
-                                   workspace=small)
+                                   workspace=ws[:n])
+
+    with pytest.raises(ops.PkvError) as e:
+        call(256)
     assert e.value.status == -4
+    m = re.search(r"smaller than the (\d+) required", str(e.value))
+    assert m, str(e.value)
+    need = int(m.group(1))
+    assert 256 < need <= ws.numel()
+    with pytest.raises(ops.PkvError) as e:
+        call(need - 16)
+    assert e.value.status == -4
+    call(need)
+    torch.cuda.synchronize()
 
 
 # ------------------------------------------------------------ full configs --
