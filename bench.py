@@ -101,11 +101,11 @@ def measured_traffic(config: str, kernel: str):
     return None
 
 
-def cpu_baseline(wl, budget_s=12.0):
+def cpu_baseline(wl, budget_s=10.0, max_runs=100):
     """The oracle, as it stands, on the host cores: one full step's attention
     over the same batch (after the oracle's own append of the step's tokens,
     in position order), repeated until about `budget_s` of wall time has
-    passed."""
+    passed (at least once, at most `max_runs` times)."""
     import oracle
     from paged_kv_decode_06_amd import workloads as W
 
@@ -137,7 +137,7 @@ def cpu_baseline(wl, budget_s=12.0):
             oracle.paged_decode_attention(q, k, v, wl.block_tables_np, cl, wl.scale, k_scale=ks,
                                           v_scale=vs, nthreads=threads)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_all > budget_s or len(times) >= 5:
+        if time.perf_counter() - t_all > budget_s or len(times) >= max_runs:
             break
     t = sum(times) / len(times)
     return {"value": round(kv_bytes(wl) / t / 1e9, 4), "unit": "GB/s", "cores": threads,
