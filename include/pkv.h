@@ -22,7 +22,9 @@
  *   - Tensors are caller-owned, contiguous, row-major device memory.  The
  *     library keeps no pointer after a call returns and allocates nothing.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
- *     No call synchronises the host with the device.
+ *     No call synchronises the host with the device, except the debug check
+ *     pkv_validate_inputs, so every other call can be captured in a HIP
+ *     graph.
  *   - bf16 means IEEE binary32 truncated to its upper 16 bits (stored as
  *     uint16); e4m3fn is the OCP 8-bit format (bias 7, no infinities, max 448).
  *   - Arguments the host can check (null pointers, unsupported shapes or
@@ -224,6 +226,13 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     int D, int BS, int NB, int MBS, int kv_dtype, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for pkv_decode_step_rope: those of
+ * pkv_paged_attention_workspace_bytes(..., max_q_len = 1) plus room for a
+ * rotated copy of q (B * Hq * D bf16, rounded up to 256 bytes).  0 for an
+ * unsupported shape. */
+size_t pkv_decode_step_rope_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
+                                            int kv_dtype);
+
 /* The decode step with RoPE ("tiny-vllm part 5", the RoPE section, with the
  * frequencies and parameters of pkv_rope_kv_append): q and k_new arrive
  * unrotated; exactly equivalent to
@@ -235,20 +244,13 @@ int pkv_decode_step(const void* q, const void* k_new, const void* v_new, void* k
  * registers and the new key rows before it stores them, so the step is two
  * launches.  Size the workspace with pkv_decode_step_rope_workspace_bytes.
  * When the call serves one kv head per partition wave (odd Hkv, or
- * pkv_select_unit_heads(1)) and Hkv <= 8, the step runs
- * as exactly those two calls instead (three launches; the rotated q goes to
- * the end of the workspace), which is faster there; a workspace of only
+ * pkv_select_unit_heads(1)) and Hkv <= 8, the step runs as exactly those
+ * two calls instead (three launches; the rotated q goes to the end of the
+ * workspace), which is faster there; a workspace of only
  * pkv_paged_attention_workspace_bytes(max_q_len = 1) bytes leaves no room
  * for it and keeps the fused kernel.  The bits are the same either way.
  * D in {64, 128}; other arguments as for pkv_decode_step.  Bad rope
  * parameters give PKV_ERR_SHAPE.  B == 0 is a no-op. */
-/* Workspace bytes for pkv_decode_step_rope: those of
- * pkv_paged_attention_workspace_bytes(..., max_q_len = 1) plus room for a
- * rotated copy of q (B * Hq * D bf16, rounded up to 256 bytes).  0 for an
- * unsupported shape. */
-size_t pkv_decode_step_rope_workspace_bytes(int B, int Hq, int Hkv, int D, int BS, int MBS,
-                                            int kv_dtype);
-
 int pkv_decode_step_rope(const void* q, const void* k_new, const void* v_new, void* k_cache,
                          void* v_cache, float* k_scale, float* v_scale,
                          const int32_t* block_tables, const int32_t* context_lens, float scale,
