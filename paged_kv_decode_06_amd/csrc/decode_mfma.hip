@@ -48,6 +48,7 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
@@ -91,22 +92,30 @@ __device__ __forceinline__ short bf16_bits(float x) {
 }
 
 // Two e4m3fn codes (the low or high half of w) -> two bf16, exactly: every
-// e4m3fn value is a bf16 value, and the gfx950 scaled conversion with scale
-// 1 produces it in one instruction (checked bit for bit against fp8 -> fp32
-// -> bf16 on all 65536 code pairs of both halves; 1.4% faster fp8 partition
-// kernel than the two-step conversion).
-template <bool HIGH>
-__device__ __forceinline__ auto fp8x2_to_bf16(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+// e4m3fn value is a bf16 value.  Two routes give the same bits (checked on
+// all 65536 code pairs of both halves): the gfx950 scaled conversion with
+// scale 1, one instruction, or fp8 -> fp32 pairs then fp32 -> bf16.  Which
+// is faster depends on the instantiation (fp8 workload: the first 1.5%
+// faster with two-head units, 1.5% slower with one head), so the tile
+// widening takes it as a parameter.
+template <bool SCALED, bool HIGH>
+__device__ __forceinline__ bf16x2_t fp8x2_to_bf16(uint32_t w) {
+  if constexpr (SCALED) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH);
+  } else {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HIGH);
+    return bf16x2_t{(__bf16)f[0], (__bf16)f[1]};
+  }
 }
 
 // 16 e4m3fn codes -> 16 bf16 (exact).
+template <bool SCALED>
 __device__ __forceinline__ void fp8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16x8_t& hi) {
   const uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const auto a = fp8x2_to_bf16<false>(w[k]);
-    const auto b = fp8x2_to_bf16<true>(w[k]);
+    const bf16x2_t a = fp8x2_to_bf16<SCALED, false>(w[k]);
+    const bf16x2_t b = fp8x2_to_bf16<SCALED, true>(w[k]);
     bf16x8_t& dst = k < 2 ? lo : hi;
     const int o = (k & 1) * 4;
     dst[o + 0] = a[0];
@@ -133,7 +142,7 @@ __device__ __forceinline__ void q8x16_to_bf16(const uint4 c, bf16x8_t& lo, bf16x
   if constexpr (S::INT8)
     i8x16_to_bf16(c, lo, hi);
   else
-    fp8x16_to_bf16(c, lo, hi);
+    fp8x16_to_bf16<(S::HG > 1)>(c, lo, hi);
 }
 
 // Tile loads: buffer loads off a descriptor for the tile's first byte
@@ -220,8 +229,8 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(const uint2 c) {
   const uint32_t w[2] = {c.x, c.y};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const auto a = fp8x2_to_bf16<false>(w[k]);
-    const auto b = fp8x2_to_bf16<true>(w[k]);
+    const bf16x2_t a = fp8x2_to_bf16<true, false>(w[k]);
+    const bf16x2_t b = fp8x2_to_bf16<true, true>(w[k]);
     r[4 * k + 0] = a[0];
     r[4 * k + 1] = a[1];
     r[4 * k + 2] = b[0];
