@@ -146,6 +146,68 @@ def cpu_baseline(wl, budget_s=10.0, max_runs=100):
                       f"{len(times)} run(s), mean {t:.3f} s per step"}
 
 
+class TimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence so
+    that recording one does not write back and invalidate the caches (HIP's
+    own documentation of the flag: it makes timings between events more
+    accurate).  Bound through ctypes to the HIP runtime already mapped in
+    this process (the one torch and libpkv use), never a second copy."""
+
+    _lib = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def lib(cls):
+        if cls._lib is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            L = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [vp, vp]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            L.hipEventDestroy.argtypes = [vp]
+            for fn in (L.hipEventCreateWithFlags, L.hipEventRecord, L.hipEventElapsedTime,
+                       L.hipEventDestroy):
+                fn.restype = ctypes.c_int
+            cls._lib = L
+        return cls._lib
+
+    def __init__(self, n: int):
+        import ctypes
+        L = self.lib()
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if L.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i: int, stream) -> None:
+        import ctypes
+        if self.lib().hipEventRecord(self.ev[i], ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self.lib().hipEventElapsedTime(ctypes.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.lib().hipEventDestroy(e)
+        self.ev = []
+
+
 def settle(runs, seconds: float) -> int:
     """Keep the GPU busy with the workload's own steps for `seconds` of wall
     time before the warmup steps: clocks ramp under load, and a timed region
@@ -215,16 +277,17 @@ def general_result(args, cfg, wl, dev, nbytes):
             run(Wm + i)
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / K
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        tev = TimingEvents(2 * K)   # (timing-only events: no system-scope fence)
         for i in range(K):
             apps, att = steps[(Wm + i) % copies]
             for a in apps:
                 a()
-            ev[i][0].record(stream)
+            tev.record(2 * i, stream)
             att()
-            ev[i][1].record(stream)
+            tev.record(2 * i + 1, stream)
         torch.cuda.synchronize()
-    att_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    att_ms = float(np.mean([tev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]))
+    tev.close()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (att_ms * 1e-3) / 1e9
     keys, _ = visible_keys(wl)
@@ -367,11 +430,29 @@ def main():
         app, att = split[i % copies]
         return app, att.partition, att.merge
 
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    # (timing-only events: no system-scope fence at each record)
+    tev = TimingEvents(2 * K)
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
         t2 = time.perf_counter()
+        for i in range(K):
+            pre, part, merge = halves(Wm + i)
+            pre()
+            tev.record(2 * i, stream)
+            part()
+            tev.record(2 * i + 1, stream)
+            merge()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+    ms_per_step_events = (t3 - t2) * 1e3 / K
+    part_ms = [tev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]
+    part_avg_ms = float(np.mean(part_ms))
+    tev.close()
+    # the same with torch's default events (a system-scope fence at each
+    # record), reported beside it
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    with torch.cuda.stream(stream):
         for i in range(K):
             pre, part, merge = halves(Wm + i)
             pre()
@@ -379,11 +460,8 @@ def main():
             part()
             ev1[i].record(stream)
             merge()
-        torch.cuda.synchronize()
-        t3 = time.perf_counter()
-    ms_per_step_events = (t3 - t2) * 1e3 / K
-    part_ms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
-    part_avg_ms = float(np.mean(part_ms))
+    torch.cuda.synchronize()
+    part_avg_ms_fenced = float(np.mean([a.elapsed_time(b) for a, b in zip(ev0, ev1)]))
 
     # breakdown of one step, each launch between its own pair of events
     nb = min(K, 50)
@@ -504,6 +582,7 @@ def main():
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
             "ms_per_step_with_partition_events": round(ms_per_step_events, 5),
             "partition_us_mean": round(part_avg_ms * 1e3, 2),
+            "partition_us_mean_default_events": round(part_avg_ms_fenced * 1e3, 2),
             "partition_us_median": round(part_med_us, 2),
             "merge_us_median": round(merge_us, 2),
             "kv_append_us_median": round(app_us, 2) if args.step == "two-call" else None,
