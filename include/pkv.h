@@ -184,7 +184,8 @@ int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cac
  *   pkv_paged_decode_attention; a query that sees no key gets 0.
  *   q, out  [total_q, Hq, D] bf16; q_start [B + 1] int32 (device), with
  *   q_len_b <= max_q_len (larger ones are clamped); G * max_q_len <= 16
- *   (one wave serves all of a sequence's queries of one kv head).  Other
+ *   (one wave serves all of a sequence's queries of its kv heads: two
+ *   adjacent ones when 2 * G * max_q_len <= 16, else one).  Other
  *   arguments as for pkv_paged_decode_attention; the workspace comes from
  *   pkv_paged_attention_workspace_bytes with the same max_q_len.
  * Always runs the MFMA partition kernel (the VALU variant serves one query
@@ -301,10 +302,11 @@ int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
  * call (a unit of adjacent kv heads whose rows lie side by side in every
  * cache row, so a wave streams one contiguous run of unit * D * elem bytes
  * per token): 2 when Hkv is even and the wider kernel fits two workgroups
- * on a compute unit, else 1; always 1 for the VALU kernel and for calls
- * with several queries or a window.  The result does not depend on it
- * beyond floating-point summation order.  0 if unsupported.
- * Informational. */
+ * on a compute unit, else 1; always 1 for the VALU kernel.  (The
+ * generalised call, pkv_paged_attention, takes the same unit when its
+ * 2 * G * max_q_len columns fit the 16 of the MFMA, else 1.)  The result
+ * does not depend on it beyond floating-point summation order.  0 if
+ * unsupported.  Informational. */
 int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
 
 /* mode 0 (default): units as above; mode 1: one kv head per wave always.

@@ -409,13 +409,14 @@ __device__ __forceinline__ void rope_rotate(const AttnParams& p, int pos, int la
 }
 
 // GEN: the generalised call (several queries per sequence, a window); the
-// decode instantiations (GEN = false) carry none of its per-lane state and
-// may serve several kv heads per wave (S::HG).  ROPE: the decode step with
-// RoPE (instantiated apart, so that the other kernels do not carry its
-// registers).
+// decode instantiations (GEN = false) carry none of its per-lane state.
+// Both may serve several kv heads per wave (S::HG; the generalised call when
+// HG * G * max_q <= 16).  ROPE: the decode step with RoPE (instantiated
+// apart, so that the other kernels do not carry its registers).
 //
-// Units of HG > 1 kv heads: the unit's HG * G query heads are the 16
-// columns, column n reading kv head `mem` = n / G of the unit.  The scores
+// Units of HG > 1 kv heads: the unit's HG * G query heads (times the
+// queries per sequence) are the columns, column n reading kv head
+// `mem` = (n % UG) / G of the unit.  The scores
 // run one MFMA chain per kv head of the unit (K of that head times every
 // column's q) and each column keeps its own head's chain; the output runs
 // O^T += V_j^T P_j^T per head j with P_j = P restricted to head j's columns,
@@ -427,7 +428,6 @@ void mfma_partition_kernel(const AttnParams p) {
   constexpr int NI = S::NI, RPI = S::RPI, LPR = S::LPR;
   constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
   constexpr int NP = NewRows<S>::NP, CH = NewRows<S>::CH;
-  static_assert(!GEN || HG == 1, "the generalised call serves one kv head per wave");
   static_assert(!(GEN && ROPE), "RoPE is fused into the decode step only");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -452,9 +452,10 @@ void mfma_partition_kernel(const AttnParams p) {
 
   const int n = lane & 15;        // column of S^T and O^T (a query head); K row of the A operand
   const int r = lane >> 4;        // 4-token group of S^T rows; 4-dim group of O^T rows
-  // kv head of the unit that column n reads (columns past the unit's UG
-  // heads, unused when UG < 16, take the last one: their loads stay in the unit)
-  const int mem = HG > 1 ? min(n / G, HG - 1) : 0;
+  // kv head of the unit that column n reads: column n is query n / UG, head
+  // n % UG of the unit (columns past the used ones also land on a head of
+  // the unit, so their loads stay in it)
+  const int mem = HG > 1 ? (n % UG) / G : 0;
   const WorkSplit split = make_split(total, p.total_waves);
   const int64_t row_bytes = (int64_t)Hkv * RB;
   // this lane's 16-byte chunk of a unit row, for the global loads: a 32-bit
@@ -487,7 +488,7 @@ void mfma_partition_kernel(const AttnParams p) {
     const int32_t* bt_row = p.block_tables + (int64_t)b * p.MBS;
     const int64_t head_off = (int64_t)g0 * RB;
     // column n: query token n / UG of the sequence, query head g0 G + n % UG
-    // (GEN: UG = G; decode: one query, the unit's UG heads)
+    // (decode: one query, the unit's UG heads)
     const int ql = GEN ? seq_queries(p, b) : 1;
     const int ncol = UG * ql;
     const int col_q = n / UG, col_h = g0 * G + n % UG;
@@ -753,7 +754,7 @@ void mfma_partition_kernel(const AttnParams p) {
 }
 
 // Calls f(MfmaShape<D, BS, G, kind, hg>{}) for the combination given at run
-// time: hg = 1, or hg = kUnitHeads(G) (the decode instantiations only).
+// time: hg = 1, or hg = kUnitHeads(G).
 // Two heads per wave measured best on every decode workload (B64 / B4 /
 // B256 / B128 bf16, fp8 and int8 shapes): 2-4% faster steps than one head
 // (fp8: 6%), while four heads lost on bf16 D = 128 G = 4 (3% slower steps:
@@ -801,8 +802,9 @@ static size_t mfma_lds_total(int B, int D, int hg) {
   return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
 
-// hg = 1: the decode and the generalised instantiations are held to the
-// same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves both.
+// The decode and the generalised instantiations of one unit size are held to
+// the same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves
+// both (the smaller of their occupancies, should registers ever differ).
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg) {
   int blocks = 0, blocks_gen = 0;
   const size_t lds = mfma_lds_total(B, D, hg);
@@ -811,12 +813,9 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S, false>,
                                                      kAttnBlockThreads, lds) != hipSuccess)
       blocks = 0;
-    blocks_gen = blocks;
-    if constexpr (S::HG == 1) {
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
-                                                       kAttnBlockThreads, lds) != hipSuccess)
-        blocks_gen = 0;
-    }
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
+                                                     kAttnBlockThreads, lds) != hipSuccess)
+      blocks_gen = 0;
   });
   return ok ? (blocks < blocks_gen ? blocks : blocks_gen) : 0;
 }
@@ -825,16 +824,14 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
                                  hipStream_t stream) {
   const size_t lds = mfma_lds_total(p.B, D, p.hg);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
-  if (gen && (p.hg != 1 || p.rope)) return hipErrorInvalidValue;
-  if (p.hg < 1 || p.Hkv % p.hg != 0) return hipErrorInvalidValue;
+  if (gen && p.rope) return hipErrorInvalidValue;
+  if (p.hg < 1 || p.Hkv % p.hg != 0 || p.hg * G * p.max_q > 16) return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);
-    if constexpr (S::HG == 1) {
-      if (gen) {
-        hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks),
-                           dim3(kAttnBlockThreads), lds, stream, p);
-        return;
-      }
+    if (gen) {
+      hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks),
+                         dim3(kAttnBlockThreads), lds, stream, p);
+      return;
     }
     if (p.rope)
       hipLaunchKernelGGL((mfma_partition_kernel<S, false, true>), dim3(blocks),

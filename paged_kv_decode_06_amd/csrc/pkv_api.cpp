@@ -107,14 +107,21 @@ std::atomic<int>& unit_heads_flag() {
   return flag;
 }
 
-// A wave of the MFMA kernel serves hg adjacent kv heads when the call is
-// decode-shaped (one query per sequence, no window), hg divides Hkv and the
-// wider instantiation still fits two workgroups on a CU; otherwise one.
-int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, int B, bool gen) {
-  if (path != pkv::AttnPath::kMfma || gen || unit_heads_flag().load(std::memory_order_relaxed) == 1)
+// The most columns (kv heads per wave * G * max_q) one partition wave
+// serves: the 16 MFMA columns.
+constexpr int kMaxCols = 16;
+
+// A wave of the MFMA kernel serves hg adjacent kv heads when hg divides
+// Hkv, the unit's columns (hg * G per query, max_q queries per sequence)
+// fit the 16 of the MFMA, and the wider instantiation still fits two
+// workgroups on a CU; otherwise one.
+int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, int B, bool gen,
+               int max_q = 1) {
+  (void)gen;
+  if (path != pkv::AttnPath::kMfma || unit_heads_flag().load(std::memory_order_relaxed) == 1)
     return 1;
   const int hg = pkv::mfma_unit_heads(G);
-  if (hg <= 1 || Hkv % hg != 0) return 1;
+  if (hg <= 1 || Hkv % hg != 0 || hg * G * max_q > kMaxCols) return 1;
   int dev;
   if (current_device(&dev) != 0) return 1;
   return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg) >= 2 ? hg : 1;
@@ -142,9 +149,6 @@ struct QueryOpts {
   int window = 0;
   bool general = false;   // the generalised call: always the MFMA kernel
 };
-
-// The largest G * max_q one partition wave serves (the 16 MFMA columns).
-constexpr int kMaxCols = 16;
 
 int check_query_opts(const QueryOpts& o, int G) {
   if (o.max_q < 1) return fail(PKV_ERR_SHAPE, "max_q_len=%d must be at least 1", o.max_q);
@@ -197,7 +201,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
   const pkv::AttnPath path = path_for(opts);
   const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
-  const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen);
+  const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
@@ -335,7 +339,7 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
   size_t need = 0;
   for (int gen = general ? 1 : 0; gen >= 0; --gen) {
     if (gen == 0 && max_q > 1) continue;
-    const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0);
+    const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0, max_q);
     const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
     if (blocks <= 0) return 0;
     const int waves = blocks * pkv::kAttnWavesPerBlock;

@@ -35,8 +35,8 @@ struct AttnParams {
   int sinks, window;
   // kv heads one partition wave serves together (a unit of adjacent kv
   // heads): the work axis runs over (sequence, unit, page), U = Hkv / hg
-  // units per sequence.  Above 1 only for one query per sequence and no
-  // window (then cols = hg * G); the VALU kernel always takes 1.
+  // units per sequence, and cols = hg * G * max_q <= 16.  The VALU kernel
+  // always takes 1.
   int hg;
   int total_waves;      // persistent waves of the partition grid
   // workspace (see workspace_layout)
@@ -107,9 +107,9 @@ int valu_blocks_per_cu(int D, int BS, int G, int kind, int B);
 // (the MFMA launch takes the unit size from p.hg)
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream);
-// hg = 1: the occupancy both instantiations (decode and generalised) reach;
-// hg > 1: that of the decode instantiation with hg kv heads per wave (0 if
-// there is none: mfma_unit_heads(G) is the one hg above 1 that exists).
+// The occupancy both instantiations (decode and generalised) with hg kv
+// heads per wave reach (0 if there is none: mfma_unit_heads(G) is the one hg
+// above 1 that exists).
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg);
 int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.

@@ -148,3 +148,65 @@ def test_units_that_do_not_divide_fall_back(Hq, Hkv, hg):
     torch.cuda.synchronize()
     host.append()
     GS.assert_attention_close(GS.bf16_to_f64(out), host.attention(), wl.kv_dtype, f"Hkv{Hkv}")
+
+
+# ------------------------------------------------ the generalised call --
+# Two-head units serve the generalised call too when 2 G max_q <= 16.
+GEN_CASES = [
+    # (B, Hq, Hkv, D, BS, lengths, q_lens, kv, sinks, window)
+    (3, 16, 4, 128, 16, (50, 333, 1200), (2, 1, 2), "bf16", 0, 0),        # G 4, 2 queries
+    (4, 32, 8, 128, 16, (100, 700, 1500, 9), (1, 1, 1, 1), "bf16", 16, 256),  # window decode
+    (3, 16, 8, 64, 32, (40, 500, 2000), (4, 4, 3), "fp8", 0, 0),         # G 2, 4 queries
+    (3, 8, 8, 128, 16, (17, 300, 1100), (8, 5, 8), "int8", 16, 128),     # G 1, 8, window
+]
+
+
+def general_pages(wl: W.Workload) -> int:
+    """Pages on the work axis: each sequence's sink and window pages."""
+    n = 0
+    for L, ql in zip(wl.lengths, wl.q_lens):
+        L, ql = int(L), int(ql)
+        pe = (L + wl.BS - 1) // wl.BS
+        if wl.window <= 0:
+            n += pe
+            continue
+        lo = max(L - ql - wl.window + 1, 0)
+        pw, ps = lo // wl.BS, min((wl.sinks + wl.BS - 1) // wl.BS, pe)
+        n += pe if pw <= ps else ps + (pe - pw)
+    return n
+
+
+@pytest.mark.parametrize("case", GEN_CASES, ids=lambda s: f"G{s[1] // s[2]}q{max(s[6])}{s[7]}w{s[9]}")
+def test_general_units_equal_one_head_bit_for_bit(case):
+    """Same precondition as the decode test: every piece one page in both
+    grids, so both split the work alike."""
+    B, Hq, Hkv, D, BS, lengths, q_lens, kv, sinks, window = case
+    from tests.test_gpu_general import build as build_general
+    wl = build_general(B, Hq, Hkv, D, BS, lengths, q_lens, kv=kv, seed=B + Hq + D,
+                       sinks=sinks, window=window)
+    assert 2 * (Hq // Hkv) * max(q_lens) <= 16
+    pages = general_pages(wl)
+    assert pages * Hkv <= waves(wl) and pages * Hkv // 2 <= waves(wl)
+    host = GS.GeneralHost(wl)                 # the oracle's view, before the GPU appends
+    GS.append_in_order(wl)
+    a = GS.general_step(wl, append=False).clone()
+    use_kernel("mfma1")
+    assert pages * Hkv <= waves(wl)
+    b = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(b))
+    host.append()
+    GS.assert_attention_close(GS.bf16_to_f64(a)[host.rows], host.attention(), kv, f"{case}")
+
+
+def test_general_one_query_equals_decode_with_units():
+    """One query, no window: the generalised call is the decode call bit for
+    bit with two-head units in both (same grid, same split)."""
+    from tests.test_gpu_general import build as build_general
+    wl = build_general(5, 32, 8, 128, 16, (1, 17, 300, 2000, 4096), (1,) * 5, seed=3)
+    assert unit_heads(wl) == 2
+    GS.append_in_order(wl)
+    a = GS.gpu_step(wl, append=False)
+    b = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(b))
