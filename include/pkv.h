@@ -35,7 +35,9 @@
  *     MBS * BS, slots must be unique.  The kernels clamp out-of-range ids and
  *     lengths so that a broken contract gives wrong numbers, never an
  *     out-of-bounds access.
- *   - Supported: D in {64, 128}; BS in {16, 32}; Hq / Hkv in {1, 2, 4, 8}.
+ *   - Supported: D in {64, 128}; BS in {16, 32}; Hq / Hkv in {1, 2, 4, 8,
+ *     16} (16: the MFMA partition kernel only, which such a call runs
+ *     whatever pkv_select_partition_kernel chose).
  *
  * Layouts:
  *   q, out            [B, Hq, D]           bf16

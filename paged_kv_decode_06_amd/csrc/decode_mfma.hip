@@ -770,7 +770,7 @@ struct ShapeKey {
 template <class F>
 bool dispatch_mfma(int D, int BS, int G, int kind, int hg, F&& f) {
   bool ok = false;
-  dispatch_shapes<ShapeKey>(D, BS, G, kind, [&](auto key) {
+  auto one = [&](auto key) {
     using Kt = decltype(key);
     constexpr int H = kUnitHeads(Kt::G);
     if (hg == 1) {
@@ -780,7 +780,17 @@ bool dispatch_mfma(int D, int BS, int G, int kind, int hg, F&& f) {
       f(MfmaShape<Kt::D, Kt::BS, Kt::G, Kt::K, H>{});
       ok = true;
     }
-  });
+  };
+  if (G == 16) {   // groups of 16 (this kernel only): one kv head's queries fill the columns
+#define PKV_G16(d, bs, k) \
+  if (D == d && BS == bs && kind == k) one(ShapeKey<d, bs, 16, k>{});
+#define PKV_G16_K(d, bs) PKV_G16(d, bs, kKvBf16) PKV_G16(d, bs, kKvFp8) PKV_G16(d, bs, kKvInt8)
+    PKV_G16_K(64, 16) PKV_G16_K(64, 32) PKV_G16_K(128, 16) PKV_G16_K(128, 32)
+#undef PKV_G16_K
+#undef PKV_G16
+    return ok;
+  }
+  dispatch_shapes<ShapeKey>(D, BS, G, kind, one);
   return ok;
 }
 

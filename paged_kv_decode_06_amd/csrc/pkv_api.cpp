@@ -82,9 +82,11 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, i
   return n;
 }
 
+// (G = 16, one kv head's queries filling the 16 MFMA columns, runs on the
+// MFMA kernel only: see path_for)
 bool supported(int D, int BS, int G, int kv_dtype) {
   return (D == 64 || D == 128) && (BS == 16 || BS == 32) &&
-         (G == 1 || G == 2 || G == 4 || G == 8) &&
+         (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
          (kv_dtype == PKV_KV_BF16 || kv_dtype == PKV_KV_FP8_E4M3FN || kv_dtype == PKV_KV_INT8);
 }
 
@@ -161,8 +163,10 @@ int check_query_opts(const QueryOpts& o, int G) {
   return PKV_OK;
 }
 
-pkv::AttnPath path_for(const QueryOpts& o) {
-  return o.general ? pkv::AttnPath::kMfma : pkv::attn_path();
+// The partition kernel a call runs: the selected one, except that the
+// generalised call and groups of 16 always run the MFMA kernel.
+pkv::AttnPath path_for(const QueryOpts& o, int G) {
+  return o.general || G > 8 ? pkv::AttnPath::kMfma : pkv::attn_path();
 }
 
 int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -199,7 +203,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
     return fail(PKV_ERR_ALIGN, "k_new and v_new must be 16-byte aligned");
   if (q8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3u))
     return fail(PKV_ERR_ALIGN, "scales must be 4-byte aligned");
-  const pkv::AttnPath path = path_for(opts);
+  const pkv::AttnPath path = path_for(opts, G);
   const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
@@ -305,7 +309,7 @@ int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
   if (B < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || B > pkv::kMaxBatch) return 0;
   const int G = Hq / Hkv;
   if (!supported(D, BS, G, kv_dtype)) return 0;
-  const pkv::AttnPath path = pkv::attn_path();
+  const pkv::AttnPath path = path_for(QueryOpts{}, G);
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, false);
   return attention_blocks(path, D, BS, G, kv_dtype, B, hg) * pkv::kAttnWavesPerBlock;
 }
@@ -314,7 +318,7 @@ int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
   if (B < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || B > pkv::kMaxBatch) return 0;
   const int G = Hq / Hkv;
   if (!supported(D, BS, G, kv_dtype)) return 0;
-  return unit_heads(pkv::attn_path(), D, BS, G, Hkv, kv_dtype, B, false);
+  return unit_heads(path_for(QueryOpts{}, G), D, BS, G, Hkv, kv_dtype, B, false);
 }
 
 int pkv_select_unit_heads(int mode) {
@@ -333,7 +337,7 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
   if (!supported(D, BS, G, kv_dtype) || B > pkv::kMaxBatch || G * max_q > kMaxCols) return 0;
   QueryOpts o;
   o.general = general;
-  const pkv::AttnPath path = path_for(o);
+  const pkv::AttnPath path = path_for(o, G);
   // the general call is decode-shaped or not depending on q_start and the
   // window: size for both unit choices
   size_t need = 0;

@@ -68,7 +68,8 @@ def test_attention_argument_checks_fail_before_launch(lib):
     assert attn(lib, Hq=6, Hkv=4) == -2            # Hq % Hkv != 0
     assert attn(lib, D=96) == -3                   # unsupported head dim
     assert attn(lib, BS=8) == -3                   # unsupported block size
-    assert attn(lib, Hq=32, Hkv=2) == -3           # G = 16
+    assert attn(lib, Hq=64, Hkv=2) == -3           # G = 32
+    assert attn(lib, Hq=24, Hkv=8) == -3           # G = 3
     assert attn(lib, kv=7) == -3
     assert attn(lib, kv=1) == -1                   # fp8 without scales
     assert attn(lib, ks=128, vs=144) == -2         # bf16 with scales

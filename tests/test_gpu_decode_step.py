@@ -87,7 +87,7 @@ def test_step_equals_two_calls_every_variant(kernel):
     """Every (D, BS, G, dtype) instantiation; lengths 1 and BS + 1 put the new
     token at offset 0 (it opens a block and, for fp8, sets the scale), the
     others put it mid-block and on the last offset of a block."""
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8, 16),
                                           ("bf16", "fp8", "int8")):
         Hkv = 4
         wl = build(5, Hkv * G, Hkv, D, BS, (1, BS + 1, 2 * BS, 9 * BS + 5, 3 * BS - 1), kv=kv,

@@ -55,6 +55,8 @@ CASES = [
     (2, 8, 2, 64, 16, (50, 400), (4, 2), "fp8", 1, 33),
     (3, 16, 4, 128, 32, (40, 700, 2000), (2, 4, 3), "int8", 0, 0),
     (2, 32, 8, 128, 16, (600, 3000), (4, 1), "int8", 8, 300),
+    (3, 128, 8, 128, 16, (700, 1500, 3000), (1, 1, 1), "bf16", 4, 256),    # G = 16, window
+    (2, 64, 4, 64, 32, (500, 2000), (1, 1), "fp8", 0, 0),                  # G = 16
 ]
 
 
@@ -68,7 +70,7 @@ def test_general_attention_matches_oracle(case):
 def test_every_variant_with_queries_and_a_window():
     """Every (D, BS, G, dtype) instantiation with the most queries it takes."""
     import itertools
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8, 16),
                                           ("bf16", "fp8", "int8")):
         Hkv = 2
         q = 16 // G

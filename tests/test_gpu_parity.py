@@ -106,6 +106,9 @@ SMALL = [
     (3, 16, 2, 128, 32, (1, 32, 1025), "int8"),
     (2, 8, 2, 64, 16, (16, 977), "int8"),
     (3, 32, 8, 128, 16, (2, 96, 3000), "int8"),
+    (3, 128, 8, 128, 16, (5, 700, 2500), "bf16"),     # G = 16 (MFMA kernel only)
+    (2, 64, 4, 128, 32, (33, 1500), "fp8"),
+    (2, 32, 2, 64, 16, (16, 977), "int8"),
 ]
 
 
@@ -119,7 +122,7 @@ def test_step_matches_oracle_small(shape, kernel):
 def test_all_supported_variants_run(kernel):
     """Every (D, BS, G, dtype) instantiation against the oracle (Hkv = 4: the
     decode call serves 2 kv heads per wave, or one with "mfma1")."""
-    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8),
+    for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8, 16),
                                           ("bf16", "fp8", "int8")):
         Hkv = 4
         wl = build(3, Hkv * G, Hkv, D, BS, (1, BS + 3, 9 * BS + 5), kv=kv, seed=D + BS + G)

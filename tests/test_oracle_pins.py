@@ -52,6 +52,7 @@ SHAPES = [
     (2, 8, 1, 128, 32, (33, 97), "bf16"),            # G = 8 (multi-query)
     (3, 16, 2, 128, 32, (1, 32, 65), "fp8"),         # fp8, G = 8
     (2, 8, 2, 64, 16, (16, 77), "fp8"),              # fp8, G = 4
+    (2, 32, 2, 64, 16, (9, 70), "bf16"),             # G = 16
 ]
 
 
