@@ -185,9 +185,12 @@ int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cac
  *   softmax(scale <q, K_j>) weighted sum of V_j over the keys it sees, as in
  *   pkv_paged_decode_attention; a query that sees no key gets 0.
  *   q, out  [total_q, Hq, D] bf16; q_start [B + 1] int32 (device), with
- *   q_len_b <= max_q_len (larger ones are clamped); G * max_q_len <= 16
- *   (one wave serves all of a sequence's queries of its kv heads: two
- *   adjacent ones when 2 * G * max_q_len <= 16, else one).  Other
+ *   q_len_b <= max_q_len (larger ones are clamped); G * max_q_len <= 32
+ *   (one wave serves all of a sequence's queries of its kv heads, as the
+ *   16-column tiles of its matrix products: two adjacent kv heads in one
+ *   tile when 2 * G * max_q_len <= 16, else one kv head in one tile, or in
+ *   two when G * max_q_len > 16; larger counts return PKV_ERR_UNSUPPORTED
+ *   and a workspace query of 0).  Other
  *   arguments as for pkv_paged_decode_attention; the workspace comes from
  *   pkv_paged_attention_workspace_bytes with the same max_q_len.
  * Always runs the MFMA partition kernel (the VALU variant serves one query

@@ -18,9 +18,11 @@
 namespace pkv {
 namespace {
 
-// Merge, one workgroup per (sequence, unit) run: the run's shares are rows
-// k0 + seg .. k1 + seg, each holding the unit's `cols` columns.  Thread t
-// owns dims 4 (t % TPR) .. + 3 of column t / TPR and folds in every share of
+// Merge, one workgroup per (sequence, unit) run and 16 columns: the run's
+// shares are rows k0 + seg .. k1 + seg, each holding the unit's `cols`
+// columns (more than 16: a second workgroup, blockIdx.y = 1, takes columns
+// 16..).  Thread t owns dims 4 (t % TPR) .. + 3 of column 16 blockIdx.y +
+// t / TPR and folds in every share of
 // the run itself, kBatch at a time: each share's (m, l) and o are loaded
 // together (one wait on memory per batch) and the running max is rescaled
 // when a batch brings a larger m.  The run's prefix sums and split are read
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams 
   const int U = p.Hkv / p.hg;
   const int seg = blockIdx.x;                  // b U + u
   const int b = seg / U, u = seg % U;
-  const int n = threadIdx.x / TPR;             // column
+  const int n = 16 * blockIdx.y + threadIdx.x / TPR;   // column
   const int d4 = (threadIdx.x % TPR) * 4;
   const int C = p.cols;
   const int UG = p.hg * G;
@@ -235,13 +237,14 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  // (a workgroup per run: cols <= 16 columns of D / 4 threads)
-  const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)));
-  if (p.cols < 1 || p.cols > 16) return hipErrorInvalidValue;
+  // (a workgroup per run and 16 columns, D / 4 threads a column)
+  if (p.cols < 1 || p.cols > 32) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)), (unsigned)((p.cols + 15) / 16));
+  const int wcols = p.cols < 16 ? p.cols : 16;
   if (D == 128)
-    hipLaunchKernelGGL(merge_seg_kernel<128>, grid, dim3(p.cols * 32), 0, stream, p, G);
+    hipLaunchKernelGGL(merge_seg_kernel<128>, grid, dim3(wcols * 32), 0, stream, p, G);
   else if (D == 64)
-    hipLaunchKernelGGL(merge_seg_kernel<64>, grid, dim3(p.cols * 16), 0, stream, p, G);
+    hipLaunchKernelGGL(merge_seg_kernel<64>, grid, dim3(wcols * 16), 0, stream, p, G);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

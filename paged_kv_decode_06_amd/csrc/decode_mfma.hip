@@ -421,14 +421,23 @@ __device__ __forceinline__ void rope_rotate(const AttnParams& p, int pos, int la
 // column's q) and each column keeps its own head's chain; the output runs
 // O^T += V_j^T P_j^T per head j with P_j = P restricted to head j's columns,
 // so every column sums only its own head's values.
-template <class S, bool GEN, bool ROPE = false>
-__global__ __launch_bounds__(kAttnBlockThreads) __attribute__((amdgpu_waves_per_eu(S::WPE, S::WPE)))
+//
+// NCT: 16-column tiles a wave serves.  The generalised call with one kv head
+// per wave takes up to 32 columns (G * max_q <= 32) as two tiles: column
+// c = 16 ct + n of tile ct.  Both tiles' score and output products take the
+// same K and V operands, read from LDS once, so the cache is still streamed
+// once; each tile keeps its own q operands, O^T accumulators and softmax
+// state.
+template <class S, bool GEN, bool ROPE = false, int NCT = 1>
+__global__ __launch_bounds__(kAttnBlockThreads)
+__attribute__((amdgpu_waves_per_eu(NCT > 1 ? 2 : S::WPE, NCT > 1 ? 2 : S::WPE)))
 void mfma_partition_kernel(const AttnParams p) {
   constexpr int D = S::D, BS = S::BS, G = S::G, RB = S::RB, HG = S::HG, UG = S::UG;
   constexpr int NI = S::NI, RPI = S::RPI, LPR = S::LPR;
   constexpr int NKK = S::NKK, NBN = S::NBN, SUB = S::SUB, PITCH = S::PITCH;
   constexpr int NP = NewRows<S>::NP, CH = NewRows<S>::CH;
   static_assert(!(GEN && ROPE), "RoPE is fused into the decode step only");
+  static_assert(NCT == 1 || (NCT == 2 && GEN && HG == 1), "two column tiles: generalised, one head");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
@@ -491,27 +500,35 @@ void mfma_partition_kernel(const AttnParams p) {
     // (decode: one query, the unit's UG heads)
     const int ql = GEN ? seq_queries(p, b) : 1;
     const int ncol = UG * ql;
-    const int col_q = n / UG, col_h = g0 * G + n % UG;
     const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;   // first q / out row
     const SeqRange sr = GEN ? seq_range(L, ql, p.sinks, p.window, BS) : SeqRange{0, 0, 0};
     auto table_page = [&](int j) { return !GEN || j < sr.ps ? j : j + sr.gap; };
-    // keys column n sees: j <= lim_n (bottom-right causal), and with a window
-    // j >= lo_n or j < sinks
-    const int lim_n = n < ncol ? L - ql + col_q : -1;
-    const int lo_n = lim_n - p.window + 1;
+    // column c = 16 ct + n of tile ct: query c / UG, query head g0 G + c % UG.
+    // Keys it sees: j <= lim (bottom-right causal), and with a window j >= lo
+    // or j < sinks.
+    int col_q[NCT], col_h[NCT], lim_n[NCT], lo_n[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + n;
+      col_q[ct] = c / UG;
+      col_h[ct] = g0 * G + c % UG;
+      lim_n[ct] = c < ncol ? L - ql + col_q[ct] : -1;
+      lo_n[ct] = lim_n[ct] - p.window + 1;
+    }
     const bool windowed = GEN && p.window > 0;
     const int gap_end = L - ql - p.window + 1;    // keys in [sinks, gap_end) no query sees
 
     // q of the columns as the B operand: element i of k-step kk is head dim
     // 32 kk + 8 r + i, the same dims the K operand's element i holds
-    bf16x8_t qB[NKK];
-    {
-      const uint16_t* qrow = qp + ((int64_t)(r0 + col_q) * p.Hq + col_h) * D + 8 * r;
+    bf16x8_t qB[NCT][NKK];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint16_t* qrow = qp + ((int64_t)(r0 + col_q[ct]) * p.Hq + col_h[ct]) * D + 8 * r;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (n < ncol) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
-        qB[kk] = __builtin_bit_cast(bf16x8_t, v);
+        if (16 * ct + n < ncol) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+        qB[ct][kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
     // The decode step's new rows when this piece holds the run's last page
@@ -535,14 +552,19 @@ void mfma_partition_kernel(const AttnParams p) {
     if (lane < min(kWave, pc.j1 - pc.j0)) bt_first = bt_row[table_page(pc.j0 + lane)];
     // (RoPE here, with those loads in flight: inside the chunk or tile loop
     // it raised the loop's registers and measured slower)
-    if constexpr (ROPE) rope_rotate<S>(p, L_in - 1, lane, r, tile, qB, new_part, has_new);
+    if constexpr (ROPE) rope_rotate<S>(p, L_in - 1, lane, r, tile, qB[0], new_part, has_new);
     float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: head mem's last-block scales after the append
 
-    float4_t O[NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
+    float4_t O[NCT][NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
+    float m_run[NCT];       // running max of column n (exp2 domain)
+    float l_run[NCT];       // this lane's share of column n's sum
 #pragma unroll
-    for (int nb = 0; nb < NBN; ++nb) O[nb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -FLT_MAX;   // running max of column n (exp2 domain)
-    float l_run = 0.0f;       // this lane's share of column n's sum
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb) O[ct][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      m_run[ct] = -FLT_MAX;
+      l_run[ct] = 0.0f;
+    }
 
     for (int jc = pc.j0; jc < pc.j1; jc += kWave) {
       const int nchunk = min(kWave, pc.j1 - jc);
@@ -636,62 +658,72 @@ void mfma_partition_kernel(const AttnParams p) {
           __builtin_amdgcn_sched_barrier(0);   // keep the V loads behind the K wait
           issue(vc, base, vb);
         }
-        float4_t s;
+        float4_t s[NCT];
         {
-          float4_t sh[HG];   // one chain per kv head of the unit
+          float4_t sh[NCT][HG];   // one chain per kv head of the unit
 #pragma unroll
-          for (int j = 0; j < HG; ++j) sh[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int j = 0; j < HG; ++j) sh[ct][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
             for (int j = 0; j < HG; ++j) {
               const bf16x8_t a =
                   *reinterpret_cast<const bf16x8_t*>(tile + k_rd + 2 * D * j + 64 * kk);
-              sh[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[kk], sh[j], 0, 0, 0);
-            }
-          s = sh[0];
 #pragma unroll
-          for (int j = 1; j < HG; ++j)
-            if (mem == j) s = sh[j];
+              for (int ct = 0; ct < NCT; ++ct)
+                sh[ct][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qB[ct][kk], sh[ct][j], 0, 0, 0);
+            }
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            s[ct] = sh[ct][0];
+#pragma unroll
+            for (int j = 1; j < HG; ++j)
+              if (mem == j) s[ct] = sh[ct][j];
+          }
         }
         const float c = S::Q8 ? p.scale_log2 * ksc : p.scale_log2;
-        // rows past a_rel are in column n's future (decode: past the history)
-        const int a_rel = GEN ? lim_n - tok0 : live - 1;
+        short4_t pb[NCT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[i] *= c;
-          if (4 * r + i > a_rel) s[i] = -INFINITY;
-        }
-        if (windowed) {
-          const int lo_rel = lo_n - tok0, sk_rel = p.sinks - tok0;
+        for (int ct = 0; ct < NCT; ++ct) {
+          // rows past a_rel are in column n's future (decode: past the history)
+          const int a_rel = GEN ? lim_n[ct] - tok0 : live - 1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (4 * r + i < lo_rel && 4 * r + i >= sk_rel) s[i] = -INFINITY;
-        }
+          for (int i = 0; i < 4; ++i) {
+            s[ct][i] *= c;
+            if (4 * r + i > a_rel) s[ct][i] = -INFINITY;
+          }
+          if (windowed) {
+            const int lo_rel = lo_n[ct] - tok0, sk_rel = p.sinks - tok0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * r + i < lo_rel && 4 * r + i >= sk_rel) s[ct][i] = -INFINITY;
+          }
 
-        // online softmax, one max per column n
-        float pm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        pm = fmaxf(pm, __shfl_xor(pm, 16));
-        pm = fmaxf(pm, __shfl_xor(pm, 32));
-        if (__builtin_amdgcn_ballot_w64(pm > m_run) != 0) {
-          const float m_new = fmaxf(m_run, pm);
-          const float alpha = fast_exp2(m_run - m_new);
-          m_run = m_new;
-          l_run *= alpha;
-          // O^T columns are this lane's column: its own factor
+          // online softmax, one max per column n
+          float pm = fmaxf(fmaxf(s[ct][0], s[ct][1]), fmaxf(s[ct][2], s[ct][3]));
+          pm = fmaxf(pm, __shfl_xor(pm, 16));
+          pm = fmaxf(pm, __shfl_xor(pm, 32));
+          if (__builtin_amdgcn_ballot_w64(pm > m_run[ct]) != 0) {
+            const float m_new = fmaxf(m_run[ct], pm);
+            const float alpha = fast_exp2(m_run[ct] - m_new);
+            m_run[ct] = m_new;
+            l_run[ct] *= alpha;
+            // O^T columns are this lane's column: its own factor
 #pragma unroll
-          for (int nb = 0; nb < NBN; ++nb)
+            for (int nb = 0; nb < NBN; ++nb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) O[nb][i] *= alpha;
-        }
-        // P^T as the B operand: lane (n, r) holds column n, tokens 4r..4r+3,
-        // the layout S^T came out in
-        short4_t pb;
+              for (int i = 0; i < 4; ++i) O[ct][nb][i] *= alpha;
+          }
+          // P^T as the B operand: lane (n, r) holds column n, tokens 4r..4r+3,
+          // the layout S^T came out in
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pr = fast_exp2(s[i] - m_run);
-          l_run += pr;
-          pb[i] = bf16_bits(S::Q8 ? pr * vsc : pr);
+          for (int i = 0; i < 4; ++i) {
+            const float pr = fast_exp2(s[ct][i] - m_run[ct]);
+            l_run[ct] += pr;
+            pb[ct][i] = bf16_bits(S::Q8 ? pr * vsc : pr);
+          }
         }
 
         // V tile -> the same LDS buffer (its K reads are done, LDS is in
@@ -703,8 +735,12 @@ void mfma_partition_kernel(const AttnParams p) {
         if (new_tile) take_new_row<S>(new_rows + 16 * CH, tile, live - 1, lane);
 #pragma unroll
         for (int j = 0; j < HG; ++j) {
-          short4_t pj = pb;
-          if (HG > 1 && mem != j) pj = short4_t{0, 0, 0, 0};
+          short4_t pj[NCT];
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            pj[ct] = pb[ct];
+            if (HG > 1 && mem != j) pj[ct] = short4_t{0, 0, 0, 0};
+          }
           // every V operand of this kv head first, then the products (the
           // reads stay pipelined whatever the register pressure elsewhere)
           short4_t vA[NBN];
@@ -714,39 +750,48 @@ void mfma_partition_kernel(const AttnParams p) {
                 (lds_short4_t*)(tile + v_rd + 2 * D * j + 32 * nb));
 #pragma unroll
           for (int nb = 0; nb < NBN; ++nb)
-            O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj, O[nb], 0, 0, 0);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+              O[ct][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj[ct], O[ct][nb], 0, 0, 0);
         }
       }
     }
 
     // ---- finish the piece ---------------------------------------------------
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);            // column n's sum, in every row group
     const int seg = b * U + pc.u;
-    if (pc.j0 == 0 && pc.j1 == pc.n_b) {
-      if (n < ncol) {
-        // (a query that sees no key gets 0)
-        const float inv = !GEN || l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        uint16_t* orow =
-            static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + col_q) * p.Hq + col_h) * D + 4 * r;
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb)
-          *reinterpret_cast<uint2*>(orow + 16 * nb) =
-              make_uint2(pack_bf16x2(O[nb][0] * inv, O[nb][1] * inv),
-                         pack_bf16x2(O[nb][2] * inv, O[nb][3] * inv));
-      }
-    } else {
-      const int64_t row = (int64_t)piece + seg;
-      const int C = p.cols;
-      if (n < ncol) {
-        float* orow = p.ws_o + (row * C + n) * D + 4 * r;
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + n;
+      float l_tot = l_run[ct];
+      l_tot += __shfl_xor(l_tot, 16);
+      l_tot += __shfl_xor(l_tot, 32);            // column n's sum, in every row group
+      if (pc.j0 == 0 && pc.j1 == pc.n_b) {
+        if (c < ncol) {
+          // (a query that sees no key gets 0)
+          const float inv = !GEN || l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+          uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                           ((int64_t)(r0 + col_q[ct]) * p.Hq + col_h[ct]) * D + 4 * r;
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb)
-          *reinterpret_cast<float4*>(orow + 16 * nb) = make_float4(O[nb][0], O[nb][1], O[nb][2], O[nb][3]);
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<uint2*>(orow + 16 * nb) =
+                make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
+                           pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
+        }
+      } else {
+        const int64_t row = (int64_t)piece + seg;
+        const int C = p.cols;
+        if (c < ncol) {
+          float* orow = p.ws_o + (row * C + c) * D + 4 * r;
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<float4*>(orow + 16 * nb) =
+                make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+        }
+        // (lanes 0..15: the tile's columns, once each; one tile: ncol <= 16)
+        if (NCT == 1 ? lane < ncol : lane < 16 && 16 * ct + lane < ncol)
+          *reinterpret_cast<float2*>(p.ws_ml + (row * C + 16 * ct + lane) * 2) =
+              make_float2(m_run[ct], l_tot);
       }
-      if (lane < ncol)
-        *reinterpret_cast<float2*>(p.ws_ml + (row * C + lane) * 2) = make_float2(m_run, l_tot);
     }
     x = pc.run_start + pc.j1;
   }
@@ -815,9 +860,22 @@ static size_t mfma_lds_total(int B, int D, int hg) {
 // The decode and the generalised instantiations of one unit size are held to
 // the same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves
 // both (the smaller of their occupancies, should registers ever differ).
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg) {
+// col_tiles = 2: the generalised instantiation with two column tiles alone.
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles) {
   int blocks = 0, blocks_gen = 0;
   const size_t lds = mfma_lds_total(B, D, hg);
+  if (col_tiles == 2) {
+    const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
+      using S = decltype(s);
+      if constexpr (S::HG == 1) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &blocks, mfma_partition_kernel<S, true, false, 2>, kAttnBlockThreads, lds) != hipSuccess)
+          blocks = 0;
+      }
+    });
+    return ok ? blocks : 0;
+  }
+  if (col_tiles != 1) return 0;
   const bool ok = dispatch_mfma(D, BS, G, kind, hg, [&](auto s) {
     using S = decltype(s);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, mfma_partition_kernel<S, false>,
@@ -835,10 +893,21 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
   const size_t lds = mfma_lds_total(p.B, D, p.hg);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
   if (gen && p.rope) return hipErrorInvalidValue;
-  if (p.hg < 1 || p.Hkv % p.hg != 0 || p.hg * G * p.max_q > 16) return hipErrorInvalidValue;
+  const int cols = p.hg * G * p.max_q;
+  // two column tiles: the generalised call with one kv head per wave only
+  if (p.hg < 1 || p.Hkv % p.hg != 0 || cols != p.cols || cols > 32 ||
+      (cols > 16 && (!gen || p.hg != 1)))
+    return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);
     if (gen) {
+      if constexpr (S::HG == 1) {
+        if (cols > 16) {
+          hipLaunchKernelGGL((mfma_partition_kernel<S, true, false, 2>), dim3(blocks),
+                             dim3(kAttnBlockThreads), lds, stream, p);
+          return;
+        }
+      }
       hipLaunchKernelGGL((mfma_partition_kernel<S, true>), dim3(blocks),
                          dim3(kAttnBlockThreads), lds, stream, p);
       return;

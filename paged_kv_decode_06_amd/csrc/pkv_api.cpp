@@ -61,10 +61,12 @@ int cu_count(int dev) {
 
 // LDS of the partition kernel grows with B; occupancy is looked up for B
 // rounded up to a multiple of 1024 so that the cache stays small.  hg: kv
-// heads per wave (MFMA only).
-int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg) {
+// heads per wave, col_tiles: 16-column tiles per wave (MFMA only).
+int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg,
+                  int col_tiles = 1) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
+  const unsigned long long key = ((unsigned long long)col_tiles << 52) |
+                                 ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
                                  ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
                                  ((unsigned long long)G << 16) | ((unsigned long long)kind << 12) |
@@ -75,8 +77,9 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, i
     auto it = c.blocks.find(key);
     if (it != c.blocks.end()) return it->second;
   }
-  const int n = path == pkv::AttnPath::kMfma ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg)
-                                             : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
+  const int n = path == pkv::AttnPath::kMfma
+                    ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg, col_tiles)
+                    : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
   return n;
@@ -91,11 +94,12 @@ bool supported(int D, int BS, int G, int kv_dtype) {
 }
 
 // Persistent grid: every workgroup that fits at once on every CU.
-int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B, int hg) {
+int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B, int hg,
+                     int col_tiles = 1) {
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
-  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg);
+  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, col_tiles);
   return ncu * per_cu;
 }
 
@@ -109,9 +113,14 @@ std::atomic<int>& unit_heads_flag() {
   return flag;
 }
 
-// The most columns (kv heads per wave * G * max_q) one partition wave
-// serves: the 16 MFMA columns.
-constexpr int kMaxCols = 16;
+// Columns (kv heads per wave * G * max_q) one partition wave serves: the 16
+// MFMA columns, or two tiles of them in the generalised call with one kv
+// head per wave.
+constexpr int kTileCols = 16;
+constexpr int kMaxCols = 2 * kTileCols;
+
+// 16-column tiles of a wave serving `cols` columns.
+int col_tiles(int cols) { return (cols + kTileCols - 1) / kTileCols; }
 
 // A wave of the MFMA kernel serves hg adjacent kv heads when hg divides
 // Hkv, the unit's columns (hg * G per query, max_q queries per sequence)
@@ -123,7 +132,7 @@ int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, 
   if (path != pkv::AttnPath::kMfma || unit_heads_flag().load(std::memory_order_relaxed) == 1)
     return 1;
   const int hg = pkv::mfma_unit_heads(G);
-  if (hg <= 1 || Hkv % hg != 0 || hg * G * max_q > kMaxCols) return 1;
+  if (hg <= 1 || Hkv % hg != 0 || hg * G * max_q > kTileCols) return 1;
   int dev;
   if (current_device(&dev) != 0) return 1;
   return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg) >= 2 ? hg : 1;
@@ -206,10 +215,10 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const pkv::AttnPath path = path_for(opts, G);
   const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
-  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
+  const int cols = hg * G * opts.max_q;
+  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols));
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
-  const int cols = hg * G * opts.max_q;
   const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv / hg, cols, D, waves);
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
@@ -344,10 +353,11 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
   for (int gen = general ? 1 : 0; gen >= 0; --gen) {
     if (gen == 0 && max_q > 1) continue;
     const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0, max_q);
-    const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg);
+    const int cols = hg * G * max_q;
+    const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols));
     if (blocks <= 0) return 0;
     const int waves = blocks * pkv::kAttnWavesPerBlock;
-    const size_t t = pkv::workspace_layout(B, Hkv / hg, hg * G * max_q, D, waves).total;
+    const size_t t = pkv::workspace_layout(B, Hkv / hg, cols, D, waves).total;
     if (t > need) need = t;
   }
   return need;

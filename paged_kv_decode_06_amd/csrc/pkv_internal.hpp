@@ -27,7 +27,7 @@ struct AttnParams {
   int B, Hq, Hkv, NB, MBS;
   // Query tokens (bottom-right causal, see decode_common.hpp): sequence b
   // owns q/out rows q_start[b] .. q_start[b+1]-1 (q_start NULL: row b only);
-  // at most max_q of them, G * max_q <= 16.  cols = hg * G * max_q columns
+  // at most max_q of them, G * max_q <= 32.  cols = hg * G * max_q columns
   // per share row.  window > 0 hides keys more than window - 1 positions behind a
   // query except the first `sinks` positions.
   const int32_t* q_start;
@@ -35,7 +35,8 @@ struct AttnParams {
   int sinks, window;
   // kv heads one partition wave serves together (a unit of adjacent kv
   // heads): the work axis runs over (sequence, unit, page), U = Hkv / hg
-  // units per sequence, and cols = hg * G * max_q <= 16.  The VALU kernel
+  // units per sequence, and cols = hg * G * max_q <= 16 (up to 32 with
+  // hg = 1 in the generalised call: two 16-column tiles).  The VALU kernel
   // always takes 1.
   int hg;
   int total_waves;      // persistent waves of the partition grid
@@ -109,8 +110,9 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
                                  hipStream_t stream);
 // The occupancy both instantiations (decode and generalised) with hg kv
 // heads per wave reach (0 if there is none: mfma_unit_heads(G) is the one hg
-// above 1 that exists).
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg);
+// above 1 that exists); with col_tiles = 2, that of the generalised
+// instantiation with two 16-column tiles (hg = 1 only).
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1);
 int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
 size_t mfma_stage_lds_bytes(int D, int hg);

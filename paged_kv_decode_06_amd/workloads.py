@@ -32,6 +32,9 @@ Recipes (lengths from ``numpy.random.default_rng(seed)``, tensors from a
   long_context_window
                 the long_context recipe (seed 2) attending a sliding window of
                 the last 8192 tokens plus 16 sink tokens
+  mixed_70b_verify4
+                the mixed_70b recipe (seed 3) with min(4, L) query tokens per
+                sequence (G = 8: 32 query columns per kv head)
 
 Every sequence's history holds L-q_len tokens before the step (q_len = 1
 unless a recipe says otherwise); the step appends tokens L-q_len .. L-1
@@ -92,12 +95,17 @@ CONFIGS = {
                                 "speculative verify: llama3_8b shapes, 4 query tokens per "
                                 "sequence, bottom-right causal", q_len=4,
                                 lengths_from="llama3_8b"),
+    "mixed_70b_verify4": Config("mixed_70b_verify4", 3, 256, 64, 8, 128, 16, "bf16", 16384,
+                                "speculative verify on the 70B-shaped mix: 4 query tokens per "
+                                "sequence (fewer where the history is shorter), bottom-right "
+                                "causal; G = 8, so 32 query columns per kv head", q_len=4,
+                                lengths_from="mixed_70b"),
     "long_context_window": Config("long_context_window", 2, 4, 32, 8, 128, 16, "bf16", 131072,
                                   "long context, sliding window 8192 + 16 sink tokens",
                                   window=8192, sinks=16, lengths_from="long_context"),
 }
 CONFIG_ORDER = ["tiny", "llama3_8b", "long_context", "mixed_70b", "fp8", "int8",
-                "llama3_8b_verify4", "long_context_window"]
+                "llama3_8b_verify4", "long_context_window", "mixed_70b_verify4"]
 
 
 def draw_lengths(cfg: Config, rng: np.random.Generator) -> np.ndarray:
@@ -300,7 +308,7 @@ def make_config_workload(name: str, device="cpu", poison: bool = False) -> Workl
     return build_workload(cfg.name, cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.BS, L,
                           kv_dtype=cfg.kv_dtype, seed=cfg.seed, NB=NB, MBS=MBS,
                           device=device, poison=poison, rng=rng,
-                          q_lens=np.full(cfg.B, cfg.q_len), window=cfg.window, sinks=cfg.sinks)
+                          q_lens=np.minimum(cfg.q_len, L), window=cfg.window, sinks=cfg.sinks)
 
 
 # ---- host views for the oracle ---------------------------------------------

@@ -57,6 +57,16 @@ CASES = [
     (2, 32, 8, 128, 16, (600, 3000), (4, 1), "int8", 8, 300),
     (3, 128, 8, 128, 16, (700, 1500, 3000), (1, 1, 1), "bf16", 4, 256),    # G = 16, window
     (2, 64, 4, 64, 32, (500, 2000), (1, 1), "fp8", 0, 0),                  # G = 16
+    # two 16-column tiles (G * max_q in 17..32, one kv head per wave)
+    (3, 64, 8, 128, 16, (9, 700, 2500), (4, 3, 4), "bf16", 0, 0),           # G = 8, 4 queries
+    (3, 32, 8, 128, 16, (40, 513, 3000), (8, 5, 1), "bf16", 2, 300),        # G = 4, 8 queries
+    (2, 16, 1, 128, 32, (100, 4000), (2, 2), "bf16", 0, 0),                 # G = 16, 2 queries
+    (2, 16, 8, 64, 16, (60, 900), (16, 11), "bf16", 0, 0),                  # G = 2, 16 queries
+    (2, 4, 4, 64, 32, (50, 1000), (32, 17), "bf16", 4, 40),                 # G = 1, 32 queries
+    (3, 32, 8, 128, 16, (5, 300, 1200), (5, 6, 6), "bf16", 0, 0),           # G = 4: 24 columns
+    (3, 64, 8, 64, 16, (3, 77, 1200), (3, 3, 2), "bf16", 1, 64),            # G = 8: 24 columns
+    (3, 64, 8, 128, 32, (40, 700, 2000), (4, 2, 4), "fp8", 0, 0),
+    (3, 64, 8, 128, 32, (40, 700, 2000), (4, 4, 3), "int8", 3, 100),
 ]
 
 
@@ -67,13 +77,15 @@ def test_general_attention_matches_oracle(case):
     check(wl, str(case))
 
 
-def test_every_variant_with_queries_and_a_window():
-    """Every (D, BS, G, dtype) instantiation with the most queries it takes."""
+@pytest.mark.parametrize("cols", [16, 32], ids=["one-tile", "two-tiles"])
+def test_every_variant_with_queries_and_a_window(cols):
+    """Every (D, BS, G, dtype) instantiation with the most queries it takes
+    in one 16-column tile, then in two."""
     import itertools
     for D, BS, G, kv in itertools.product((64, 128), (16, 32), (1, 2, 4, 8, 16),
                                           ("bf16", "fp8", "int8")):
         Hkv = 2
-        q = 16 // G
+        q = cols // G
         wl = build(3, Hkv * G, Hkv, D, BS, (q, BS + q + 3, 9 * BS + 5), (q, q, max(1, q // 2)),
                    kv=kv, seed=D + BS + G, sinks=2, window=BS + 5)
         check(wl, f"D{D} BS{BS} G{G} {kv} q{q}")
@@ -141,7 +153,7 @@ def test_pages_outside_the_window_are_never_read():
     assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_verify4", "long_context_window"])
+@pytest.mark.parametrize("name", ["llama3_8b_verify4", "long_context_window", "mixed_70b_verify4"])
 def test_full_configuration_sampled(name):
     say(f"config {name}")
     wl = W.make_config_workload(name, device=DEV, poison=True)
@@ -160,11 +172,12 @@ def test_full_configuration_sampled(name):
 
 
 def test_unsupported_query_counts_are_rejected():
-    wl = build(2, 16, 2, 64, 16, (10, 20), (2, 3), seed=7)
+    wl = build(2, 16, 2, 64, 16, (10, 20), (2, 5), seed=7)
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
     out = torch.empty_like(wl.q)
-    with pytest.raises(ops.PkvError) as e:          # G = 8: at most 2 queries
+    with pytest.raises(ops.PkvError) as e:          # G = 8: at most 4 queries
         ops.paged_attention(wl.q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens,
-                            wl.scale, out, q_start=wl.q_start, max_q_len=3, workspace=ws)
+                            wl.scale, out, q_start=wl.q_start, max_q_len=5, workspace=ws)
     assert e.value.status == -3
-    assert ops.attention_workspace_bytes(2, 16, 2, 64, 16, wl.MBS, 0, 3) == 0
+    assert ops.attention_workspace_bytes(2, 16, 2, 64, 16, wl.MBS, 0, 5) == 0
+    assert ops.attention_workspace_bytes(2, 16, 2, 64, 16, wl.MBS, 0, 4) > 0

@@ -71,3 +71,22 @@ def test_random_general_attention(seed):
         f"window={window} sinks={sinks}")
     wl = build_general(B, Hq, Hkv, D, BS, L, q, kv=kv, seed=seed, sinks=sinks, window=window)
     check_general(wl, f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_general_attention_two_tiles(seed):
+    """Query counts past one 16-column tile (16 < G * max_q <= 32); one
+    sequence always takes the most, the others are ragged."""
+    rng = np.random.default_rng(9000 + seed)
+    B, Hq, Hkv, D, BS, kv = draw_shape(rng)
+    G = Hq // Hkv
+    qmax = 32 // G
+    q = [int(rng.integers(1, qmax + 1)) for _ in range(B)]
+    q[int(rng.integers(0, B))] = qmax
+    L = [max(l, qq) for l, qq in zip(draw_lengths(rng, B, BS), q)]
+    window = int(rng.choice([0, 0, int(rng.integers(1, 600))]))
+    sinks = int(rng.integers(0, 40)) if window > 0 and rng.random() < 0.6 else 0
+    say(f"seed {seed}: B={B} Hq={Hq} Hkv={Hkv} D={D} BS={BS} {kv} L={L} q={q} "
+        f"window={window} sinks={sinks}")
+    wl = build_general(B, Hq, Hkv, D, BS, L, q, kv=kv, seed=seed, sinks=sinks, window=window)
+    check_general(wl, f"seed {seed}")
