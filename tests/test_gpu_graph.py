@@ -87,8 +87,10 @@ def test_decode_attention_replays():
     replay_and_check(call, out, ws, ref, "decode attention fp8")
 
 
-def test_general_attention_replays():
-    wl = build_general(4, 32, 8, 128, 16, (50, 900, 2500, 4), (4, 1, 3, 4), seed=12,
+@pytest.mark.parametrize("Hq,q_lens", [(32, (4, 1, 3, 4)), (64, (4, 2, 3, 4))],
+                         ids=["one-tile", "two-tiles"])
+def test_general_attention_replays(Hq, q_lens):
+    wl = build_general(4, Hq, 8, 128, 16, (50, 900, 2500, 4), q_lens, seed=12,
                        sinks=16, window=512)
     GS.append_in_order(wl)
     mq = int(wl.q_lens.max())
@@ -106,7 +108,7 @@ def test_general_attention_replays():
                             wl.scale, out, q_start=wl.q_start, max_q_len=mq, sinks=wl.sinks,
                             window=wl.window, workspace=ws)
 
-    replay_and_check(call, out, ws, ref, "general attention, window and sinks")
+    replay_and_check(call, out, ws, ref, f"general attention, window and sinks, Hq={Hq}")
 
 
 @pytest.mark.parametrize("units", ["mfma", "mfma1"])
