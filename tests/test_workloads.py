@@ -55,3 +55,17 @@ def test_pool_tables_and_slots(kv):
         if L[b] > 1:
             blk0 = wl.block_tables_np[b, 0]
             assert (k[blk0, 0] != (W.BF16_NAN_BITS if kv == "bf16" else W.E4M3FN_NAN_CODE)).all()
+
+
+def test_verify_recipes_query_counts():
+    """Verify workloads take q_len tokens per sequence, fewer where the
+    history is shorter (the 70B mix has sequences of length 1)."""
+    for name, G, q in (("llama3_8b_verify4", 4, 4), ("mixed_70b_verify4", 8, 4)):
+        cfg = W.CONFIGS[name]
+        assert cfg.Hq // cfg.Hkv == G and cfg.q_len == q
+        wl = W.make_config_workload(name)
+        L = np.asarray(wl.lengths)
+        assert np.array_equal(wl.q_lens, np.minimum(q, L))
+        assert np.array_equal(L, lengths(name))
+        assert wl.q_start_np[-1] == wl.q_lens.sum() == wl.q.shape[0]
+    assert (wl.q_lens == 1).sum() >= 13
