@@ -153,6 +153,26 @@ def test_pages_outside_the_window_are_never_read():
     assert torch.equal(a.view(torch.int16), b_.view(torch.int16))
 
 
+@pytest.mark.parametrize("Hq", [16, 32, 64], ids=["G2-units", "G4-one-tile", "G8-two-tiles"])
+def test_a_sequence_without_queries(Hq):
+    """q_start may give a sequence no queries: it takes no rows, and every
+    other sequence's output is bit for bit that of the call where it has
+    them (the work split depends on the lengths only)."""
+    wl = build(3, Hq, 8, 128, 16, (300, 900, 2000), (2, 3, 4), seed=8)
+    GS.append_in_order(wl)
+    full = GS.general_step(wl, append=False).clone()
+    keep = torch.from_numpy(np.r_[0:2, 5:9]).to(DEV)      # sequence 1's rows 2..4 dropped
+    q = wl.q.index_select(0, keep).contiguous()
+    q_start = torch.tensor([0, 2, 2, 6], dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    n = ops.attention_workspace_bytes(3, Hq, 8, 128, 16, wl.MBS, ops.KV_BF16, 4)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ops.paged_attention(q, wl.k_cache, wl.v_cache, wl.block_tables, wl.context_lens, wl.scale,
+                        out, q_start=q_start, max_q_len=4, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), full.index_select(0, keep).view(torch.int16))
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_verify4", "long_context_window", "mixed_70b_verify4"])
 def test_full_configuration_sampled(name):
     say(f"config {name}")
