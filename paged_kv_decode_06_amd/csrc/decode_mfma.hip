@@ -201,13 +201,13 @@ __device__ __forceinline__ void stage_tile(unsigned char* tile, const uint4 (&ch
 // new rows (the unit's HG kv heads) in the cache and writes the same values
 // over that row of its staged tile in LDS (after the tile's own rows: LDS
 // writes of a wave land in order), so it attends to what an append before
-// the call would have left; no other wave reads the row.  All the work is
-// done early: the new rows are loaded beside q at the start of the run, and
-// when the first tile of the chunk holding the last page has its loads in
-// flight, the rows are encoded (fp8 / int8), stored to the cache and parked
-// in the wave's LDS slot in tile format, hidden behind that tile's load
-// latency; the tile holding position L - 1 then only copies two unit rows
-// within LDS.
+// the call would have left; no other wave reads the row.  The work is done
+// early: the new rows are loaded beside q at the start of the run, and when
+// the first tile of the chunk holding the last page has its loads in flight,
+// the rows are encoded (fp8 / int8) and parked in the wave's LDS slot in
+// tile format, hidden behind that tile's load latency; the tile holding
+// position L - 1 then only copies two unit rows within LDS.  The cache
+// stores wait until the run's tiles are all read (store_new_rows).
 // fp8 / int8: a token at offset 0 opens its block and sets the block's
 // per-head scales to amax / 448 (fp8) or amax / 127 (int8) first; otherwise
 // the block keeps its scales (the same arithmetic as the stand-alone append).
@@ -249,18 +249,17 @@ struct NewRows {
 };
 
 // Park the unit's new K and V rows in the wave's LDS slot `rows` ([K | V],
-// 2 CH chunks, tile format) and store them in the cache unit rows `kdst` /
-// `vdst`.  fp8 / int8: `ks` / `vs` are the block's scales of the unit's heads
-// (read when the token lands inside the block), `ksw` / `vsw` the same
-// slots for writing (when it opens the block, lane 0 stores the scales set
-// from the rows); `sk` / `sv` leave as the scales of head `mem` after the
-// append.
+// 2 CH chunks, tile format).  fp8 / int8: `ks` / `vs` are the block's scales
+// of the unit's heads (read when the token lands inside the block); when it
+// opens the block the scales are set from the rows.  `codes_out` leave as
+// this lane's encoded chunks and `gsc_out` as the unit's K and V scales after
+// the append, for store_new_rows; `sk` / `sv` as the scales of head `mem`.
 template <class S>
 __device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP], int lane,
-                                              int mem, unsigned char* rows, unsigned char* kdst,
-                                              unsigned char* vdst, bool opens, float& sk,
+                                              int mem, unsigned char* rows, bool opens, float& sk,
                                               float& sv, const float* ks, const float* vs,
-                                              float* ksw, float* vsw) {
+                                              uint2 (&codes_out)[NewRows<S>::NP],
+                                              float (&gsc_out)[2 * S::HG]) {
   constexpr int HG = S::HG, CH = NewRows<S>::CH, NP = NewRows<S>::NP;
   constexpr int CPH = S::D / 8;   // chunks per head row
   if constexpr (S::Q8) {
@@ -294,13 +293,6 @@ __device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP
         for (int i = 0; i < NP; ++i) am = fmaxf(am, grp[i] == gi ? amc[i] : 0.0f);
         gsc[gi] = block_scale(wave_max(am));
       }
-      if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < HG; ++j) {
-          ksw[j] = gsc[j];
-          vsw[j] = gsc[HG + j];
-        }
-      }
     } else {
 #pragma unroll
       for (int j = 0; j < HG; ++j) {
@@ -308,6 +300,8 @@ __device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP
         gsc[HG + j] = vs[j];
       }
     }
+#pragma unroll
+    for (int gi = 0; gi < 2 * HG; ++gi) gsc_out[gi] = gsc[gi];
     sk = gsc[0];
     sv = gsc[HG];
 #pragma unroll
@@ -323,16 +317,15 @@ __device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP
 #pragma unroll
       for (int gi = 1; gi < 2 * HG; ++gi)
         if (grp[i] == gi) sc = gsc[gi];
+      codes_out[i] = make_uint2(0, 0);
       if (grp[i] >= 0) {
         const int q = lane + kWave * i;
-        const bool is_k = q < CH;
-        const int c = is_k ? q : q - CH;
         uint2 codes;
         codes.x = enc(x[i][0], sc) | (enc(x[i][1], sc) << 8) | (enc(x[i][2], sc) << 16) |
                   (enc(x[i][3], sc) << 24);
         codes.y = enc(x[i][4], sc) | (enc(x[i][5], sc) << 8) | (enc(x[i][6], sc) << 16) |
                   (enc(x[i][7], sc) << 24);
-        *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes;
+        codes_out[i] = codes;
         *reinterpret_cast<bf16x8_t*>(rows + 16 * q) =
             S::INT8 ? i8x8_to_bf16(codes) : fp8x8_to_bf16(codes);
       }
@@ -341,10 +334,42 @@ __device__ __forceinline__ void park_new_rows(const uint4 (&part)[NewRows<S>::NP
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int q = lane + kWave * i;
-      if (q < 2 * CH) {
-        const bool is_k = q < CH;
-        *reinterpret_cast<uint4*>((is_k ? kdst : vdst) + 16 * (is_k ? q : q - CH)) = part[i];
-        *reinterpret_cast<uint4*>(rows + 16 * q) = part[i];
+      if (q < 2 * CH) *reinterpret_cast<uint4*>(rows + 16 * q) = part[i];
+    }
+  }
+}
+
+// Store the parked rows in the cache unit rows `kdst` / `vdst` (bf16: the
+// rows themselves; fp8 / int8: their codes) and, when the token opened the
+// block, the unit's scales in `ksw` / `vsw` (lane 0).  Called once the run's
+// tiles have all been read: a wave's memory counter covers stores as well as
+// loads, so a store issued earlier would hold up the waits for the tiles
+// loaded after it.
+template <class S>
+__device__ __forceinline__ void store_new_rows(const uint4 (&part)[NewRows<S>::NP],
+                                               const uint2 (&codes)[NewRows<S>::NP],
+                                               const float (&gsc)[2 * S::HG], int lane,
+                                               unsigned char* kdst, unsigned char* vdst,
+                                               bool opens, float* ksw, float* vsw) {
+  constexpr int HG = S::HG, CH = NewRows<S>::CH, NP = NewRows<S>::NP;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int q = lane + kWave * i;
+    if (q < 2 * CH) {
+      const bool is_k = q < CH;
+      const int c = is_k ? q : q - CH;
+      if constexpr (S::Q8)
+        *reinterpret_cast<uint2*>((is_k ? kdst : vdst) + 8 * c) = codes[i];
+      else
+        *reinterpret_cast<uint4*>((is_k ? kdst : vdst) + 16 * c) = part[i];
+    }
+  }
+  if constexpr (S::Q8) {
+    if (opens && lane == 0) {
+#pragma unroll
+      for (int j = 0; j < HG; ++j) {
+        ksw[j] = gsc[j];
+        vsw[j] = gsc[HG + j];
       }
     }
   }
@@ -554,6 +579,11 @@ void mfma_partition_kernel(const AttnParams p) {
     // it raised the loop's registers and measured slower)
     if constexpr (ROPE) rope_rotate<S>(p, L_in - 1, lane, r, tile, qB[0], new_part, has_new);
     float new_ksc = 1.0f, new_vsc = 1.0f;   // fp8 / int8: head mem's last-block scales after the append
+    // the append's cache stores, issued after the run's last tile (store_new_rows)
+    uint2 new_codes[NP];
+    float new_gsc[2 * HG];
+    int64_t new_row = 0, new_sslot = 0;
+    bool new_opens = false, parked = false;
 
     float4_t O[NCT][NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
     float m_run[NCT];       // running max of column n (exp2 domain)
@@ -635,14 +665,14 @@ void mfma_partition_kernel(const AttnParams p) {
         if (new_here && u == 0) {   // park the new rows while this tile's loads fly
           const int blk = __builtin_amdgcn_readlane(phys_l, k_last);
           const int off = (L - 1) % BS;
-          const int64_t row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g0 * RB;
-          const int64_t sslot = (int64_t)blk * Hkv + g0;
+          new_row = ((int64_t)blk * BS + off) * row_bytes + (int64_t)g0 * RB;
+          new_sslot = (int64_t)blk * Hkv + g0;
+          new_opens = off == 0;
+          parked = true;
           // (bf16 caches have no scales: null pointers then)
-          park_new_rows<S>(new_part, lane, mem, new_rows, p.k_cache_w + row, p.v_cache_w + row,
-                           off == 0, new_ksc, new_vsc, S::Q8 ? p.k_scale + sslot : nullptr,
-                           S::Q8 ? p.v_scale + sslot : nullptr,
-                           S::Q8 ? p.k_scale_w + sslot : nullptr,
-                           S::Q8 ? p.v_scale_w + sslot : nullptr);
+          park_new_rows<S>(new_part, lane, mem, new_rows, new_opens, new_ksc, new_vsc,
+                           S::Q8 ? p.k_scale + new_sslot : nullptr,
+                           S::Q8 ? p.v_scale + new_sslot : nullptr, new_codes, new_gsc);
         }
 
         // K tile -> LDS -> A operands; scores S^T (16 tokens x 16 columns)
@@ -757,6 +787,12 @@ void mfma_partition_kernel(const AttnParams p) {
       }
     }
 
+    if (parked)   // (wave-uniform)
+      store_new_rows<S>(new_part, new_codes, new_gsc, lane, p.k_cache_w + new_row,
+                        p.v_cache_w + new_row, new_opens,
+                        S::Q8 ? p.k_scale_w + new_sslot : nullptr,
+                        S::Q8 ? p.v_scale_w + new_sslot : nullptr);
+
     // ---- finish the piece ---------------------------------------------------
     const int seg = b * U + pc.u;
 #pragma unroll
@@ -857,12 +893,19 @@ static size_t mfma_lds_total(int B, int D, int hg) {
   return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
 
+// Workgroups per CU at `wpe` waves per SIMD (4 SIMDs a CU).
+constexpr int blocks_at(int wpe) { return wpe * 4 / kAttnWavesPerBlock; }
+
 // The decode and the generalised instantiations of one unit size are held to
 // the same waves per SIMD (amdgpu_waves_per_eu), so one grid size serves
 // both (the smaller of their occupancies, should registers ever differ).
+// The occupancy query goes by the registers a kernel ended up with, which
+// may allow more waves than it was compiled for (a one-head kernel at 128
+// VGPRs would run 4 per SIMD, measured 13-15% slower than 3), so the grid
+// is capped at the waves per SIMD of the instantiation.
 // col_tiles = 2: the generalised instantiation with two column tiles alone.
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles) {
-  int blocks = 0, blocks_gen = 0;
+  int blocks = 0, blocks_gen = 0, cap = 0;
   const size_t lds = mfma_lds_total(B, D, hg);
   if (col_tiles == 2) {
     const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
@@ -871,9 +914,10 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_ti
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &blocks, mfma_partition_kernel<S, true, false, 2>, kAttnBlockThreads, lds) != hipSuccess)
           blocks = 0;
+        cap = blocks_at(2);
       }
     });
-    return ok ? blocks : 0;
+    return ok ? (blocks < cap ? blocks : cap) : 0;
   }
   if (col_tiles != 1) return 0;
   const bool ok = dispatch_mfma(D, BS, G, kind, hg, [&](auto s) {
@@ -884,8 +928,11 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_ti
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks_gen, mfma_partition_kernel<S, true>,
                                                      kAttnBlockThreads, lds) != hipSuccess)
       blocks_gen = 0;
+    cap = blocks_at(S::WPE);
   });
-  return ok ? (blocks < blocks_gen ? blocks : blocks_gen) : 0;
+  if (!ok) return 0;
+  const int b = blocks < blocks_gen ? blocks : blocks_gen;
+  return b < cap ? b : cap;
 }
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
