@@ -54,6 +54,23 @@ def test_unit_heads_of_the_configurations(name, hg):
     assert ops.decode_unit_heads(B, c.Hq, c.Hkv, c.D, c.BS, kvd) == 1
 
 
+@pytest.mark.parametrize("name", ["llama3_8b", "fp8", "int8", "mixed_70b"])
+def test_grid_is_the_compiled_waves_per_simd(name):
+    """The persistent grid is 2 waves per SIMD with two-head units and 3
+    with one head, on every CU (4 SIMDs a CU), whatever registers the
+    kernels end up with: the occupancy query alone once gave one-head calls
+    4 per SIMD, which ran 13-15% slower."""
+    c = W.CONFIGS[name]
+    kvd = GS.KV_KIND[c.kv_dtype]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ops.attention_waves(c.B, c.Hq, c.Hkv, c.D, c.BS, kvd) == cus * 4 * 2
+    use_kernel("mfma1")
+    try:
+        assert ops.attention_waves(c.B, c.Hq, c.Hkv, c.D, c.BS, kvd) == cus * 4 * 3
+    finally:
+        default_kernel()
+
+
 def one_page_pieces(wl: W.Workload) -> bool:
     pages = int(sum((int(L) + wl.BS - 1) // wl.BS for L in wl.lengths))
     return pages * wl.Hkv <= waves(wl) and pages * wl.Hkv // max(unit_heads(wl), 1) <= waves(wl)
