@@ -153,6 +153,27 @@ int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v
                                int NB, int MBS, int kv_dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Bytes of the static scratch of pkv_paged_decode_attention_noalloc (32 MiB
+ * per GPU). */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* pkv_paged_decode_attention for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, serving loops that must not
+ * allocate, harnesses that forbid it): the same arguments without the
+ * workspace, the same kernels and the same result, bit for bit.  The
+ * partial results go to a static device array of PKV_STATIC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends;
+ * the call allocates nothing.  Sizes whose workspace
+ * (pkv_paged_decode_workspace_bytes) exceeds it return PKV_ERR_WORKSPACE
+ * before any launch.  The scratch needs no clearing, but every call on one
+ * GPU shares it: calls that overlap in time on the same GPU (two streams,
+ * two host threads) race and give wrong results; serialise them. */
+int pkv_paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       float scale, void* out, int B, int Hq, int Hkv, int D,
+                                       int BS, int NB, int MBS, int kv_dtype, void* stream);
+
 /* The two halves of pkv_paged_decode_attention, with the same arguments:
  * calling partition then merge on one stream is exactly the full call.
  * Exposed so that each kernel can be timed on its own. */

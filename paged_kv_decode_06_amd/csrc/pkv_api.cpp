@@ -143,7 +143,7 @@ struct AttnCall {
   pkv::AttnPath path;
   int D, BS, G, blocks;
   int kind;          // pkv::KvKind (= kv_dtype)
-  size_t ws_used;    // workspace bytes the call's layout takes (a multiple of 256)
+  size_t ws_used = 0;   // workspace bytes the call's layout takes (a multiple of 256)
 };
 
 // Room for a rotated copy of q ([B, Hq, D] bf16) at the end of a decode step
@@ -220,6 +220,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
   const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv / hg, cols, D, waves);
+  call->ws_used = lay.total;
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, lay.total);
@@ -455,6 +456,85 @@ int pkv_paged_decode_attention(const void* q, const void* k_cache, const void* v
   if (B == 0) return PKV_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_partition(call, s);
+  if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
+  e = pkv::launch_merge(call.p, call.D, call.G, s);
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// The workspace of pkv_paged_decode_attention_noalloc, for callers that cannot
+// allocate: a static device array, one copy per GPU (the loader places it when
+// the library's code object is loaded on a device; it stays until the
+// process ends).  Host code never passes `scratch` itself to a kernel (on the
+// host that name is a stand-in, not a device address): it looks up each
+// device's address once, with that device current, and uses that.
+constexpr size_t kStaticScratchBytes = PKV_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+struct ScratchTable {
+  std::mutex mu;
+  std::unordered_map<int, void*> ptr;   // device -> address of its `scratch`
+};
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device), or NULL with *err set.
+void* static_scratch(hipError_t* err) {
+  int dev;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  auto& t = scratch_table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  auto it = t.ptr.find(dev);
+  if (it != t.ptr.end()) return it->second;
+  void* p = nullptr;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || p == nullptr) {
+    if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  t.ptr[dev] = p;
+  return p;
+}
+
+// A placeholder workspace address for the host-side checks (16-byte aligned,
+// never dereferenced: the checks launch nothing).
+void* const kCheckOnly = reinterpret_cast<void*>(uintptr_t(256));
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       float scale, void* out, int B, int Hq, int Hkv, int D,
+                                       int BS, int NB, int MBS, int kv_dtype, void* stream) {
+  AttnCall call;
+  // host-side checks and the call's layout first, against the scratch's size
+  int st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                             scale, out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, kCheckOnly,
+                             kStaticScratchBytes, &call);
+  if (st == PKV_ERR_WORKSPACE)
+    return fail(PKV_ERR_WORKSPACE, "these sizes need %zu bytes of workspace, more than the %zu "
+                "bytes of the static scratch; use pkv_paged_decode_attention with a workspace",
+                call.ws_used, kStaticScratchBytes);
+  if (st != PKV_OK) return st;
+  if (B == 0) return PKV_OK;
+  hipError_t e;
+  void* ws = static_scratch(&e);
+  if (ws == nullptr) return hip_fail(e, "address of the static scratch");
+  st = prepare_attention(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
+                         out, B, Hq, Hkv, D, BS, NB, MBS, kv_dtype, ws, kStaticScratchBytes, &call);
+  if (st != PKV_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = launch_partition(call, s);
   if (e != hipSuccess) return hip_fail(e, "partition kernel launch");
   e = pkv::launch_merge(call.p, call.D, call.G, s);
   return e == hipSuccess ? PKV_OK : hip_fail(e, "merge kernel launch");

@@ -61,6 +61,8 @@ def _load():
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = I
+        lib.pkv_paged_decode_attention_noalloc.argtypes = attn_args[:17] + [P]
+        lib.pkv_paged_decode_attention_noalloc.restype = I
         Dd = ctypes.c_double
         lib.pkv_rope_kv_append.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                            Dd, Dd, Dd, Dd, Dd, P]
@@ -244,6 +246,9 @@ def workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:
     return int(_load().pkv_paged_decode_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype))
 
 
+_NO_WORKSPACE = object()
+
+
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                workspace, stream):
     kvd = _kv_dtype(k_cache)
@@ -263,6 +268,10 @@ def _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_sc
         raise ValueError("q/out/cache shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables/context_lens must have B rows")
+    if workspace is _NO_WORKSPACE:   # (the static-scratch call: no workspace arguments)
+        return (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
+                B, Hq, Hkv, D, BS, NB, MBS, kvd, _stream(stream))
     if workspace is None:
         raise ValueError("workspace is required (see workspace_bytes)")
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
@@ -279,6 +288,20 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
                       v_scale, workspace, stream)
     _check("pkv_paged_decode_attention", _load().pkv_paged_decode_attention(*args))
+
+
+STATIC_SCRATCH_BYTES = 32 << 20   # PKV_STATIC_SCRATCH_BYTES
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                   k_scale=None, v_scale=None, stream=None) -> None:
+    """pkv_paged_decode_attention_noalloc: paged_decode_attention without a
+    workspace argument; the library's static per-GPU scratch holds the partial
+    results (calls on one GPU must not overlap in time)."""
+    args = _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale,
+                      v_scale, _NO_WORKSPACE, stream)
+    _check("pkv_paged_decode_attention_noalloc",
+           _load().pkv_paged_decode_attention_noalloc(*args))
 
 
 def validate_inputs(q, k_cache, v_cache, block_tables, context_lens, scale, out,
