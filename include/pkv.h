@@ -105,13 +105,13 @@ int pkv_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapp
 
 /* RoPE fused with the append ("tiny-vllm part 5", the RoPE section: each
  * head's pairs (x[2i], x[2i+1]) rotate by pos * f_i, f_i = theta^(-2i/D),
- * with the Llama 3 frequency scaling of the page's table path: where the
- * wavelength 2 pi / f_i exceeds original_max_len / low_freq_factor, f_i is
- * divided by rope_factor; between that and original_max_len /
- * high_freq_factor it is blended, (1 - a) f_i / rope_factor + a f_i with
- * a = (original_max_len / wavelength - low_freq_factor) / (high_freq_factor
- * - low_freq_factor).  rope_factor = 1 is plain RoPE.  The page's Llama 3
- * setting is theta 500000, factor 32, 1, 4, 8192.)
+ * with the Llama 3 frequency scaling of the page's table path.  With
+ * r = original_max_len * f_i / (2 pi), the turns pair i makes over the
+ * original context, and s = clamp((r - low_freq_factor) / (high_freq_factor
+ * - low_freq_factor), 0, 1), the frequency used is f_i (s + (1 - s) /
+ * rope_factor): slowed by rope_factor for pairs with few turns, kept for
+ * pairs with many, fading linearly in r between.  rope_factor = 1 is plain
+ * RoPE.  The page's Llama 3 setting is theta 500000, factor 32, 1, 4, 8192.)
  * For each token i < N at position positions[i]:
  *   q_out[i]  = RoPE(q[i])     [N, Hq, D] bf16 (q_out may be q itself)
  *   k_rot     = RoPE(k_new[i]) [Hkv, D]

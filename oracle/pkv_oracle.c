@@ -472,29 +472,28 @@ int pkvo_kv_append(const uint16_t* k_new, const uint16_t* v_new,
 
 /* ---- RoPE ----------------------------------------------------------------- */
 
-/* Frequencies f_i, i < D/2, of the rotary embedding: theta^(-2i/D), then the
- * Llama 3 scaling of the table path.  With lw = original_max / low_freq_factor
- * and hw = original_max / high_freq_factor, and wavelength w = 2 pi / f:
- *   w > lw            -> f / factor
- *   hw <= w <= lw     -> (1 - a) f / factor + a f,  a = (original_max / w -
- *                        low_freq_factor) / (high_freq_factor - low_freq_factor)
- *   w < hw            -> f.
+/* Frequencies f_i, i < D/2, of the rotary embedding ("tiny-vllm part 5",
+ * RoPE section): pair i turns by f_i = theta^(-2i/D) radians per position,
+ * then the Llama 3 scaling of the page's table path.  That scaling is stated
+ * here by what it does to a pair: count the turns the pair makes over the
+ * original training context, r = original_max * f_i / (2 pi).  A pair making
+ * at most low_freq_factor turns there is slowed down by `factor`, one making
+ * at least high_freq_factor turns is kept, and in between the slowdown
+ * fades linearly in r:
+ *   s = clamp((r - low_freq_factor) / (high_freq_factor - low_freq_factor), 0, 1)
+ *   f_i' = f_i * (s + (1 - s) / factor).
+ * (r <= low is a wavelength 2 pi / f_i >= original_max / low_freq_factor.)
  * factor = 1 leaves every frequency unscaled. */
 void pkvo_rope_freqs(int D, double theta, double factor, double low_freq_factor,
                      double high_freq_factor, double original_max, double* f) {
-  const double lw = original_max / low_freq_factor;
-  const double hw = original_max / high_freq_factor;
+  const double two_pi = 2.0 * 3.14159265358979323846;
   for (int i = 0; i < D / 2; ++i) {
-    const double base = 1.0 / pow(theta, (2.0 * i) / (double)D);
-    const double w = 2.0 * 3.14159265358979323846 / base;   /* 2 pi / f */
-    double fi = base;
-    if (w > lw) {
-      fi = base / factor;
-    } else if (w >= hw) {
-      const double a = (original_max / w - low_freq_factor) / (high_freq_factor - low_freq_factor);
-      fi = (1.0 - a) * (base / factor) + a * base;
-    }
-    f[i] = fi;
+    const double fi = pow(theta, -(2.0 * i) / (double)D);
+    const double turns = original_max * fi / two_pi;
+    double s = (turns - low_freq_factor) / (high_freq_factor - low_freq_factor);
+    if (s < 0.0) s = 0.0;
+    if (s > 1.0) s = 1.0;
+    f[i] = fi * (s + (1.0 - s) / factor);
   }
 }
 

@@ -22,6 +22,7 @@
 // the rotation are computed in fp64 and the result is rounded once, straight
 // from fp64 to bf16 (nearest even).
 
+#include <algorithm>
 #include <cmath>
 
 #include "pkv_device.hpp"
@@ -136,28 +137,22 @@ __global__ __launch_bounds__(kRopeThreads) void rope_append_kernel(
 
 }  // namespace
 
-// f_i of pair i < D / 2 (fp64, on the host), each operation a separately
-// rounded IEEE one in the order of the formula.  The blend is continuous at
-// both band edges.
+// f_i of pair i < D / 2 (fp64, on the host): theta^(-2i/D), then the Llama 3
+// scaling.  Seen from the wavelength lambda = 2 pi / f: the slowdown
+// 1 / factor applies in full to pairs whose wavelength is at least
+// original_max / low_freq_factor, not at all to those at most original_max /
+// high_freq_factor, and between the two the unscaled frequency's share grows
+// linearly in original_max / lambda.
 void rope_freqs(int D, RopeParams& rp) {
   const double pi = 3.14159265358979323846;
-  const double lw = rp.original_max / rp.low_freq_factor;
-  const double hw = rp.original_max / rp.high_freq_factor;
   for (int i = 0; i < D / 2; ++i) {
-    const volatile double e = (2.0 * i) / (double)D;   // (volatile: no contraction or reordering)
-    const double base = 1.0 / std::pow(rp.theta, (double)e);
-    const double w = 2.0 * pi / base;                   // wavelength
-    double f = base;
-    if (w > lw) {
-      f = base / rp.factor;
-    } else if (w >= hw) {
-      const volatile double a =
-          (rp.original_max / w - rp.low_freq_factor) / (rp.high_freq_factor - rp.low_freq_factor);
-      const volatile double t0 = (1.0 - a) * (base / rp.factor);
-      const volatile double t1 = a * base;
-      f = t0 + t1;
-    }
-    rp.freq[i] = f;
+    const double f = std::pow(rp.theta, -(2.0 * i) / (double)D);
+    const double lambda = 2.0 * pi / f;
+    const double keep =
+        std::min(1.0, std::max(0.0, (rp.original_max / lambda - rp.low_freq_factor) /
+                                        (rp.high_freq_factor - rp.low_freq_factor)));
+    const double slow = f / rp.factor;
+    rp.freq[i] = slow + keep * (f - slow);
   }
 }
 

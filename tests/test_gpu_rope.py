@@ -90,14 +90,18 @@ def test_plain_rope_and_in_place():
 @pytest.mark.parametrize("kv", ["fp8", "int8"])
 def test_quantised_append_of_the_rotated_keys_is_bit_exact(kv):
     """Blocks opened by the new token and blocks already open: the codes and
-    scales equal the oracle's kv_append of the rotated keys (taken from the
-    same fused call on a bf16 twin cache)."""
+    scales equal the oracle's kv_append of the oracle's own rotation of the
+    keys.  (The rotated bf16 keys of the two sides agree bit for bit on these
+    inputs, checked on a bf16 twin cache: the encoding is then compared on
+    identical values.)"""
     L = [1, 33, 64, 65, 1000, 4097]
     wl = build(len(L), 32, 8, 128, 32, L, kv=kv, seed=7)
     twin = build(len(L), 32, 8, 128, 32, L, kv="bf16", seed=7)
     pos = positions_of(wl)
+    pos_np = (wl.lengths - 1).astype(np.int32)
     host_k, host_v = W.cache_host(wl.k_cache).copy(), W.cache_host(wl.v_cache).copy()
     ks, vs = wl.k_scale.cpu().numpy().copy(), wl.v_scale.cpu().numpy().copy()
+    k0, v0 = W.bf16_bits(wl.k_new), W.bf16_bits(wl.v_new)
     qa, qb = torch.empty_like(wl.q), torch.empty_like(wl.q)
     ops.rope_kv_append(wl.q, wl.k_new, wl.v_new, pos, wl.slot_mapping, wl.k_cache, wl.v_cache,
                        wl.k_scale, wl.v_scale, q_out=qa)
@@ -105,8 +109,10 @@ def test_quantised_append_of_the_rotated_keys_is_bit_exact(kv):
                        twin.v_cache, q_out=qb)
     torch.cuda.synchronize()
     assert torch.equal(qa.view(torch.int16), qb.view(torch.int16))
-    k_rot = W.cache_host(twin.k_cache).reshape(-1, 8, 128)[twin.slot_mapping_np]
-    oracle.kv_append(k_rot, W.bf16_bits(wl.v_new), wl.slot_mapping_np, host_k, host_v, ks, vs)
+    k_rot, _ = oracle.rope_apply(k0, pos_np, freqs(128))
+    gpu_rot = W.cache_host(twin.k_cache).reshape(-1, 8, 128)[twin.slot_mapping_np]
+    assert np.array_equal(gpu_rot, k_rot), "rotated keys differ: the encodings are not comparable"
+    oracle.kv_append(k_rot, v0, wl.slot_mapping_np, host_k, host_v, ks, vs)
     assert np.array_equal(W.cache_host(wl.k_cache), host_k)
     assert np.array_equal(W.cache_host(wl.v_cache), host_v)
     assert np.array_equal(wl.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))

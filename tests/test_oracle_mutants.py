@@ -51,8 +51,19 @@ MUTANTS = [
     ("rotation sign flipped in one component", "const double r0 = x0 * c - x1 * sn;", "const double r0 = x0 * c + x1 * sn;"),
     ("pair members swapped", "const double x1 = pkvo_bf16_to_f64(x[base + 2 * i + 1]);",
      "const double x1 = pkvo_bf16_to_f64(x[base + (2 * i + 2) % D]);"),
-    ("frequencies theta^(-i/D)", "pow(theta, (2.0 * i) / (double)D)", "pow(theta, (double)i / (double)D)"),
-    ("Llama 3 long band starts at the short edge", "if (w > lw) {", "if (w > hw) {"),
+    ("frequencies theta^(-i/D)", "pow(theta, -(2.0 * i) / (double)D)", "pow(theta, -(double)i / (double)D)"),
+    ("Llama 3 band measured from the high edge",
+     "double s = (turns - low_freq_factor) / (high_freq_factor - low_freq_factor);",
+     "double s = (turns - high_freq_factor) / (high_freq_factor - low_freq_factor);"),
+    ("Llama 3 ramp not clamped above the band", "if (s > 1.0) s = 1.0;", "(void)0;"),
+    # two blends that agree with the right one at both band edges and are
+    # monotone inside: only the library and hand-derived values catch them
+    ("Llama 3 harmonic blend", "f[i] = fi * (s + (1.0 - s) / factor);",
+     "f[i] = fi / ((1.0 - s) * factor + s);"),
+    ("Llama 3 ramp linear in the wavelength",
+     "double s = (turns - low_freq_factor) / (high_freq_factor - low_freq_factor);",
+     "double s = (original_max / low_freq_factor - two_pi / fi) /\n"
+     "               (original_max / low_freq_factor - original_max / high_freq_factor);"),
     ("bf16 rounding truncates", "if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0)) lo += 1.0;", "(void)frac;"),
 ]
 

@@ -382,3 +382,50 @@ def test_rope_frequencies_follow_the_llama3_bands():
     mid = ~short & ~long_
     r = f[mid] / base[mid]
     assert ((r > 1 / 32) & (r < 1)).all() and (np.diff(r) < 0).all()
+
+
+def _library_inv_freq(D, rope_parameters):
+    """Inverse frequencies from transformers' RoPE initialisers (computed in
+    float32 there), for a Llama config with head dim D."""
+    transformers = pytest.importorskip("transformers")
+    from transformers.modeling_rope_utils import ROPE_INIT_FUNCTIONS
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding
+    cfg = transformers.LlamaConfig(hidden_size=32 * D, num_attention_heads=32, head_dim=D,
+                                   max_position_embeddings=131072,
+                                   rope_parameters=dict(rope_parameters))
+    kind = rope_parameters["rope_type"]
+    init = (LlamaRotaryEmbedding.compute_default_rope_parameters if kind == "default"
+            else ROPE_INIT_FUNCTIONS[kind])
+    inv, _ = init(cfg, torch.device("cpu"))
+    return inv.double().numpy()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rope_frequencies_match_the_library_llama3_and_default_rope(D):
+    """transformers' 'llama3' initialiser with the page's parameters (theta
+    500000, factor 32, low 1, high 4, original context 8192), and its plain
+    'default' rope for factor 1; float32 there, hence 1e-6."""
+    llama3 = _library_inv_freq(D, dict(rope_type="llama3", rope_theta=500000.0, factor=32.0,
+                                       low_freq_factor=1.0, high_freq_factor=4.0,
+                                       original_max_position_embeddings=8192))
+    plain = _library_inv_freq(D, dict(rope_type="default", rope_theta=500000.0))
+    f = oracle.rope_freqs(D)
+    np.testing.assert_allclose(f, llama3, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(oracle.rope_freqs(D, factor=1.0), plain, rtol=1e-6, atol=0)
+    # the comparison covers the blended band (pairs 15..17 at D = 64, 29..34 at 128)
+    w = 2 * math.pi / plain
+    assert ((w >= 8192 / 4) & (w <= 8192)).sum() >= 3
+
+
+def test_rope_mid_band_frequency_derived_by_hand():
+    """Pair i = D/4 turns at theta^(-1/2) = sqrt(2)/1000 per position (D = 64
+    and 128 alike).  Over the 8192-token original context that is
+    r = 8192 sqrt(2) / (2000 pi) = 1.8438478154897532 turns, inside the band
+    [1, 4]; the slowdown fades by s = (r - 1) / 3 = 0.28128260516325108, so
+    f' = (sqrt(2)/1000) (s + (1 - s)/32) = 4.2955679655936820e-4 (40-digit
+    decimal arithmetic)."""
+    expected = 4.295567965593682005407e-4
+    assert abs(oracle.rope_freqs(128)[32] - expected) <= 2e-15 * expected
+    assert abs(oracle.rope_freqs(64)[16] - expected) <= 2e-15 * expected
+    # the unscaled frequency of the same pair
+    assert abs(oracle.rope_freqs(128, factor=1.0)[32] - math.sqrt(2) / 1000) <= 2e-16
