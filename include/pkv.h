@@ -206,7 +206,12 @@ int pkv_paged_decode_merge(const void* q, const void* k_cache, const void* v_cac
  *   softmax(scale <q, K_j>) weighted sum of V_j over the keys it sees, as in
  *   pkv_paged_decode_attention; a query that sees no key gets 0.
  *   q, out  [total_q, Hq, D] bf16; q_start [B + 1] int32 (device), with
- *   q_len_b <= max_q_len (larger ones are clamped); G * max_q_len <= 32
+ *   q_len_b <= max_q_len (larger ones are clamped; negative ones count as
+ *   0).  q_start is device-resident and, like block ids, the caller's
+ *   contract: 0 <= q_start[b] <= q_start[b + 1] and q_start[B] <= total_q
+ *   (the rows of q and out); the kernels read and write rows q_start[b] ..
+ *   q_start[b] + q_len_b - 1 as given, so entries past total_q read and
+ *   write out of bounds.  G * max_q_len <= 32
  *   (one wave serves all of a sequence's queries of its kv heads, as the
  *   16-column tiles of its matrix products: two adjacent kv heads in one
  *   tile when 2 * G * max_q_len <= 16, else one kv head in one tile, or in

@@ -123,16 +123,44 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _need(t: torch.Tensor, name: str, dtype, ndim: int):
+    """Type, dtype, rank and layout of one argument (the device is checked
+    last, by _on_gpu, once every shape agrees)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+
+
+def _cache_args(k_cache, v_cache, k_scale, v_scale):
+    """The caches ([NB, BS, Hkv, D], K and V alike) and, for a quantised
+    cache, the scales ([NB, Hkv] fp32 each: the kernels index them by block
+    and kv head).  Returns (kv_dtype, NB, BS, Hkv, D)."""
+    kvd = _kv_dtype(k_cache)
+    _need(k_cache, "k_cache", k_cache.dtype, 4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} differs from k_cache "
+                         f"{tuple(k_cache.shape)}")
+    NB, BS, Hkv, D = k_cache.shape
+    if kvd != KV_BF16:
+        _need(k_scale, "k_scale", torch.float32, 2)
+        _need(v_scale, "v_scale", torch.float32, 2)
+        for t, name in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+            if tuple(t.shape) != (NB, Hkv):
+                raise ValueError(f"{name} must be [NB, Hkv] = {(NB, Hkv)}, got {tuple(t.shape)}")
+    elif k_scale is not None or v_scale is not None:
+        raise ValueError("a bf16 cache takes no scales")
+    return kvd, NB, BS, Hkv, D
 
 
 def _kv_dtype(k_cache: torch.Tensor) -> int:
@@ -145,28 +173,28 @@ def _kv_dtype(k_cache: torch.Tensor) -> int:
     raise TypeError(f"cache dtype must be bfloat16, uint8/float8_e4m3fn or int8, got {k_cache.dtype}")
 
 
-def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
-              stream=None) -> None:
-    """pkv_kv_append: store each sequence's new K/V token into its slot."""
-    kvd = _kv_dtype(k_cache)
+def _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream):
+    kvd, NB, BS, Hkv, D = _cache_args(k_cache, v_cache, k_scale, v_scale)
     _need(k_new, "k_new", torch.bfloat16, 3)
     _need(v_new, "v_new", torch.bfloat16, 3)
     _need(slot_mapping, "slot_mapping", torch.int32, 1)
-    _need(k_cache, "k_cache", k_cache.dtype, 4)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
-    if kvd != KV_BF16:
-        _need(k_scale, "k_scale", torch.float32, 2)
-        _need(v_scale, "v_scale", torch.float32, 2)
-    N, Hkv, D = k_new.shape
-    NB, BS = k_cache.shape[0], k_cache.shape[1]
-    if tuple(v_new.shape) != (N, Hkv, D) or slot_mapping.shape[0] != N:
-        raise ValueError("k_new, v_new and slot_mapping disagree on N/Hkv/D")
-    if tuple(k_cache.shape) != (NB, BS, Hkv, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("cache shape must be [NB, BS, Hkv, D] and match k_new")
-    st = _load().pkv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
-                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB,
-                               kvd, _stream(stream))
-    _check("pkv_kv_append", st)
+    N = k_new.shape[0]
+    if tuple(k_new.shape) != (N, Hkv, D) or tuple(v_new.shape) != (N, Hkv, D):
+        raise ValueError(f"k_new and v_new must be [N, Hkv, D] with the cache's Hkv, D = "
+                         f"{Hkv}, {D}; got {tuple(k_new.shape)}, {tuple(v_new.shape)}")
+    if slot_mapping.shape[0] != N:
+        raise ValueError("slot_mapping must have one entry per token of k_new")
+    _on_gpu(k_new=k_new, v_new=v_new, slot_mapping=slot_mapping, k_cache=k_cache,
+            v_cache=v_cache, k_scale=k_scale, v_scale=v_scale)
+    return (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB, kvd, _stream(stream))
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
+              stream=None) -> None:
+    """pkv_kv_append: store each sequence's new K/V token into its slot."""
+    args = _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream)
+    _check("pkv_kv_append", _load().pkv_kv_append(*args))
 
 
 LLAMA3_ROPE = dict(theta=500000.0, factor=32.0, low_freq_factor=1.0, high_freq_factor=4.0,
@@ -179,25 +207,21 @@ def rope_kv_append(q, k_new, v_new, positions, slot_mapping, k_cache, v_cache, k
     """pkv_rope_kv_append: rotate q (into q_out; in place when q_out is None)
     and the new keys at `positions`, then append the rotated keys and the
     values into their slots.  Defaults are the Llama 3 RoPE parameters."""
-    kvd = _kv_dtype(k_cache)
+    kvd, NB, BS, Hkv, D = _cache_args(k_cache, v_cache, k_scale, v_scale)
     if q_out is None:
         q_out = q
     for t, name in ((q, "q"), (q_out, "q_out"), (k_new, "k_new"), (v_new, "v_new")):
         _need(t, name, torch.bfloat16, 3)
     _need(positions, "positions", torch.int32, 1)
     _need(slot_mapping, "slot_mapping", torch.int32, 1)
-    _need(k_cache, "k_cache", k_cache.dtype, 4)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
-    if kvd != KV_BF16:
-        _need(k_scale, "k_scale", torch.float32, 2)
-        _need(v_scale, "v_scale", torch.float32, 2)
-    N, Hq, D = q.shape
-    Hkv = k_new.shape[1]
-    NB, BS = k_cache.shape[0], k_cache.shape[1]
-    if (tuple(q_out.shape) != (N, Hq, D) or tuple(k_new.shape) != (N, Hkv, D)
-            or tuple(v_new.shape) != (N, Hkv, D) or positions.shape[0] != N
-            or slot_mapping.shape[0] != N or tuple(k_cache.shape) != (NB, BS, Hkv, D)):
+    N, Hq = q.shape[0], q.shape[1]
+    if (tuple(q.shape) != (N, Hq, D) or tuple(q_out.shape) != (N, Hq, D)
+            or tuple(k_new.shape) != (N, Hkv, D) or tuple(v_new.shape) != (N, Hkv, D)
+            or positions.shape[0] != N or slot_mapping.shape[0] != N):
         raise ValueError("q, q_out, k_new, v_new, positions, slot_mapping and the caches disagree")
+    _on_gpu(q=q, q_out=q_out, k_new=k_new, v_new=v_new, positions=positions,
+            slot_mapping=slot_mapping, k_cache=k_cache, v_cache=v_cache, k_scale=k_scale,
+            v_scale=v_scale)
     st = _load().pkv_rope_kv_append(
         _ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(slot_mapping),
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), N, Hq, Hkv, D, BS, NB, kvd,
@@ -251,23 +275,19 @@ _NO_WORKSPACE = object()
 
 def _attn_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, k_scale, v_scale,
                workspace, stream):
-    kvd = _kv_dtype(k_cache)
+    kvd, NB, BS, Hkv, D2 = _cache_args(k_cache, v_cache, k_scale, v_scale)
     _need(q, "q", torch.bfloat16, 3)
     _need(out, "out", torch.bfloat16, 3)
-    _need(k_cache, "k_cache", k_cache.dtype, 4)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    if kvd != KV_BF16:
-        _need(k_scale, "k_scale", torch.float32, 2)
-        _need(v_scale, "v_scale", torch.float32, 2)
     B, Hq, D = q.shape
-    NB, BS, Hkv, D2 = k_cache.shape
     MBS = block_tables.shape[1]
-    if D2 != D or v_cache.shape != k_cache.shape or tuple(out.shape) != (B, Hq, D):
+    if D2 != D or tuple(out.shape) != (B, Hq, D):
         raise ValueError("q/out/cache shapes disagree")
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("block_tables/context_lens must have B rows")
+    _on_gpu(q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+            context_lens=context_lens, k_scale=k_scale, v_scale=v_scale)
     if workspace is _NO_WORKSPACE:   # (the static-scratch call: no workspace arguments)
         return (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                 _ptr(block_tables), _ptr(context_lens), ctypes.c_float(scale), _ptr(out),
@@ -342,16 +362,11 @@ def attention_workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16, max_q_le
 
 def _general_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, q_start,
                   max_q_len, sinks, window, k_scale, v_scale, workspace, stream):
-    kvd = _kv_dtype(k_cache)
+    kvd, NB, BS, Hkv, D2 = _cache_args(k_cache, v_cache, k_scale, v_scale)
     _need(q, "q", torch.bfloat16, 3)
     _need(out, "out", torch.bfloat16, 3)
-    _need(k_cache, "k_cache", k_cache.dtype, 4)
-    _need(v_cache, "v_cache", k_cache.dtype, 4)
     _need(block_tables, "block_tables", torch.int32, 2)
     _need(context_lens, "context_lens", torch.int32, 1)
-    if kvd != KV_BF16:
-        _need(k_scale, "k_scale", torch.float32, 2)
-        _need(v_scale, "v_scale", torch.float32, 2)
     B = context_lens.shape[0]
     if q_start is not None:
         _need(q_start, "q_start", torch.int32, 1)
@@ -360,12 +375,13 @@ def _general_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, q
     elif q.shape[0] != B:
         raise ValueError("without q_start, q has one row per sequence")
     TQ, Hq, D = q.shape
-    NB, BS, Hkv, D2 = k_cache.shape
     MBS = block_tables.shape[1]
-    if D2 != D or v_cache.shape != k_cache.shape or tuple(out.shape) != (TQ, Hq, D):
+    if D2 != D or tuple(out.shape) != (TQ, Hq, D):
         raise ValueError("q/out/cache shapes disagree")
     if block_tables.shape[0] != B:
         raise ValueError("block_tables must have B rows")
+    _on_gpu(q=q, out=out, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+            context_lens=context_lens, q_start=q_start, k_scale=k_scale, v_scale=v_scale)
     if workspace is None or workspace.dtype != torch.uint8 or not workspace.is_cuda:
         raise ValueError("workspace must be a uint8 GPU tensor (see attention_workspace_bytes)")
     return (_ptr(q), _ptr(q_start), int(max_q_len), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
@@ -409,6 +425,7 @@ def _step_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, sc
     B, Hkv, D = q.shape[0], k_cache.shape[2], q.shape[2]
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
         raise ValueError("k_new and v_new must be [B, Hkv, D]")
+    _on_gpu(k_new=k_new, v_new=v_new)
     # (q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, ...)
     return (a[0], _ptr(k_new), _ptr(v_new)) + a[1:]
 
@@ -496,14 +513,8 @@ class PreparedAppend:
 
     def __init__(self, k_new, v_new, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None,
                  stream=None):
-        kvd = _kv_dtype(k_cache)
-        N, Hkv, D = k_new.shape
-        NB, BS = k_cache.shape[0], k_cache.shape[1]
-        for t, name in ((k_new, "k_new"), (v_new, "v_new")):
-            _need(t, name, torch.bfloat16, 3)
-        _need(slot_mapping, "slot_mapping", torch.int32, 1)
-        self._args = (_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
-                      _ptr(k_scale), _ptr(v_scale), N, Hkv, D, BS, NB, kvd, _stream(stream))
+        self._args = _append_args(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale,
+                                  stream)
         self._lib = _load()
 
     def __call__(self):
