@@ -37,6 +37,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+ARITHMETIC = ("bf16 q and KV (fp8 / int8 codes widened exactly to bf16) as MFMA operands, "
+              "softmax weights as two bf16 terms (to 2^-16), fp32 accumulation and softmax, "
+              "bf16 output")
+ARITHMETIC_VALU = "bf16 q and KV widened to fp32, fp32 FMA, fp32 softmax, bf16 output"
 
 
 def visible_keys(wl):
@@ -295,7 +299,7 @@ def general_result(args, cfg, wl, dev, nbytes):
         "metric": "KV-read GB/s per decode-attention step (1 MI355X)",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": Wm,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.description}", "kv_dtype": wl.kv_dtype,
             "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "D": wl.D, "block_size": wl.BS,
@@ -303,6 +307,7 @@ def general_result(args, cfg, wl, dev, nbytes):
             "sum_context": int(wl.lengths.sum()), "keys_seen": int(keys.sum()),
             "num_blocks": wl.NB, "kv_bytes_per_step": nbytes, "kv_cache_copies_cycled": copies,
             "step": "kv_append of the new tokens + paged_attention (partition + merge)",
+            "arithmetic": ARITHMETIC,
         },
         "roofline": {
             "bound": "hbm", "kernel": "paged_attention call (mfma_partition_kernel + merge)",
@@ -558,7 +563,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: {cfg.description}",
@@ -568,6 +573,7 @@ def main():
             "kv_bytes_per_step": nbytes, "kv_cache_copies_cycled": copies,
             "step": ("decode_step: partition with the append inside + merge"
                      if args.step == "fused" else "kv_append + partition + merge"),
+            "arithmetic": ARITHMETIC if args.kernel == "mfma" else ARITHMETIC_VALU,
         },
         "roofline": {
             "bound": "hbm",

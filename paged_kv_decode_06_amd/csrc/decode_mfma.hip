@@ -9,7 +9,8 @@
 //           (columns past G are zero)
 //   output  O^T[d][h] += sum_t V[t][d] P[h][t]        16x16x16 bf16 MFMA,
 //           A = four tokens of one head dim of the V tile, B = P^T in
-//           exactly the register layout S^T came out in
+//           exactly the register layout S^T came out in (P as two bf16
+//           terms, high and low part, one product each: P to 2^-16)
 //
 // Lane l (n = l % 16, r = l / 16) ends a score step holding S^T for tokens
 // 4r..4r+3 of the tile and column n, which is the B-operand layout of the
@@ -463,6 +464,16 @@ void mfma_partition_kernel(const AttnParams p) {
   constexpr int NP = NewRows<S>::NP, CH = NewRows<S>::CH;
   static_assert(!(GEN && ROPE), "RoPE is fused into the decode step only");
   static_assert(NCT == 1 || (NCT == 2 && GEN && HG == 1), "two column tiles: generalised, one head");
+  // P enters the PV product as two bf16 parts (see below).  When the columns
+  // fit in 8 of the 16, column n + 8 repeats column n's query and carries
+  // the low part, so one product covers both and the halves are added once
+  // per piece; otherwise each part has a product of its own.  The choice
+  // goes by G (at most 4: a unit of either size fits in 8 columns), so one-
+  // and two-head units of a group sum alike; the generalised instantiation
+  // takes it when the call's columns fit too (one query per sequence).
+  constexpr bool DUP_OK = NCT == 1 && G <= 4;
+  constexpr bool ALWAYS_DUP = DUP_OK && !GEN;
+  const bool dup = ALWAYS_DUP || (DUP_OK && p.cols <= 8);   // (wave-uniform)
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
@@ -534,7 +545,7 @@ void mfma_partition_kernel(const AttnParams p) {
     int col_q[NCT], col_h[NCT], lim_n[NCT], lo_n[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + n;
+      const int c = dup ? (n & 7) : 16 * ct + n;   // (dup: column n + 8 repeats column n)
       col_q[ct] = c / UG;
       col_h[ct] = g0 * G + c % UG;
       lim_n[ct] = c < ncol ? L - ql + col_q[ct] : -1;
@@ -552,7 +563,7 @@ void mfma_partition_kernel(const AttnParams p) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (16 * ct + n < ncol) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
+        if ((dup ? (n & 7) : 16 * ct + n) < ncol) v = *reinterpret_cast<const uint4*>(qrow + 32 * kk);
         qB[ct][kk] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
@@ -714,7 +725,7 @@ void mfma_partition_kernel(const AttnParams p) {
           }
         }
         const float c = S::Q8 ? p.scale_log2 * ksc : p.scale_log2;
-        short4_t pb[NCT];
+        short4_t pb[NCT], pl[NCT];   // P^T in two bf16 parts (high, low)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           // rows past a_rel are in column n's future (decode: past the history)
@@ -747,12 +758,21 @@ void mfma_partition_kernel(const AttnParams p) {
               for (int i = 0; i < 4; ++i) O[ct][nb][i] *= alpha;
           }
           // P^T as the B operand: lane (n, r) holds column n, tokens 4r..4r+3,
-          // the layout S^T came out in
+          // the layout S^T came out in.  The weight x goes in as two bf16
+          // terms, hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in
+          // fp32), so the product sees x to 2^-16 relative instead of bf16's
+          // 2^-8: with few keys of large, cancelling values a single bf16
+          // rounding of P could move the output by 2^-8 sum_t p_t |v_t|.
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float pr = fast_exp2(s[ct][i] - m_run[ct]);
             l_run[ct] += pr;
-            pb[ct][i] = bf16_bits(S::Q8 ? pr * vsc : pr);
+            const float x = S::Q8 ? pr * vsc : pr;
+            const __bf16 hi = (__bf16)x;
+            const short lo = bf16_bits(x - (float)hi);
+            // (dup: the lanes of columns 8..15 carry the low part)
+            pb[ct][i] = dup && n >= 8 ? lo : __builtin_bit_cast(short, hi);
+            if constexpr (!ALWAYS_DUP) pl[ct][i] = lo;
           }
         }
 
@@ -765,11 +785,15 @@ void mfma_partition_kernel(const AttnParams p) {
         if (new_tile) take_new_row<S>(new_rows + 16 * CH, tile, live - 1, lane);
 #pragma unroll
         for (int j = 0; j < HG; ++j) {
-          short4_t pj[NCT];
+          short4_t pj[NCT], plj[NCT];
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             pj[ct] = pb[ct];
-            if (HG > 1 && mem != j) pj[ct] = short4_t{0, 0, 0, 0};
+            if constexpr (!ALWAYS_DUP) plj[ct] = pl[ct];
+            if (HG > 1 && mem != j) {
+              pj[ct] = short4_t{0, 0, 0, 0};
+              if constexpr (!ALWAYS_DUP) plj[ct] = short4_t{0, 0, 0, 0};
+            }
           }
           // every V operand of this kv head first, then the products (the
           // reads stay pipelined whatever the register pressure elsewhere)
@@ -778,11 +802,22 @@ void mfma_partition_kernel(const AttnParams p) {
           for (int nb = 0; nb < NBN; ++nb)   // (C-style cast: generic -> LDS address space)
             vA[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (lds_short4_t*)(tile + v_rd + 2 * D * j + 32 * nb));
+          if (ALWAYS_DUP || dup) {
 #pragma unroll
-          for (int nb = 0; nb < NBN; ++nb)
+            for (int nb = 0; nb < NBN; ++nb)
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-              O[ct][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj[ct], O[ct][nb], 0, 0, 0);
+              for (int ct = 0; ct < NCT; ++ct)
+                O[ct][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj[ct], O[ct][nb], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb)
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct)
+                O[ct][nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    vA[nb], plj[ct],
+                    __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vA[nb], pj[ct], O[ct][nb], 0, 0, 0),
+                    0, 0, 0);
+          }
         }
       }
     }
@@ -794,6 +829,12 @@ void mfma_partition_kernel(const AttnParams p) {
                         S::Q8 ? p.v_scale_w + new_sslot : nullptr);
 
     // ---- finish the piece ---------------------------------------------------
+    if (dup) {   // column n's high-part sum plus column n + 8's low-part sum
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[0][nb][i] += __shfl_xor(O[0][nb][i], 8);
+    }
     const int seg = b * U + pc.u;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {

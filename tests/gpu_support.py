@@ -111,24 +111,15 @@ def tolerance_bar(ref: np.ndarray, kv_dtype: str) -> np.ndarray:
     assert_attention_close)."""
     if kv_dtype == "fp8":
         return np.full(ref.shape, FP8_ATOL)
-    if kv_dtype == "int8":
-        return INT8_ATOL + BF16_RTOL * np.abs(ref)
     return BF16_ATOL + BF16_RTOL * np.abs(ref)
 
 
-# int8: the largest value a V code holds in the generated caches (127 times
-# the largest scale, 0.02); the bar is 2^-8 of it plus the bf16 relative term.
-INT8_VMAX = 127 * 0.02
-INT8_ATOL = INT8_VMAX * 2.0 ** -8
-
-
 def assert_attention_close(gpu: np.ndarray, ref: np.ndarray, kv_dtype: str, what: str = ""):
-    """bf16 cache: |gpu - ref| <= 4e-3 + 8e-3 |ref|; fp8: <= 3e-2 absolute;
-    int8: <= 2^-8 vmax + 8e-3 |ref|.  The int8 bar is derived from the
-    arithmetic: codes and scales are exact inputs to both sides, and the GPU
-    rounds the softmax weights to bf16 (relative 2^-9) before the PV
-    product, which can move the output by up to 2^-9 max|v| when the
-    roundings align; doubled, plus the bf16 rounding of the output."""
+    """bf16 and int8 caches: |gpu - ref| <= 4e-3 + 8e-3 |ref| elementwise;
+    fp8: <= 3e-2 absolute (both against the oracle on the stored values: the
+    dequantised codes for fp8 and int8).  The int8 cache is held to the bf16
+    bar: its codes and scales are exact inputs to both sides, as bf16 values
+    are."""
     assert gpu.shape == ref.shape
     assert np.isfinite(gpu).all(), f"{what}: non-finite output"
     err = np.abs(gpu - ref)

@@ -174,17 +174,18 @@ def test_a_sequence_without_queries(Hq):
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_verify4", "long_context_window", "mixed_70b_verify4"])
-def test_full_configuration_sampled(name):
+def test_full_configuration(name):
+    """The full-size generalised workloads: every query row of every sequence
+    against the oracle."""
     say(f"config {name}")
     wl = W.make_config_workload(name, device=DEV, poison=True)
-    L = wl.lengths
-    seqs = sorted({0, wl.B - 1, int(np.argmax(L)), int(np.argmin(L))})
-    host = GS.GeneralHost(wl, seqs)
+    host = GS.GeneralHost(wl)
     out = GS.general_step(wl)
     torch.cuda.synchronize()
     host.append()
     idx = torch.from_numpy(host.old_blocks).to(DEV)
     assert np.array_equal(W.cache_host(wl.k_cache.index_select(0, idx)), host.k)
+    assert np.array_equal(W.cache_host(wl.v_cache.index_select(0, idx)), host.v)
     ref = host.attention()
     gpu = GS.bf16_to_f64(out)[host.rows]
     GS.assert_attention_close(gpu, ref, wl.kv_dtype, name)
