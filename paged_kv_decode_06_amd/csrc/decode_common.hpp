@@ -74,33 +74,40 @@ __device__ __forceinline__ int seq_pages(const AttnParams& p, int b, int BS) {
   return seq_range(seq_length(p, b, BS), seq_queries(p, b), p.sinks, p.window, BS).n;
 }
 
-// Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]).
-// Called by every thread of the workgroup.
-__device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
-                                    int32_t* s_tmp) {
+// Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]); with
+// s_len non-NULL also each sequence's context length as given (s_len[0..B)).
+// Called by every thread of the workgroup.  Each thread sums the pages of a
+// slice of sequences; the slices' sums are scanned within each wave by lane
+// shifts, and the waves' totals are added through LDS (one barrier).
+__device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre, int32_t* s_tmp,
+                                    int32_t* s_len) {
   const int B = p.B;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
+  const int lane = tid & (kWave - 1);
   const int per = (B + nt - 1) / nt;
   const int b0 = tid * per;
   const int b1 = min(B, b0 + per);
   int sum = 0;
-  for (int b = b0; b < b1; ++b) sum += seq_pages(p, b, BS);
-  s_tmp[tid] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the per-thread sums
-  for (int off = 1; off < nt; off <<= 1) {
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
+  for (int b = b0; b < b1; ++b) {
+    if (s_len != nullptr) s_len[b] = p.context_lens[b];
+    sum += seq_pages(p, b, BS);
   }
-  int run = tid == 0 ? 0 : s_tmp[tid - 1];
+  int incl = sum;   // inclusive scan of the slice sums within the wave
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) s_tmp[tid / kWave] = incl;
+  __syncthreads();
+  int run = incl - sum;
+  for (int w = 0; w < tid / kWave; ++w) run += s_tmp[w];
   for (int b = b0; b < b1; ++b) {
     s_pre[b] = run;
     run += seq_pages(p, b, BS);
   }
-  if (tid == nt - 1) s_pre[B] = s_tmp[nt - 1];
+  if (tid == nt - 1) s_pre[B] = run;
   __syncthreads();
 }
 

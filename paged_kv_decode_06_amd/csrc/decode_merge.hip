@@ -21,25 +21,36 @@ namespace {
 // Merge, one workgroup per (sequence, unit) run and 16 columns: the run's
 // shares are rows k0 + seg .. k1 + seg, each holding the unit's `cols`
 // columns (more than 16: a second workgroup, blockIdx.y = 1, takes columns
-// 16..).  Thread t owns dims 4 (t % TPR) .. + 3 of column 16 blockIdx.y +
-// t / TPR and folds in every share of
-// the run itself, kBatch at a time: each share's (m, l) and o are loaded
-// together (one wait on memory per batch) and the running max is rescaled
-// when a batch brings a larger m.  The run's prefix sums and split are read
-// once for all its columns.
-template <int D>
-__global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams p, int G) {
+// 16..).  The workgroup is NGRP groups of wcols * D / 4 threads; in a group,
+// thread t owns dims 4 (t % TPR) .. + 3 of column 16 blockIdx.y + t / TPR,
+// and group g folds in shares g, g + NGRP, ..., kBatch at a time: each
+// share's (m, l) and o are loaded together (one wait on memory per batch)
+// and the running max is rescaled when a batch brings a larger m.  The
+// groups then meet in LDS.  With NGRP groups a run of up to NGRP * kBatch
+// shares takes one trip to memory after the prefix sums (a run of 8 columns
+// has two groups: the B64 Llama-shaped step's runs have about 9 shares).
+// The run's prefix sums and split are read once for all its columns.
+template <int D, int NGRP>
+__global__ __launch_bounds__(NGRP * 8 * D / 4 > 16 * D / 4 ? NGRP * 8 * D / 4 : 16 * D / 4)
+void merge_seg_kernel(const AttnParams p, int G) {
   constexpr int TPR = D / 4;                   // threads per column (4 dims each)
   constexpr int kBatch = 8;
+  __shared__ float s_acc[NGRP > 1 ? NGRP : 1][NGRP > 1 ? 8 : 1][NGRP > 1 ? D : 1];
+  __shared__ float s_den[NGRP > 1 ? NGRP : 1][NGRP > 1 ? 8 : 1];
+  __shared__ float s_max[NGRP > 1 ? NGRP : 1][NGRP > 1 ? 8 : 1];
+  const int gthreads = blockDim.x / NGRP;      // threads of one group (wcols * TPR)
+  const int grp = threadIdx.x / gthreads;
+  const int t = threadIdx.x % gthreads;
   const int U = p.Hkv / p.hg;
   const int seg = blockIdx.x;                  // b U + u
   const int b = seg / U, u = seg % U;
-  const int n = 16 * blockIdx.y + threadIdx.x / TPR;   // column
-  const int d4 = (threadIdx.x % TPR) * 4;
+  const int cl = t / TPR;                      // column within the workgroup
+  const int n = 16 * blockIdx.y + cl;          // column
+  const int d4 = (t % TPR) * 4;
   const int C = p.cols;
   const int UG = p.hg * G;
   const int qi = n / UG;
-  if (n >= C || qi >= seq_queries(p, b)) return;
+  const bool live = n < C && qi < seq_queries(p, b);
   const int h = u * UG + n % UG;
   const int32_t* __restrict__ pre = p.ws_pre;
   const int pre_B = pre[p.B], pre_b = pre[b], pre_b1 = pre[b + 1];
@@ -47,8 +58,8 @@ __global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams 
   const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
   uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D + d4;
   if (n_b == 0) {                              // empty history: defined as 0
-    *reinterpret_cast<uint2*>(op) = make_uint2(0, 0);
-    return;
+    if (live && grp == 0) *reinterpret_cast<uint2*>(op) = make_uint2(0, 0);
+    return;                                    // (the whole workgroup)
   }
   const WorkSplit split = make_split(U * pre_B, p.total_waves);
   const int start = U * pre_b + u * n_b;
@@ -63,15 +74,16 @@ __global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams 
   float M = -FLT_MAX;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
-  for (int i0 = 0; i0 < P; i0 += kBatch) {
+  for (int i0 = grp; i0 < P; i0 += NGRP * kBatch) {
     float2 mlv[kBatch];
     float4 o[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k * NGRP;
       mlv[k] = make_float2(-FLT_MAX, 0.0f);
       o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i0 + k < P) {
-        const int64_t row = (row0 + i0 + k) * C + n;
+      if (live && i < P) {
+        const int64_t row = (row0 + i) * C + n;
         mlv[k] = *reinterpret_cast<const float2*>(ml + row * 2);
         o[k] = *reinterpret_cast<const float4*>(po + row * D + d4);
       }
@@ -96,6 +108,31 @@ __global__ __launch_bounds__(16 * D / 4) void merge_seg_kernel(const AttnParams 
     }
     M = mb;
   }
+  if constexpr (NGRP > 1) {   // the groups meet in LDS, each brought to the common max
+    *reinterpret_cast<float4*>(&s_acc[grp][cl][d4]) = acc;
+    if (d4 == 0) {
+      s_den[grp][cl] = den;
+      s_max[grp][cl] = M;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    float Mt = s_max[0][cl];
+#pragma unroll
+    for (int q = 1; q < NGRP; ++q) Mt = fmaxf(Mt, s_max[q][cl]);
+    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    den = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NGRP; ++q) {
+      const float a = fast_exp2(s_max[q][cl] - Mt);
+      const float4 v = *reinterpret_cast<const float4*>(&s_acc[q][cl][d4]);
+      acc.x = fmaf(a, v.x, acc.x);
+      acc.y = fmaf(a, v.y, acc.y);
+      acc.z = fmaf(a, v.z, acc.z);
+      acc.w = fmaf(a, v.w, acc.w);
+      den = fmaf(a, s_den[q][cl], den);
+    }
+  }
+  if (!live) return;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // 0: the query sees no key
   *reinterpret_cast<uint2*>(op) =
       make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
@@ -237,16 +274,25 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  // (a workgroup per run and 16 columns, D / 4 threads a column)
+  // (a workgroup per run and 16 columns, D / 4 threads a column; runs of at
+  // most 8 columns get two thread groups, which split the shares)
   if (p.cols < 1 || p.cols > 32) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)), (unsigned)((p.cols + 15) / 16));
   const int wcols = p.cols < 16 ? p.cols : 16;
-  if (D == 128)
-    hipLaunchKernelGGL(merge_seg_kernel<128>, grid, dim3(wcols * 32), 0, stream, p, G);
-  else if (D == 64)
-    hipLaunchKernelGGL(merge_seg_kernel<64>, grid, dim3(wcols * 16), 0, stream, p, G);
-  else
+  const bool two = wcols <= 8;
+  if (D == 128) {
+    if (two)
+      hipLaunchKernelGGL((merge_seg_kernel<128, 2>), grid, dim3(2 * wcols * 32), 0, stream, p, G);
+    else
+      hipLaunchKernelGGL((merge_seg_kernel<128, 1>), grid, dim3(wcols * 32), 0, stream, p, G);
+  } else if (D == 64) {
+    if (two)
+      hipLaunchKernelGGL((merge_seg_kernel<64, 2>), grid, dim3(2 * wcols * 16), 0, stream, p, G);
+    else
+      hipLaunchKernelGGL((merge_seg_kernel<64, 1>), grid, dim3(wcols * 16), 0, stream, p, G);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -478,7 +478,8 @@ void mfma_partition_kernel(const AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
   int32_t* s_tmp = s_pre + p.B + 1;                          // [blockDim]
-  build_prefix(p, BS, s_pre, s_tmp);
+  int32_t* s_len = len_lds_entries(p.B) ? s_tmp + kAttnBlockThreads : nullptr;   // [B]
+  build_prefix(p, BS, s_pre, s_tmp, s_len);
 
   const int Hkv = p.Hkv;
   const int U = Hkv / HG;                  // units per sequence
@@ -490,7 +491,7 @@ void mfma_partition_kernel(const AttnParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave_in_block = threadIdx.x >> 6;
   const int wave = blockIdx.x * kAttnWavesPerBlock + wave_in_block;
-  const size_t pre_bytes = (sizeof(int32_t) * ((size_t)p.B + 1 + kAttnBlockThreads) + 15) & ~size_t(15);
+  const size_t pre_bytes = (sizeof(int32_t) * prefix_lds_words(p.B) + 15) & ~size_t(15);
   constexpr int WAVE_LDS = 16 * PITCH + 32 * CH;   // staged tile + the new K and V unit rows (bf16)
   unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * WAVE_LDS;
   unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
@@ -525,7 +526,7 @@ void mfma_partition_kernel(const AttnParams p) {
     pc.j0 = __builtin_amdgcn_readfirstlane(pc.j0);
     pc.j1 = __builtin_amdgcn_readfirstlane(pc.j1);
     const int b = pc.b, g0 = pc.u * HG;   // the unit's first kv head
-    const int L_in = p.context_lens[b];
+    const int L_in = s_len != nullptr ? s_len[b] : p.context_lens[b];
     const int L = min(max(L_in, 0), p.MBS * BS);
     // a length outside [1, MBS * BS] breaks the contract: no append then
     // (the decode step is one query per sequence: never the GEN instantiation)

@@ -92,10 +92,21 @@ constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
 constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
 constexpr int kMaxBatch = 8192;          // sequence prefix sums live in LDS
 
-// LDS of the sequence prefix sums (plus the scan scratch) for B sequences.
-inline size_t prefix_lds_bytes(int B) {
-  return sizeof(int32_t) * ((size_t)B + 1 + kAttnBlockThreads);
+// Batches up to this size keep their context lengths in LDS beside the
+// prefix sums (the partition kernels then read a run's length there instead
+// of from memory); larger ones would cost occupancy.
+constexpr int kLenLdsMax = 2048;
+__host__ __device__ inline int len_lds_entries(int B) { return B <= kLenLdsMax ? B : 0; }
+
+// 32-bit words of LDS the sequence prefix sums take: s_pre [B + 1], the
+// scan's scratch [kAttnBlockThreads], the lengths [len_lds_entries(B)].
+__host__ __device__ inline size_t prefix_lds_words(int B) {
+  return (size_t)B + 1 + kAttnBlockThreads + len_lds_entries(B);
 }
+
+// LDS of the sequence prefix sums (plus the scan scratch and the cached
+// lengths) for B sequences.
+inline size_t prefix_lds_bytes(int B) { return sizeof(int32_t) * prefix_lds_words(B); }
 
 // The two partition-kernel variants.  Launchers return hipErrorInvalidValue
 // for an unsupported (D, BS, G, kind) combination; *_blocks_per_cu give the
