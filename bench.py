@@ -20,7 +20,12 @@ with a HIP event pair around every partition launch (recorded on the stream
 the kernel runs on), whose mean gives the roofline entry.  The oracle timed
 on the host cores gives the CPU baseline.
 
+The default run also times every other configuration's step (fewer
+steps each) for `detail.configs`, and a streaming read of a 2 GiB buffer
+(pkv_read_probe) for the device's read ceiling.
+
   python bench.py [--steps K] [--warmup W] [--config NAME] [--step fused|two-call] [--no-cpu]
+                  [--no-configs] [--only-step]
 """
 from __future__ import annotations
 
@@ -105,11 +110,21 @@ def measured_traffic(config: str, kernel: str):
     return None
 
 
-def cpu_baseline(wl, budget_s=10.0, max_runs=100):
-    """The oracle, as it stands, on the host cores: one full step's attention
-    over the same batch (after the oracle's own append of the step's tokens,
-    in position order), repeated until about `budget_s` of wall time has
-    passed (at least once, at most `max_runs` times)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_step_seconds(wl, nthreads: int, budget_s: float, max_runs: int):
+    """Mean wall time of the oracle's attention over the whole batch (after
+    its own append of the step's tokens, in position order), repeated until
+    about `budget_s` of wall time has passed; (mean seconds, runs)."""
     import oracle
     from paged_kv_decode_06_amd import workloads as W
 
@@ -124,11 +139,6 @@ def cpu_baseline(wl, budget_s=10.0, max_runs=100):
     q = W.bf16_bits(wl.q)
     cl = wl.lengths.astype(np.int32)
     general = int(wl.q_lens.max()) > 1 or wl.window > 0
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except AttributeError:
-        threads = os.cpu_count() or 1
-    threads = min(threads, int(os.environ.get("OMP_NUM_THREADS", threads) or threads))
     times = []
     t_all = time.perf_counter()
     while True:
@@ -136,18 +146,45 @@ def cpu_baseline(wl, budget_s=10.0, max_runs=100):
         if general:
             oracle.paged_attention(q, k, v, wl.block_tables_np, cl, wl.scale, q_start=wl.q_start_np,
                                    sinks=wl.sinks, window=wl.window, k_scale=ks, v_scale=vs,
-                                   nthreads=threads)
+                                   nthreads=nthreads)
         else:
             oracle.paged_decode_attention(q, k, v, wl.block_tables_np, cl, wl.scale, k_scale=ks,
-                                          v_scale=vs, nthreads=threads)
+                                          v_scale=vs, nthreads=nthreads)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_all > budget_s or len(times) >= max_runs:
             break
-    t = sum(times) / len(times)
-    return {"value": round(kv_bytes(wl) / t / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {wl.name} batch (B={wl.B}), fp64 attention of one step, "
-                      f"{len(times)} run(s), mean {t:.3f} s per step"}
+    return sum(times) / len(times), len(times)
+
+
+def cpu_baseline(wl, budget_s=10.0, max_runs=100, single_thread=True):
+    """The oracle, as it stands, on the host cores: one full step's attention
+    over the same batch, repeated for about `budget_s` of wall time on every
+    core the process may use; beside it the same oracle on one thread, for
+    this batch and for the tiny configuration (one run or more each)."""
+    from paged_kv_decode_06_amd import workloads as W
+
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count() or 1
+    threads = min(threads, int(os.environ.get("OMP_NUM_THREADS", threads) or threads))
+    t, runs = oracle_step_seconds(wl, threads, budget_s, max_runs)
+    res = {"value": round(kv_bytes(wl) / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"full {wl.name} batch (B={wl.B}), fp64 attention of one step, "
+                     f"{runs} run(s), mean {t:.3f} s per step",
+           "cpu_model": cpu_model()}
+    if single_thread:
+        one = {}
+        t1, r1 = oracle_step_seconds(wl, 1, 0.0, 1)
+        one[wl.name] = {"s_per_step": round(t1, 4), "GB/s": round(kv_bytes(wl) / t1 / 1e9, 4),
+                        "runs": r1}
+        tiny = W.make_config_workload("tiny", device="cpu")
+        tt, rt = oracle_step_seconds(tiny, 1, 1.0, 1000)
+        one["tiny"] = {"s_per_step": round(tt, 7), "GB/s": round(kv_bytes(tiny) / tt / 1e9, 4),
+                       "runs": rt}
+        res["single_thread"] = one
+    return res
 
 
 class TimingEvents:
@@ -281,6 +318,8 @@ def general_result(args, cfg, wl, dev, nbytes):
             run(Wm + i)
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+        if args.only_step:
+            return only_step_line(args, cfg, nbytes, ms_per_step)
         tev = TimingEvents(2 * K)   # (timing-only events: no system-scope fence)
         for i in range(K):
             apps, att = steps[(Wm + i) % copies]
@@ -324,6 +363,127 @@ def general_result(args, cfg, wl, dev, nbytes):
     return result
 
 
+def only_step_line(args, cfg, nbytes, ms_per_step):
+    """The line of an --only-step run (for profiler runs: the timed steps and
+    nothing else on the GPU)."""
+    return {"metric": "KV-read GB/s per decode-attention step (1 MI355X)",
+            "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5), "config": {"workload": cfg.name},
+            "only_step": True}
+
+
+def decode_detail(name, args, dev):
+    """One decode configuration for detail.configs: K one-call steps (wall
+    clock), then the same K steps with timing-only events around the
+    partition launch (append inside) and the merge."""
+    import torch
+    from paged_kv_decode_06_amd import ops
+    from paged_kv_decode_06_amd import workloads as W
+
+    wl = W.make_config_workload(name, device=dev, poison=False)
+    nbytes = kv_bytes(wl)
+    kvd = {"bf16": ops.KV_BF16, "fp8": ops.KV_FP8, "int8": ops.KV_INT8}[wl.kv_dtype]
+    pool_bytes = 2 * wl.k_cache.numel() * wl.k_cache.element_size()
+    copies = min(16, max(2, int(np.ceil(2.0e9 / pool_bytes))))   # (tiny: latency-bound anyway)
+    stream = torch.cuda.Stream(device=dev)
+    ws = torch.zeros(ops.workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.D, wl.BS, wl.MBS, kvd),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(wl.q)
+    caches = [(wl.k_cache, wl.v_cache, wl.k_scale, wl.v_scale)]
+    for _ in range(copies - 1):
+        caches.append(tuple(None if t is None else t.clone() for t in caches[0]))
+    steps = [ops.PreparedStep(wl.q, wl.k_new, wl.v_new, kc, vc, wl.block_tables, wl.context_lens,
+                              wl.scale, out, ks, vs, ws, stream=stream)
+             for kc, vc, ks, vs in caches]
+    K, Wm = args.detail_steps, max(3, args.warmup // 2)
+    with torch.cuda.stream(stream):
+        settle([lambda i: steps[i % copies]()], args.settle)
+        for i in range(Wm):
+            steps[i % copies]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            steps[(Wm + i) % copies]()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / K
+        tev = TimingEvents(4 * K)
+        for i in range(K):
+            st = steps[(Wm + i) % copies]
+            tev.record(4 * i, stream)
+            st.partition()
+            tev.record(4 * i + 1, stream)
+            tev.record(4 * i + 2, stream)
+            st.merge()
+            tev.record(4 * i + 3, stream)
+        torch.cuda.synchronize()
+    part = float(np.mean([tev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]))
+    merge = float(np.mean([tev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]))
+    tev.close()
+    res = {"kv_bytes_per_step": nbytes, "kv_dtype": wl.kv_dtype,
+           "shape": f"B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} D{wl.D} BS{wl.BS}",
+           "step_us": round(ms * 1e3, 2), "step_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "step_pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "partition_us": round(part * 1e3, 2), "merge_us": round(merge * 1e3, 2),
+           "partition_frac": round(nbytes / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "seq_heads_per_s": round(wl.B * wl.Hq / (ms * 1e-3), 1),
+           "steps": K, "kernel_heads_per_wave": ops.decode_unit_heads(wl.B, wl.Hq, wl.Hkv, wl.D,
+                                                                      wl.BS, kvd)}
+    del steps, caches, ws, out, wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def general_detail(name, args, dev):
+    """One generalised configuration for detail.configs (general_result with
+    the detail step count)."""
+    import torch
+    from paged_kv_decode_06_amd import workloads as W
+
+    cfg = W.CONFIGS[name]
+    wl = W.make_config_workload(name, device=dev, poison=False)
+    nbytes = kv_bytes(wl)
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.only_step = args.detail_steps, max(3, args.warmup // 2), False
+    r = general_result(sub, cfg, wl, dev, nbytes)
+    res = {"kv_bytes_per_step": nbytes, "kv_dtype": wl.kv_dtype,
+           "shape": (f"B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} D{wl.D} BS{wl.BS} q_len {cfg.q_len} "
+                     f"window {cfg.window} sinks {cfg.sinks}"),
+           "step_us": round(r["ms_per_step"] * 1e3, 2), "step_GBs": r["value"],
+           "step_pct_peak": r["detail"]["pct_hbm_peak_step"],
+           "attention_call_us": r["detail"]["attention_call_us_mean"],
+           "attention_call_frac": r["roofline"]["frac"], "steps": sub.steps}
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def probe_ceiling(dev, nbytes=2 << 30, reps=20):
+    """Read bandwidth of pkv_read_probe over a 2 GiB buffer (timing-only
+    events around each of `reps` launches, after 3 untimed ones)."""
+    import torch
+    from paged_kv_decode_06_amd import ops
+
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(ops.read_probe_waves(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    tev = TimingEvents(2 * reps)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            ops.read_probe(buf, sink, stream=stream)
+        for i in range(reps):
+            tev.record(2 * i, stream)
+            ops.read_probe(buf, sink, stream=stream)
+            tev.record(2 * i + 1, stream)
+        torch.cuda.synchronize()
+    ms = float(np.mean([tev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]))
+    tev.close()
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes, "us": round(ms * 1e3, 2),
+            "waves": ops.read_probe_waves()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -338,6 +498,13 @@ def main():
                     help="partition-kernel variant")
     ap.add_argument("--step", choices=["fused", "two-call"], default="fused",
                     help="decode_step (one call) or kv_append + attention (two calls)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (detail.configs) and the read probe")
+    ap.add_argument("--detail-steps", type=int, default=20,
+                    help="timed steps per configuration in detail.configs")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the selected step only (no events, comparisons, other "
+                         "configurations or CPU baseline): for profiler runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reads 1 GiB, writes "
                          "1 GiB) a few times, to scale hardware byte counters")
@@ -369,7 +536,7 @@ def main():
     nbytes = kv_bytes(wl)
     if cfg.q_len > 1 or cfg.window > 0:
         result = general_result(args, cfg, wl, dev, nbytes)
-        if not args.no_cpu:
+        if not args.only_step and not args.no_cpu:
             result["cpu_baseline"] = cpu_baseline(wl)
         print(json.dumps(result), flush=True)
         return
@@ -423,6 +590,9 @@ def main():
             main_run(i)
         # timed region: exactly K steps, nothing else in the stream
         ms_per_step = timed(main_run, Wm)
+        if args.only_step:
+            print(json.dumps(only_step_line(args, cfg, nbytes, ms_per_step)), flush=True)
+            return
         ms_per_step_other = timed(other_run, Wm)
 
     # the same K steps again with a HIP event pair around every partition
@@ -603,6 +773,24 @@ def main():
             "kv_heads_per_wave": unit_heads,
         },
     }
+    if not args.no_configs:
+        # every other configuration, fewer steps each, and the read ceiling
+        probe = probe_ceiling(dev)
+        result["detail"]["read_probe"] = probe
+        result["detail"]["partition_pct_of_read_probe"] = round(100 * achieved / probe["GB/s"], 2)
+        configs = {}
+        for name in W.CONFIG_ORDER:
+            if name == args.config:
+                continue
+            c = W.CONFIGS[name]
+            if c.q_len > 1 or c.window > 0:
+                configs[name] = general_detail(name, args, dev)
+            else:
+                configs[name] = decode_detail(name, args, dev)
+            if name != "tiny":
+                frac = configs[name].get("partition_frac", configs[name].get("attention_call_frac"))
+                configs[name]["pct_of_read_probe"] = round(100 * frac * HBM_PEAK_GBS / probe["GB/s"], 2)
+        result["detail"]["configs"] = configs
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(result), flush=True)

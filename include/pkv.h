@@ -340,6 +340,19 @@ int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
  * unsupported.  Informational. */
 int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
 
+/* Streaming-read probe: the read bandwidth the device reaches with nothing
+ * but 16-byte non-temporal loads, the ceiling the attention kernels' KV
+ * reads are measured against (the "Decode Phase" glossary bounds a decode
+ * step by the KV cache bytes over the memory bandwidth).  Reads every whole
+ * 1 KB unit of `buf` (device memory, 16-byte aligned; a tail under 1 KB is
+ * not read) with a persistent grid, and stores one XOR fold per wave in
+ * sink (device memory, at least pkv_read_probe_waves() uint32 words;
+ * PKV_ERR_WORKSPACE if smaller).  bytes == 0 is a no-op.  Asynchronous on
+ * `stream`. */
+int pkv_read_probe_waves(void);
+int pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                   void* stream);
+
 /* mode 0 (default): units as above; mode 1: one kv head per wave always.
  * Process-wide, read at the start of every attention call and workspace
  * query, like pkv_select_partition_kernel (switch only between calls, size
@@ -347,6 +360,19 @@ int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype);
  * selects mode 1 when the library loads.  PKV_ERR_UNSUPPORTED for another
  * value. */
 int pkv_select_unit_heads(int mode);
+
+/* mode 1 (default): the waves of a partition workgroup, which stream
+ * consecutive pieces of the work, combine their partial results for the
+ * runs they share in LDS, so a run inside a workgroup's range is finished
+ * there and one crossing its edge leaves one partial row per workgroup
+ * instead of one per wave (taken by MFMA calls whose partial rows have at
+ * most 8 columns, i.e. kv heads per wave x G x queries per sequence <= 8,
+ * and B <= 1024); mode 0: one partial row per wave always.  The result
+ * differs only in floating-point summation order.  Process-wide, read at
+ * the start of every attention call and workspace query, like
+ * pkv_select_unit_heads.  PKV_SHARE_COMBINE=0 in the environment selects
+ * mode 0 when the library loads.  PKV_ERR_UNSUPPORTED for another value. */
+int pkv_select_share_combine(int mode);
 
 /* Partition-kernel variants.  Both compute the same attention; MFMA (the
  * default) puts the GQA group on the matrix cores, VALU uses fp32 vector

@@ -61,10 +61,13 @@ void merge_seg_kernel(const AttnParams p, int G) {
     if (live && grp == 0) *reinterpret_cast<uint2*>(op) = make_uint2(0, 0);
     return;                                    // (the whole workgroup)
   }
+  // (pieces, or with the workgroup combine the workgroups' ranges of
+  // kAttnWavesPerBlock pieces, are the share rows' owners)
   const WorkSplit split = make_split(U * pre_B, p.total_waves);
+  const int owner = p.wgc ? kAttnWavesPerBlock : 1;
   const int start = U * pre_b + u * n_b;
-  const int k0 = piece_of(split, start);
-  const int k1 = piece_of(split, start + n_b - 1);
+  const int k0 = piece_of(split, start) / owner;
+  const int k1 = piece_of(split, start + n_b - 1) / owner;
   if (k0 == k1) return;                        // finished by the partition kernel
   const int P = k1 - k0 + 1;
   const int64_t row0 = (int64_t)k0 + seg;
@@ -173,9 +176,10 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
     return;
   }
   const WorkSplit split = make_split(total, p.total_waves);
+  const int owner = p.wgc ? kAttnWavesPerBlock : 1;   // (share rows per workgroup: see above)
   const int start = U * pre_b + u * n_b;
-  const int k0 = piece_of(split, start);
-  const int k1 = piece_of(split, start + n_b - 1);
+  const int k0 = piece_of(split, start) / owner;
+  const int k1 = piece_of(split, start + n_b - 1) / owner;
   if (k0 == k1) return;
   const int seg = b * U + u;
   const int P = k1 - k0 + 1;

@@ -434,6 +434,87 @@ __device__ __forceinline__ void rope_rotate(const AttnParams& p, int pos, int la
   }
 }
 
+// Workgroup combine.  The waves of a workgroup stream consecutive pieces,
+// so a run that crosses the edge between two of them has its shares there:
+// the end share of the earlier piece (the run continues past it) and the
+// head share of the later one (or its only share, if the piece lies inside
+// the run).  Each wave leaves at most two shares in LDS: a head share (the
+// piece starts inside a run and finishes it) in its head slot, and an end
+// share (the piece ends inside a run) in its tile buffer, each as o
+// [kWgcMaxCols][D], then m and l [kWgcMaxCols], with a descriptor (segment,
+// starts at the run's first page, ends at its last).  After the workgroup
+// barrier the shares, in axis order, are grouped by run: a group that starts
+// at the run's first page and ends at its last is the whole run, finished
+// here (bf16 out); any other is merged into one share row of the workgroup,
+// row g + segment, for the merge kernel.  Combining is by the log-sum-exp
+// rule of the merge kernel, in a fixed order, so results stay deterministic.
+template <int D>
+constexpr int kWgcSlot = kWgcMaxCols * (D + 2) * (int)sizeof(float);
+
+template <class S, bool GEN>
+__device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* waves_lds,
+                                            int wave_lds, const int* s_desc, int U) {
+  constexpr int D = S::D, UG = S::UG, G = S::G, HG = S::HG;
+  constexpr int TPR = D / 4;                    // threads per column (4 dims each)
+  __syncthreads();
+  // the shares in axis order: wave 0's head, wave 0's end, wave 1's head, ...
+  int nsh = 0;
+  int sseg[2 * kAttnWavesPerBlock], sflg[2 * kAttnWavesPerBlock];
+  const float* sptr[2 * kAttnWavesPerBlock];
+#pragma unroll
+  for (int w = 0; w < kAttnWavesPerBlock; ++w)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int seg = s_desc[4 * w + 2 * k];
+      if (seg >= 0) {
+        unsigned char* base = waves_lds + (size_t)w * wave_lds;
+        sseg[nsh] = seg;
+        sflg[nsh] = s_desc[4 * w + 2 * k + 1];
+        sptr[nsh] = reinterpret_cast<const float*>(k == 0 ? base + 16 * S::PITCH + 32 * NewRows<S>::CH
+                                                          : base);
+        ++nsh;
+      }
+    }
+  const int t = threadIdx.x;
+  const int c = t / TPR, d4 = (t % TPR) * 4;
+  for (int i = 0; i < nsh;) {
+    int j = i;
+    while (j + 1 < nsh && sseg[j + 1] == sseg[i]) ++j;
+    const int seg = sseg[i];
+    const int b = seg / U, u = seg % U;
+    const int ql = GEN ? seq_queries(p, b) : 1;
+    if (c < UG * ql) {
+      float M = -FLT_MAX;
+      for (int k = i; k <= j; ++k) M = fmaxf(M, sptr[k][kWgcMaxCols * D + c]);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float den = 0.0f;
+      for (int k = i; k <= j; ++k) {
+        const float w = fast_exp2(sptr[k][kWgcMaxCols * D + c] - M);
+        const float4 o = *reinterpret_cast<const float4*>(sptr[k] + c * D + d4);
+        den = fmaf(w, sptr[k][kWgcMaxCols * D + kWgcMaxCols + c], den);
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
+      }
+      if ((sflg[i] & 1) && (sflg[j] & 2)) {   // the whole run: out
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // (0: the query sees no key)
+        const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;
+        uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                         ((int64_t)(r0 + c / UG) * p.Hq + u * HG * G + c % UG) * D + d4;
+        *reinterpret_cast<uint2*>(orow) =
+            make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+      } else {                                 // the workgroup's share row of the run
+        const int64_t row = (int64_t)blockIdx.x + seg;
+        const int C = p.cols;
+        *reinterpret_cast<float4*>(p.ws_o + (row * C + c) * D + d4) = acc;
+        if (d4 == 0) *reinterpret_cast<float2*>(p.ws_ml + (row * C + c) * 2) = make_float2(M, den);
+      }
+    }
+    i = j + 1;
+  }
+}
+
 // GEN: the generalised call (several queries per sequence, a window); the
 // decode instantiations (GEN = false) carry none of its per-lane state.
 // Both may serve several kv heads per wave (S::HG; the generalised call when
@@ -492,9 +573,15 @@ void mfma_partition_kernel(const AttnParams p) {
   const int wave_in_block = threadIdx.x >> 6;
   const int wave = blockIdx.x * kAttnWavesPerBlock + wave_in_block;
   const size_t pre_bytes = (sizeof(int32_t) * prefix_lds_words(p.B) + 15) & ~size_t(15);
-  constexpr int WAVE_LDS = 16 * PITCH + 32 * CH;   // staged tile + the new K and V unit rows (bf16)
-  unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * WAVE_LDS;
+  // per wave: staged tile, the new K and V unit rows (bf16) and, with the
+  // workgroup combine, a slot for the share of the run the piece starts in
+  const int wave_lds = 16 * PITCH + 32 * CH + (p.wgc ? kWgcSlot<D> : 0);
+  unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * wave_lds;
   unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
+  float* head_slot = reinterpret_cast<float*>(new_rows + 32 * CH);
+  // workgroup combine: (segment, flags) of each wave's head and end shares
+  int* s_desc = reinterpret_cast<int*>(smem + pre_bytes + (size_t)kAttnWavesPerBlock * wave_lds);
+  if (p.wgc && lane < 4) s_desc[4 * wave_in_block + lane] = -1;
 
   const int n = lane & 15;        // column of S^T and O^T (a query head); K row of the A operand
   const int r = lane >> 4;        // 4-token group of S^T rows; 4-dim group of O^T rows
@@ -855,6 +942,26 @@ void mfma_partition_kernel(const AttnParams p) {
                 make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
                            pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
         }
+      } else if (NCT == 1 && p.wgc) {
+        // the share goes to LDS for the workgroup combine: a piece ending
+        // inside the run leaves its end share in its (now free) tile buffer,
+        // one starting inside a run that it finishes in its head slot
+        const bool is_end = pc.j1 < pc.n_b;
+        float* sh = is_end ? reinterpret_cast<float*>(tile) : head_slot;
+        if (c < ncol) {
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<float4*>(sh + c * D + 16 * nb + 4 * r) =
+                make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+          if (r == 0) {
+            sh[kWgcMaxCols * D + c] = m_run[ct];
+            sh[kWgcMaxCols * D + kWgcMaxCols + c] = l_tot;
+          }
+        }
+        if (lane == 0) {
+          s_desc[4 * wave_in_block + 2 * is_end] = seg;
+          s_desc[4 * wave_in_block + 2 * is_end + 1] = (pc.j0 == 0) | (pc.j1 == pc.n_b) << 1;
+        }
       } else {
         const int64_t row = (int64_t)piece + seg;
         const int C = p.cols;
@@ -874,6 +981,8 @@ void mfma_partition_kernel(const AttnParams p) {
     x = pc.run_start + pc.j1;
   }
   });
+  if constexpr (NCT == 1)
+    if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U);
 }
 
 // Calls f(MfmaShape<D, BS, G, kind, hg>{}) for the combination given at run
@@ -921,8 +1030,10 @@ bool dispatch_mfma(int D, int BS, int G, int kind, int hg, F&& f) {
 
 int mfma_unit_heads(int G) { return kUnitHeads(G); }
 
-size_t mfma_stage_lds_bytes(int D, int hg) {
-  return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + 4 * hg * D);
+size_t mfma_stage_lds_bytes(int D, int hg, bool wgc) {
+  const size_t slot = wgc ? (size_t)kWgcMaxCols * (D + 2) * sizeof(float) : 0;
+  return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + 4 * hg * D + slot) +
+         (wgc ? 4 * kAttnWavesPerBlock * sizeof(int) : 0);
 }
 
 // Units of several kv heads run at two workgroups (8 waves) per CU: each
@@ -930,8 +1041,8 @@ size_t mfma_stage_lds_bytes(int D, int hg) {
 // (three waves per SIMD measured slower for them: see MfmaShape::WPE).
 constexpr size_t kUnitLdsFloor = 56 * 1024;
 
-static size_t mfma_lds_total(int B, int D, int hg) {
-  const size_t t = ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg);
+static size_t mfma_lds_total(int B, int D, int hg, bool wgc) {
+  const size_t t = ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg, wgc);
   return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
 
@@ -946,9 +1057,9 @@ constexpr int blocks_at(int wpe) { return wpe * 4 / kAttnWavesPerBlock; }
 // VGPRs would run 4 per SIMD, measured 13-15% slower than 3), so the grid
 // is capped at the waves per SIMD of the instantiation.
 // col_tiles = 2: the generalised instantiation with two column tiles alone.
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles) {
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, bool wgc) {
   int blocks = 0, blocks_gen = 0, cap = 0;
-  const size_t lds = mfma_lds_total(B, D, hg);
+  const size_t lds = mfma_lds_total(B, D, hg, wgc && col_tiles == 1);
   if (col_tiles == 2) {
     const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
       using S = decltype(s);
@@ -979,13 +1090,13 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_ti
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
-  const size_t lds = mfma_lds_total(p.B, D, p.hg);
+  const size_t lds = mfma_lds_total(p.B, D, p.hg, p.wgc != 0);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
   if (gen && p.rope) return hipErrorInvalidValue;
   const int cols = p.hg * G * p.max_q;
   // two column tiles: the generalised call with one kv head per wave only
   if (p.hg < 1 || p.Hkv % p.hg != 0 || cols != p.cols || cols > 32 ||
-      (cols > 16 && (!gen || p.hg != 1)))
+      (cols > 16 && (!gen || p.hg != 1)) || (p.wgc && (cols > kWgcMaxCols || kPiecesPerWave != 1)))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

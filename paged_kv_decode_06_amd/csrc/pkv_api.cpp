@@ -63,9 +63,10 @@ int cu_count(int dev) {
 // rounded up to a multiple of 1024 so that the cache stays small.  hg: kv
 // heads per wave, col_tiles: 16-column tiles per wave (MFMA only).
 int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg,
-                  int col_tiles = 1) {
+                  int col_tiles = 1, bool wgc = false) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)col_tiles << 52) |
+  const unsigned long long key = ((unsigned long long)wgc << 56) |
+                                 ((unsigned long long)col_tiles << 52) |
                                  ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
                                  ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
@@ -78,7 +79,7 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, i
     if (it != c.blocks.end()) return it->second;
   }
   const int n = path == pkv::AttnPath::kMfma
-                    ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg, col_tiles)
+                    ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg, col_tiles, wgc)
                     : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
@@ -95,11 +96,11 @@ bool supported(int D, int BS, int G, int kv_dtype) {
 
 // Persistent grid: every workgroup that fits at once on every CU.
 int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B, int hg,
-                     int col_tiles = 1) {
+                     int col_tiles = 1, bool wgc = false) {
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
-  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, col_tiles);
+  const int per_cu = blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, col_tiles, wgc);
   return ncu * per_cu;
 }
 
@@ -111,6 +112,24 @@ std::atomic<int>& unit_heads_flag() {
     return (e && std::string(e) == "1") ? 1 : 0;
   }());
   return flag;
+}
+
+// Workgroup combine of the partition kernel's shares (pkv::AttnParams::wgc):
+// on unless PKV_SHARE_COMBINE=0 is set when the library loads or
+// pkv_select_share_combine(0) switched it off; taken by MFMA calls whose share
+// rows have at most kWgcMaxCols columns and whose batch is at most
+// kWgcMaxBatch.
+std::atomic<int>& share_combine_flag() {
+  static std::atomic<int> flag([] {
+    const char* e = std::getenv("PKV_SHARE_COMBINE");
+    return (e && std::string(e) == "0") ? 0 : 1;
+  }());
+  return flag;
+}
+
+bool use_wgc(pkv::AttnPath path, int cols, int B) {
+  return path == pkv::AttnPath::kMfma && share_combine_flag().load(std::memory_order_relaxed) &&
+         cols <= pkv::kWgcMaxCols && B <= pkv::kWgcMaxBatch && pkv::kPiecesPerWave == 1;
 }
 
 // Columns (kv heads per wave * G * max_q) one partition wave serves: the 16
@@ -135,7 +154,9 @@ int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, 
   if (hg <= 1 || Hkv % hg != 0 || hg * G * max_q > kTileCols) return 1;
   int dev;
   if (current_device(&dev) != 0) return 1;
-  return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg) >= 2 ? hg : 1;
+  return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, 1, use_wgc(path, hg * G * max_q, B)) >= 2
+             ? hg
+             : 1;
 }
 
 struct AttnCall {
@@ -216,10 +237,11 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
   const int cols = hg * G * opts.max_q;
-  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols));
+  const bool wgc = use_wgc(path, cols, B);
+  const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
-  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv / hg, cols, D, waves);
+  const pkv::WorkspaceLayout lay = pkv::workspace_layout(B, Hkv / hg, cols, D, waves, wgc);
   call->ws_used = lay.total;
   if (!workspace || workspace_bytes < lay.total)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
@@ -248,6 +270,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.window = opts.window;
   p.hg = hg;
   p.total_waves = waves;
+  p.wgc = wgc ? 1 : 0;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
@@ -321,7 +344,8 @@ int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
   if (!supported(D, BS, G, kv_dtype)) return 0;
   const pkv::AttnPath path = path_for(QueryOpts{}, G);
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, false);
-  return attention_blocks(path, D, BS, G, kv_dtype, B, hg) * pkv::kAttnWavesPerBlock;
+  return attention_blocks(path, D, BS, G, kv_dtype, B, hg, 1, use_wgc(path, hg * G, B)) *
+         pkv::kAttnWavesPerBlock;
 }
 
 int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
@@ -329,6 +353,35 @@ int pkv_decode_unit_heads(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
   const int G = Hq / Hkv;
   if (!supported(D, BS, G, kv_dtype)) return 0;
   return unit_heads(path_for(QueryOpts{}, G), D, BS, G, Hkv, kv_dtype, B, false);
+}
+
+int pkv_read_probe_waves(void) {
+  int dev;
+  if (current_device(&dev) != 0) return 0;
+  return pkv::read_probe_waves(cu_count(dev));
+}
+
+int pkv_read_probe(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                   void* stream) {
+  g_last_error.clear();
+  if (bytes == 0) return PKV_OK;
+  if (!buf || !sink) return fail(PKV_ERR_NULL, "buf and sink are required");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return fail(PKV_ERR_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
+  const int waves = pkv_read_probe_waves();
+  if (waves <= 0) return fail(PKV_ERR_HIP, "could not size the probe's grid on the current device");
+  if (sink_words < (size_t)waves)
+    return fail(PKV_ERR_WORKSPACE, "sink of %zu words is smaller than the %d waves", sink_words,
+                waves);
+  hipError_t e = pkv::launch_read_probe(buf, bytes, sink, waves, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : hip_fail(e, "read probe launch");
+}
+
+int pkv_select_share_combine(int mode) {
+  if (mode != 0 && mode != 1)
+    return fail(PKV_ERR_UNSUPPORTED, "share-combine mode %d is not 0 or 1", mode);
+  share_combine_flag().store(mode, std::memory_order_relaxed);
+  return PKV_OK;
 }
 
 int pkv_select_unit_heads(int mode) {
@@ -355,10 +408,11 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
     if (gen == 0 && max_q > 1) continue;
     const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0, max_q);
     const int cols = hg * G * max_q;
-    const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols));
+    const bool wgc = use_wgc(path, cols, B);
+    const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
     if (blocks <= 0) return 0;
     const int waves = blocks * pkv::kAttnWavesPerBlock;
-    const size_t t = pkv::workspace_layout(B, Hkv / hg, cols, D, waves).total;
+    const size_t t = pkv::workspace_layout(B, Hkv / hg, cols, D, waves, wgc).total;
     if (t > need) need = t;
   }
   return need;

@@ -40,6 +40,11 @@ struct AttnParams {
   // always takes 1.
   int hg;
   int total_waves;      // persistent waves of the partition grid
+  // wgc: the waves of a workgroup (consecutive pieces) combine their shares
+  // of a run in LDS at the end; a run inside the workgroup's range is
+  // finished there, and one crossing its edge leaves one share row per
+  // workgroup (row g + segment, g the workgroup) instead of one per piece.
+  int wgc;
   // workspace (see workspace_layout)
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
   float* ws_ml;         // [rows, cols, 2] running max (log2 domain) and sum
@@ -75,12 +80,23 @@ struct WorkspaceLayout {
 #endif
 constexpr int kPiecesPerWave = PKV_PIECES_PER_WAVE;
 
+constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
+constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
+
+// Shares are combined within workgroups (AttnParams::wgc) when a share row
+// has at most this many columns and the batch at most kWgcMaxBatch
+// sequences (the LDS for it then fits beside the rest at the same
+// occupancy).
+constexpr int kWgcMaxCols = 8;
+constexpr int kWgcMaxBatch = 1024;
+
 // `U` = units per sequence (Hkv / hg), `cols` = hg * G * (query tokens per
-// sequence, at most).
-inline WorkspaceLayout workspace_layout(int B, int U, int cols, int D, int total_waves) {
+// sequence, at most).  With wgc the share rows are per workgroup.
+inline WorkspaceLayout workspace_layout(int B, int U, int cols, int D, int total_waves,
+                                        bool wgc = false) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
-  w.rows = kPiecesPerWave * total_waves + B * U;
+  w.rows = (wgc ? total_waves / kAttnWavesPerBlock : kPiecesPerWave * total_waves) + B * U;
   w.pre_off = 0;
   w.ml_off = w.pre_off + up(sizeof(int32_t) * (size_t)(B + 1));
   w.o_off = w.ml_off + up(sizeof(float) * 2 * (size_t)w.rows * cols);
@@ -88,8 +104,6 @@ inline WorkspaceLayout workspace_layout(int B, int U, int cols, int D, int total
   return w;
 }
 
-constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
-constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
 constexpr int kMaxBatch = 8192;          // sequence prefix sums live in LDS
 
 // Batches up to this size keep their context lengths in LDS beside the
@@ -123,10 +137,12 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
 // heads per wave reach (0 if there is none: mfma_unit_heads(G) is the one hg
 // above 1 that exists); with col_tiles = 2, that of the generalised
 // instantiation with two 16-column tiles (hg = 1 only).
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1);
+// wgc: with the LDS of the workgroup combine.
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1,
+                       bool wgc = false);
 int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
-size_t mfma_stage_lds_bytes(int D, int hg);
+size_t mfma_stage_lds_bytes(int D, int hg, bool wgc = false);
 
 // Variant used by the attention calls: MFMA unless PKV_ATTN_KERNEL=valu is
 // set when the library loads, or pkv_select_partition_kernel changes it.
@@ -161,6 +177,13 @@ hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, con
 hipError_t launch_validate(const int32_t* block_tables, const int32_t* context_lens,
                            const float* k_scale, const float* v_scale, int B, int Hkv, int BS,
                            int NB, int MBS, unsigned long long* first, hipStream_t stream);
+
+// Streaming read probe (read_probe.hip): the waves of its persistent grid on
+// a device with cu_count compute units, and the launch reading the whole
+// 1 KB units of buf into sink[waves].
+int read_probe_waves(int cu_count);
+hipError_t launch_read_probe(const void* buf, size_t bytes, unsigned* sink, int waves,
+                             hipStream_t stream);
 
 // One-token append.  With `slots` NULL the slot of token i is derived from
 // the block table instead: position context_lens[i] - 1 of sequence i

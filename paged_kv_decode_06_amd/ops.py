@@ -90,6 +90,12 @@ def _load():
         lib.pkv_attention_waves.restype = I
         lib.pkv_decode_unit_heads.argtypes = [I, I, I, I, I, I]
         lib.pkv_decode_unit_heads.restype = I
+        lib.pkv_read_probe_waves.argtypes = []
+        lib.pkv_read_probe_waves.restype = I
+        lib.pkv_read_probe.argtypes = [P, S, P, S, P]
+        lib.pkv_read_probe.restype = I
+        lib.pkv_select_share_combine.argtypes = [I]
+        lib.pkv_select_share_combine.restype = I
         lib.pkv_select_unit_heads.argtypes = [I]
         lib.pkv_select_unit_heads.restype = I
         lib.pkv_select_partition_kernel.argtypes = [I]
@@ -255,6 +261,13 @@ def select_unit_heads(mode: int) -> None:
     _check("pkv_select_unit_heads", _load().pkv_select_unit_heads(int(mode)))
 
 
+def select_share_combine(mode: int) -> None:
+    """pkv_select_share_combine: 1 = the waves of a workgroup combine their
+    partial results in LDS where the call allows it (default), 0 = one partial
+    row per wave (process-wide; resize workspaces afterwards)."""
+    _check("pkv_select_share_combine", _load().pkv_select_share_combine(int(mode)))
+
+
 def decode_unit_heads(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:
     """Kv heads per partition wave a decode call with these sizes uses
     (kv_dtype: KV_BF16, KV_FP8 or KV_INT8)."""
@@ -264,6 +277,25 @@ def decode_unit_heads(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int)
 def attention_waves(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:
     """Persistent waves of a decode call's partition grid with these sizes."""
     return int(_load().pkv_attention_waves(B, Hq, Hkv, D, BS, int(kv_dtype)))
+
+
+def read_probe_waves() -> int:
+    """Waves of the streaming-read probe's grid (the words its sink needs)."""
+    return int(_load().pkv_read_probe_waves())
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """pkv_read_probe: read every whole 1 KB unit of `buf` (a contiguous GPU
+    tensor) with 16-byte non-temporal loads; one XOR fold per wave in `sink`
+    (int32 / uint32 GPU tensor of at least read_probe_waves() words)."""
+    if not (isinstance(buf, torch.Tensor) and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous tensor")
+    if not (isinstance(sink, torch.Tensor) and sink.is_contiguous() and sink.element_size() == 4):
+        raise ValueError("sink must be a contiguous tensor of 32-bit words")
+    _on_gpu(buf=buf, sink=sink)
+    _check("pkv_read_probe", _load().pkv_read_probe(
+        _ptr(buf), ctypes.c_size_t(buf.numel() * buf.element_size()), _ptr(sink),
+        ctypes.c_size_t(sink.numel()), _stream(stream)))
 
 
 def workspace_bytes(B, Hq, Hkv, D, BS, MBS, kv_dtype=KV_BF16) -> int:

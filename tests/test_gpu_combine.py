@@ -1,0 +1,127 @@
+"""The workgroup combine of the partition kernel's shares (GPU).
+
+The four waves of a partition workgroup stream consecutive pieces of the
+work axis; with the combine on (the default, for calls whose share rows have
+at most 8 columns and B <= 1024) they merge their shares of a run in LDS, so
+a run inside a workgroup's range is finished by the workgroup and a run
+crossing its edge leaves one share row per workgroup.  Checked: the same
+oracle bar with the combine on and off, results that differ only by
+summation order, repeated calls bit for bit, runs inside and across
+workgroup ranges, the generalised call, and the workspace each mode needs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_decode_06_amd import ops
+from paged_kv_decode_06_amd import workloads as W
+from tests import gpu_support as GS
+from tests.test_gpu_parity import DEV, build, check_step, default_kernel, say, use_kernel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _restore():
+    yield
+    default_kernel()
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16)
+
+
+def twin(wl: W.Workload) -> W.Workload:
+    """A second copy of a workload's tensors (same values, other memory)."""
+    import copy
+    o = copy.copy(wl)
+    for name in ("q", "k_new", "v_new", "k_cache", "v_cache", "k_scale", "v_scale",
+                 "context_lens", "block_tables", "slot_mapping", "q_start"):
+        t = getattr(wl, name)
+        setattr(o, name, None if t is None else t.clone())
+    return o
+
+
+CASES = [
+    # (B, Hq, Hkv, D, BS, lengths, kv, kernel mode)
+    (6, 32, 8, 128, 16, (40, 700, 1500, 3, 2600, 17), "bf16", "mfma"),   # two heads, G = 4
+    (5, 16, 8, 128, 32, (33, 1, 900, 64, 2049), "fp8", "mfma"),          # two heads, G = 2
+    (5, 16, 8, 64, 16, (500, 2, 1200, 77, 300), "int8", "mfma"),
+    (4, 64, 8, 128, 16, (20, 1000, 2000, 5), "bf16", "mfma1"),           # one head, G = 8
+    (4, 32, 8, 128, 16, (20, 1000, 2000, 5), "bf16", "mfma1"),           # one head, G = 4
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"Hq{c[1]}Hkv{c[2]}D{c[3]}{c[6]}{c[7]}")
+def test_combine_on_and_off_meet_the_oracle_and_agree(case):
+    B, Hq, Hkv, D, BS, lengths, kv, mode = case
+    use_kernel(mode)
+    wl = build(B, Hq, Hkv, D, BS, lengths, kv=kv, seed=B + Hq + D)
+    other = twin(wl)
+    on, _ = check_step(wl, f"{case} combine on")
+    ops.select_share_combine(0)
+    off, _ = check_step(other, f"{case} combine off")
+    # only the summation order differs: within two bf16 steps of each other
+    a, b = GS.bf16_to_f64(on), GS.bf16_to_f64(off)
+    assert np.all(np.abs(a - b) <= 2 * 2.0 ** -8 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
+
+
+def test_repeated_calls_are_bit_identical():
+    wl = build(16, 32, 8, 128, 16, np.random.default_rng(5).integers(100, 3000, 16), seed=5,
+               poison=False)
+    GS.append_in_order(wl)
+    ws = GS.workspace_for(wl)
+    first = GS.gpu_step(wl, workspace=ws, append=False).clone()
+    for _ in range(3):
+        again = GS.gpu_step(wl, workspace=ws, append=False)
+        assert torch.equal(bits(again), bits(first))
+
+
+def test_runs_inside_and_across_workgroup_ranges():
+    """Many short sequences (runs inside one workgroup's range, finished in
+    the workgroup, some by several waves) and a few long ones (runs across
+    many ranges, left to the merge), lengths 1 .. 9000."""
+    rng = np.random.default_rng(31)
+    L = np.concatenate([rng.integers(1, 80, 200), rng.integers(3000, 9000, 6)])
+    rng.shuffle(L)
+    wl = build(len(L), 32, 8, 128, 16, L, seed=31)
+    check_step(wl, "short and long runs")
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_generalised_call_with_one_query(window):
+    """The generalised instantiation takes the combine when its columns fit
+    (one query per sequence at G <= 4): against the oracle, and without a
+    window bit for bit the decode call (same split, same grouping)."""
+    wl = build(5, 32, 8, 128, 16, (1, 400, 1800, 3100, 66), seed=9, poison=True)
+    wl_q = W.build_workload("t", 5, 32, 8, 128, 16, list(wl.lengths), seed=9, device=DEV,
+                            poison=True, q_lens=[1] * 5, window=window, sinks=4 if window else 0)
+    host = GS.GeneralHost(wl_q)
+    out = GS.general_step(wl_q)
+    torch.cuda.synchronize()
+    host.append()
+    GS.assert_attention_close(GS.bf16_to_f64(out)[host.rows], host.attention(), "bf16",
+                              f"window {window}")
+    if window == 0:
+        dec = GS.gpu_step(wl)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(dec), bits(out))
+
+
+def test_workspace_follows_the_mode():
+    """Share rows are per workgroup with the combine (a quarter as many
+    wave rows) and per wave without it; calls with more than 8 columns or
+    more than 1024 sequences never combine."""
+    kv = ops.KV_BF16
+    on = ops.workspace_bytes(64, 32, 8, 128, 16, 256, kv)
+    ops.select_share_combine(0)
+    off = ops.workspace_bytes(64, 32, 8, 128, 16, 256, kv)
+    wide_off = ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv)        # G = 8: 16 columns
+    big_off = ops.workspace_bytes(2000, 32, 8, 128, 16, 64, kv)
+    ops.select_share_combine(1)
+    assert on < off
+    assert ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv) == wide_off
+    assert ops.workspace_bytes(2000, 32, 8, 128, 16, 64, kv) == big_off
+    say("workspace bytes, Llama shape: combine", on, "per wave", off)

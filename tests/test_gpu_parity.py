@@ -45,6 +45,7 @@ def use_kernel(name: str) -> None:
 def default_kernel() -> None:
     ops.select_partition_kernel(ops.PARTITION_MFMA)
     ops.select_unit_heads(ops.UNITS_AUTO)
+    ops.select_share_combine(1)
 
 
 @pytest.fixture(params=list(KERNELS))

@@ -10,7 +10,10 @@ adds the other heads' products with P = 0 (exact zeros).  So every share is
 the same bits as with one head per wave whenever both split the work into
 the same page ranges, which holds when every piece is one page (the total
 page count does not exceed either grid's waves); the test checks that
-precondition before comparing.
+precondition before comparing.  These comparisons run with the workgroup
+combine of the shares switched off: it groups the pieces of four waves, and
+the two unit sizes lay out the work axis differently, so they would group
+different pages (tests/test_gpu_combine.py covers the combine).
 """
 from __future__ import annotations
 
@@ -31,6 +34,13 @@ pytestmark = pytest.mark.gpu
 def _restore():
     yield
     default_kernel()
+
+
+@pytest.fixture
+def no_combine():
+    ops.select_share_combine(0)
+    yield
+    ops.select_share_combine(1)
 
 
 def unit_heads(wl: W.Workload) -> int:
@@ -90,7 +100,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda s: f"Hq{s[1]}Hkv{s[2]}D{s[3]}BS{s[4]}{s[6]}")
-def test_units_equal_one_head_bit_for_bit(case):
+def test_units_equal_one_head_bit_for_bit(case, no_combine):
     B, Hq, Hkv, D, BS, lengths, kv = case
     wl = build(B, Hq, Hkv, D, BS, lengths, kv=kv, seed=Hq + Hkv + D + BS)
     assert unit_heads(wl) > 1
@@ -108,7 +118,7 @@ def test_units_equal_one_head_bit_for_bit(case):
 
 
 @pytest.mark.parametrize("case", CASES[:2] + CASES[4:6], ids=lambda s: f"Hq{s[1]}Hkv{s[2]}{s[6]}")
-def test_fused_step_units_equal_one_head_bit_for_bit(case):
+def test_fused_step_units_equal_one_head_bit_for_bit(case, no_combine):
     B, Hq, Hkv, D, BS, lengths, kv = case
     wl = build(B, Hq, Hkv, D, BS, lengths, kv=kv, seed=Hq + Hkv + D + BS + 1)
     assert unit_heads(wl) > 1 and one_page_pieces(wl)
@@ -194,7 +204,7 @@ def general_pages(wl: W.Workload) -> int:
 
 
 @pytest.mark.parametrize("case", GEN_CASES, ids=lambda s: f"G{s[1] // s[2]}q{max(s[6])}{s[7]}w{s[9]}")
-def test_general_units_equal_one_head_bit_for_bit(case):
+def test_general_units_equal_one_head_bit_for_bit(case, no_combine):
     """Same precondition as the decode test: every piece one page in both
     grids, so both split the work alike."""
     B, Hq, Hkv, D, BS, lengths, q_lens, kv, sinks, window = case
