@@ -23,7 +23,7 @@
 // kv head (U = Hkv units per sequence) or, in the MFMA kernel's decode
 // instantiations, HG adjacent kv heads (U = Hkv / HG).  The axis is cut into consecutive pieces of equal page count
 // for a persistent grid of W waves, so every wave streams the same number of
-// KV bytes whatever the length mix.  kPiecesPerWave pieces per wave are
+// KV bytes (to one page) whatever the length mix.  kPiecesPerWave pieces per wave are
 // taken from far apart on the axis; the default is one (measured: a second
 // or third piece costs more in per-piece setup than it recovers in balance).
 //
@@ -124,34 +124,58 @@ __device__ __forceinline__ int find_sequence(const int32_t* s_pre, int B, int U,
   return lo;
 }
 
-// The axis is cut into kPiecesPerWave * W consecutive pieces of Qp pages;
-// wave w streams pieces w, w + W, w + 2W, ...
+// The axis is cut into N = kPiecesPerWave * W consecutive pieces.  By
+// default every piece has Qp = ceil(total / N) pages (the last ones fewer or
+// none).  When that leaves more than N / 16 pieces empty although there are
+// at least N pages (small workloads: a fifth of the grid for the B4 window
+// workload), piece k covers [floor(k total / N), floor((k + 1) total / N))
+// instead, floor(total / N) or ceil(total / N) >= 1 pages each, so every wave
+// has work (3.3% faster there; level on the configurations that leave few
+// pieces empty, except 2.5% slower on the 70B-shaped mix, so those keep the
+// rounded-up length).  Either way the empty pieces, if any, come after the
+// last page: the merge kernel takes every piece between a run's first and
+// last page as one that wrote a share of it.  Wave w streams pieces w,
+// w + W, w + 2W, ...
 struct WorkSplit {
-  int total;  // pages on the axis
-  int W;      // waves
-  int Qp;     // piece length (pages)
+  int total;      // pages on the axis
+  int W;          // waves
+  int N;          // pieces
+  int Qp;         // piece length of the rounded-up split
+  bool balanced;  // the floor(k total / N) split
 };
 
 __device__ __forceinline__ WorkSplit make_split(int total, int W) {
   WorkSplit s;
   s.total = total;
   s.W = W;
-  s.Qp = (total + kPiecesPerWave * W - 1) / (kPiecesPerWave * W);
+  s.N = kPiecesPerWave * W;
+  s.Qp = total > 0 ? (total + s.N - 1) / s.N : 1;
+  const int used = (total + s.Qp - 1) / s.Qp;   // pieces the rounded-up split fills
+  s.balanced = total >= s.N && 16 * (s.N - used) > s.N;
   return s;
 }
 
-// Piece containing axis position x.
-__device__ __forceinline__ int piece_of(const WorkSplit& s, int x) { return x / s.Qp; }
+// First axis position of piece k (k <= N).
+__device__ __forceinline__ int piece_start(const WorkSplit& s, int k) {
+  if (s.balanced) return (int)(((int64_t)k * s.total) / s.N);
+  return (int)min((int64_t)k * s.Qp, (int64_t)s.total);
+}
+
+// Piece containing axis position x < total: the largest k with start(k) <= x.
+__device__ __forceinline__ int piece_of(const WorkSplit& s, int x) {
+  if (s.balanced) return (int)((((int64_t)x + 1) * s.N - 1) / s.total);
+  return x / s.Qp;
+}
 
 // Drives one wave through its pieces; body(x, x_end, k) streams axis pages
-// [x, x_end) of piece k.
+// [x, x_end) of piece k (empty pieces are skipped).
 template <class Body>
 __device__ __forceinline__ void run_split(const WorkSplit& s, int wave, Body&& body) {
   for (int i = 0; i < kPiecesPerWave; ++i) {
     const int k = i * s.W + wave;
-    const int x = k * s.Qp;
-    if (x >= s.total) break;
-    body(x, min(s.total, x + s.Qp), k);
+    const int x = piece_start(s, k);
+    const int x_end = piece_start(s, k + 1);
+    if (x < x_end) body(x, x_end, k);
   }
 }
 

@@ -7,7 +7,8 @@ a run inside a workgroup's range is finished by the workgroup and a run
 crossing its edge leaves one share row per workgroup.  Checked: the same
 oracle bar with the combine on and off, results that differ only by
 summation order, repeated calls bit for bit, runs inside and across
-workgroup ranges, the generalised call, and the workspace each mode needs.
+workgroup ranges, the generalised call, the workspace each mode needs, and
+the floor/ceil split of small workloads.
 """
 from __future__ import annotations
 
@@ -125,3 +126,33 @@ def test_workspace_follows_the_mode():
     assert ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv) == wide_off
     assert ops.workspace_bytes(2000, 32, 8, 128, 16, 64, kv) == big_off
     say("workspace bytes, Llama shape: combine", on, "per wave", off)
+
+
+def balanced_split(total: int, pieces: int) -> bool:
+    """Whether the partition kernels cut a work axis of `total` pages into
+    `pieces` pieces of floor/ceil(total / pieces) pages (else every piece
+    has ceil(total / pieces) pages and the last ones are empty)."""
+    qp = -(-total // pieces)
+    used = -(-total // qp)
+    return total >= pieces and 16 * (pieces - used) > pieces
+
+
+@pytest.mark.parametrize("mode", ["mfma", "mfma1"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_balanced_split(mode, kv):
+    """A batch of about 700 pages per kv head: the rounded-up split would
+    leave a third of the waves idle, so the pieces are floor/ceil sized and
+    every wave streams one or two pages; runs of one to 250 pages cross many
+    piece (and workgroup) edges.  Against the oracle, combine on and off."""
+    use_kernel(mode)
+    lengths = (40, 3000, 1, 2500, 700, 4000, 17, 900)
+    wl = build(len(lengths), 32, 8, 128, 16, lengths, kv=kv, seed=77)
+    kvd = GS.KV_KIND[kv]
+    waves = ops.attention_waves(wl.B, 32, 8, 128, 16, kvd)
+    U = 8 // ops.decode_unit_heads(wl.B, 32, 8, 128, 16, kvd)
+    total = U * sum(-(-L // 16) for L in lengths)
+    assert balanced_split(total, waves), (total, waves)
+    other = twin(wl)
+    check_step(wl, f"balanced split {mode} {kv} combine on")
+    ops.select_share_combine(0)
+    check_step(other, f"balanced split {mode} {kv} combine off")
