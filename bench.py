@@ -376,7 +376,9 @@ def only_step_line(args, cfg, nbytes, ms_per_step):
 def decode_detail(name, args, dev):
     """One decode configuration for detail.configs: K one-call steps (wall
     clock), then the same K steps with timing-only events around the
-    partition launch (append inside) and the merge."""
+    partition launch (append inside) and the merge, each step followed by
+    the attention call's partition alone on another cache copy (the cost of
+    the fused append is the difference of the two partition means)."""
     import torch
     from paged_kv_decode_06_amd import ops
     from paged_kv_decode_06_amd import workloads as W
@@ -396,6 +398,9 @@ def decode_detail(name, args, dev):
     steps = [ops.PreparedStep(wl.q, wl.k_new, wl.v_new, kc, vc, wl.block_tables, wl.context_lens,
                               wl.scale, out, ks, vs, ws, stream=stream)
              for kc, vc, ks, vs in caches]
+    atts = [ops.PreparedAttention(wl.q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, out,
+                                  ks, vs, ws, stream=stream)
+            for kc, vc, ks, vs in caches]
     K, Wm = args.detail_steps, max(3, args.warmup // 2)
     with torch.cuda.stream(stream):
         settle([lambda i: steps[i % copies]()], args.settle)
@@ -407,29 +412,37 @@ def decode_detail(name, args, dev):
             steps[(Wm + i) % copies]()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / K
-        tev = TimingEvents(4 * K)
+        tev = TimingEvents(6 * K)
         for i in range(K):
             st = steps[(Wm + i) % copies]
-            tev.record(4 * i, stream)
+            tev.record(6 * i, stream)
             st.partition()
-            tev.record(4 * i + 1, stream)
-            tev.record(4 * i + 2, stream)
+            tev.record(6 * i + 1, stream)
+            tev.record(6 * i + 2, stream)
             st.merge()
-            tev.record(4 * i + 3, stream)
+            tev.record(6 * i + 3, stream)
+            at = atts[(Wm + i + copies // 2) % copies]
+            tev.record(6 * i + 4, stream)
+            at.partition()
+            tev.record(6 * i + 5, stream)
+            at.merge()
         torch.cuda.synchronize()
-    part = float(np.mean([tev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]))
-    merge = float(np.mean([tev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]))
+    part = float(np.mean([tev.elapsed_ms(6 * i, 6 * i + 1) for i in range(K)]))
+    merge = float(np.mean([tev.elapsed_ms(6 * i + 2, 6 * i + 3) for i in range(K)]))
+    apart = float(np.mean([tev.elapsed_ms(6 * i + 4, 6 * i + 5) for i in range(K)]))
     tev.close()
     res = {"kv_bytes_per_step": nbytes, "kv_dtype": wl.kv_dtype,
            "shape": f"B{wl.B} Hq{wl.Hq} Hkv{wl.Hkv} D{wl.D} BS{wl.BS}",
            "step_us": round(ms * 1e3, 2), "step_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
            "step_pct_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
            "partition_us": round(part * 1e3, 2), "merge_us": round(merge * 1e3, 2),
+           "attention_partition_us": round(apart * 1e3, 2),
+           "fused_append_us": round((part - apart) * 1e3, 2),
            "partition_frac": round(nbytes / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "seq_heads_per_s": round(wl.B * wl.Hq / (ms * 1e-3), 1),
            "steps": K, "kernel_heads_per_wave": ops.decode_unit_heads(wl.B, wl.Hq, wl.Hkv, wl.D,
                                                                       wl.BS, kvd)}
-    del steps, caches, ws, out, wl
+    del steps, atts, caches, ws, out, wl
     torch.cuda.empty_cache()
     return res
 

@@ -603,6 +603,22 @@ void mfma_partition_kernel(const AttnParams p) {
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(p.q);
 
   run_split(split, wave, [&](int x, const int x_end, const int piece) {
+  // The append's cache stores wait for the end of the piece: a store counts
+  // against the same wait counter as the loads that follow it, so stores
+  // issued between runs would hold up the next run's first tiles until they
+  // complete.  (A piece holding several runs' last pages stores the earlier
+  // ones when the next arrives.)
+  uint4 pend_part[NP];
+  uint2 pend_codes[NP];
+  float pend_gsc[2 * HG];
+  int64_t pend_row = 0, pend_sslot = 0;
+  bool pend_opens = false, pending = false;
+  auto flush_pending = [&]() {
+    store_new_rows<S>(pend_part, pend_codes, pend_gsc, lane, p.k_cache_w + pend_row,
+                      p.v_cache_w + pend_row, pend_opens,
+                      S::Q8 ? p.k_scale_w + pend_sslot : nullptr,
+                      S::Q8 ? p.v_scale_w + pend_sslot : nullptr);
+  };
   while (x < x_end) {
     Piece pc = locate_piece(s_pre, p.B, U, x, x_end);
     // (wave-uniform: kept in scalar registers)
@@ -910,11 +926,20 @@ void mfma_partition_kernel(const AttnParams p) {
       }
     }
 
-    if (parked)   // (wave-uniform)
-      store_new_rows<S>(new_part, new_codes, new_gsc, lane, p.k_cache_w + new_row,
-                        p.v_cache_w + new_row, new_opens,
-                        S::Q8 ? p.k_scale_w + new_sslot : nullptr,
-                        S::Q8 ? p.v_scale_w + new_sslot : nullptr);
+    if (parked) {   // (wave-uniform)
+      if (pending) flush_pending();
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        pend_part[i] = new_part[i];
+        pend_codes[i] = new_codes[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * HG; ++i) pend_gsc[i] = new_gsc[i];
+      pend_row = new_row;
+      pend_sslot = new_sslot;
+      pend_opens = new_opens;
+      pending = true;
+    }
 
     // ---- finish the piece ---------------------------------------------------
     if (dup) {   // column n's high-part sum plus column n + 8's low-part sum
@@ -980,6 +1005,7 @@ void mfma_partition_kernel(const AttnParams p) {
     }
     x = pc.run_start + pc.j1;
   }
+  if (pending) flush_pending();
   });
   if constexpr (NCT == 1)
     if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U);
