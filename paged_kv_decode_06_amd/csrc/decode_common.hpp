@@ -75,12 +75,14 @@ __device__ __forceinline__ int seq_pages(const AttnParams& p, int b, int BS) {
 }
 
 // Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]); with
-// s_len non-NULL also each sequence's context length as given (s_len[0..B)).
+// keep_len also each sequence's context length as given, in
+// s_tmp[kAttnBlockThreads + b] for b < B.
 // Called by every thread of the workgroup.  Each thread sums the pages of a
 // slice of sequences; the slices' sums are scanned within each wave by lane
 // shifts, and the waves' totals are added through LDS (one barrier).
 __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre, int32_t* s_tmp,
-                                    int32_t* s_len) {
+                                    bool keep_len) {
+  int32_t* s_len = s_tmp + kAttnBlockThreads;
   const int B = p.B;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
@@ -90,7 +92,7 @@ __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
   const int b1 = min(B, b0 + per);
   int sum = 0;
   for (int b = b0; b < b1; ++b) {
-    if (s_len != nullptr) s_len[b] = p.context_lens[b];
+    if (keep_len) s_len[b] = p.context_lens[b];
     sum += seq_pages(p, b, BS);
   }
   int incl = sum;   // inclusive scan of the slice sums within the wave

@@ -456,48 +456,62 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
                                             int wave_lds, const int* s_desc, int U) {
   constexpr int D = S::D, UG = S::UG, G = S::G, HG = S::HG;
   constexpr int TPR = D / 4;                    // threads per column (4 dims each)
+  // Share slots in axis order: wave w's head share is slot 2w, its end share
+  // slot 2w + 1.  Every slot index below is a constant once the loops are
+  // unrolled, so the descriptors stay in registers (an array indexed at run
+  // time would live in scratch memory, whose loads wait on the wave's
+  // outstanding global stores too).
+  constexpr int NS = 2 * kAttnWavesPerBlock;
   __syncthreads();
-  // the shares in axis order: wave 0's head, wave 0's end, wave 1's head, ...
-  int nsh = 0;
-  int sseg[2 * kAttnWavesPerBlock], sflg[2 * kAttnWavesPerBlock];
-  const float* sptr[2 * kAttnWavesPerBlock];
+  int sseg[NS], sflg[NS];
 #pragma unroll
-  for (int w = 0; w < kAttnWavesPerBlock; ++w)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int seg = s_desc[4 * w + 2 * k];
-      if (seg >= 0) {
-        unsigned char* base = waves_lds + (size_t)w * wave_lds;
-        sseg[nsh] = seg;
-        sflg[nsh] = s_desc[4 * w + 2 * k + 1];
-        sptr[nsh] = reinterpret_cast<const float*>(k == 0 ? base + 16 * S::PITCH + 32 * NewRows<S>::CH
-                                                          : base);
-        ++nsh;
-      }
-    }
+  for (int sl = 0; sl < NS; ++sl) {
+    sseg[sl] = s_desc[2 * sl];
+    sflg[sl] = s_desc[2 * sl + 1];
+  }
+  auto share = [&](int sl) {
+    return reinterpret_cast<const float*>(
+        waves_lds + (sl / 2) * wave_lds + (sl % 2 == 0 ? 16 * S::PITCH + 32 * NewRows<S>::CH : 0));
+  };
   const int t = threadIdx.x;
   const int c = t / TPR, d4 = (t % TPR) * 4;
-  for (int i = 0; i < nsh;) {
-    int j = i;
-    while (j + 1 < nsh && sseg[j + 1] == sseg[i]) ++j;
+  int prev = -1;                                // run of the last share seen
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
     const int seg = sseg[i];
+    if (seg < 0 || seg == prev) continue;       // no share, or not its run's first
+    prev = seg;
     const int b = seg / U, u = seg % U;
     const int ql = GEN ? seq_queries(p, b) : 1;
     if (c < UG * ql) {
+      // the run's shares are slots i .. last (consecutive: shares are in axis order)
       float M = -FLT_MAX;
-      for (int k = i; k <= j; ++k) M = fmaxf(M, sptr[k][kWgcMaxCols * D + c]);
+      int last = i;
+#pragma unroll
+      for (int k = i; k < NS; ++k)
+        if (sseg[k] == seg) {
+          M = fmaxf(M, share(k)[kWgcMaxCols * D + c]);
+          last = k;
+        }
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       float den = 0.0f;
-      for (int k = i; k <= j; ++k) {
-        const float w = fast_exp2(sptr[k][kWgcMaxCols * D + c] - M);
-        const float4 o = *reinterpret_cast<const float4*>(sptr[k] + c * D + d4);
-        den = fmaf(w, sptr[k][kWgcMaxCols * D + kWgcMaxCols + c], den);
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
-      }
-      if ((sflg[i] & 1) && (sflg[j] & 2)) {   // the whole run: out
+#pragma unroll
+      for (int k = i; k < NS; ++k)
+        if (sseg[k] == seg) {
+          const float* sh = share(k);
+          const float w = fast_exp2(sh[kWgcMaxCols * D + c] - M);
+          const float4 o = *reinterpret_cast<const float4*>(sh + c * D + d4);
+          den = fmaf(w, sh[kWgcMaxCols * D + kWgcMaxCols + c], den);
+          acc.x = fmaf(w, o.x, acc.x);
+          acc.y = fmaf(w, o.y, acc.y);
+          acc.z = fmaf(w, o.z, acc.z);
+          acc.w = fmaf(w, o.w, acc.w);
+        }
+      int lflg = sflg[i];
+#pragma unroll
+      for (int k = i + 1; k < NS; ++k)
+        if (k == last) lflg = sflg[k];
+      if ((sflg[i] & 1) && (lflg & 2)) {      // the whole run: out
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // (0: the query sees no key)
         const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;
         uint16_t* orow = static_cast<uint16_t*>(p.out) +
@@ -511,7 +525,6 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
         if (d4 == 0) *reinterpret_cast<float2*>(p.ws_ml + (row * C + c) * 2) = make_float2(M, den);
       }
     }
-    i = j + 1;
   }
 }
 
@@ -559,8 +572,13 @@ void mfma_partition_kernel(const AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int32_t* s_pre = reinterpret_cast<int32_t*>(smem);       // [B + 1]
   int32_t* s_tmp = s_pre + p.B + 1;                          // [blockDim]
-  int32_t* s_len = len_lds_entries(p.B) ? s_tmp + kAttnBlockThreads : nullptr;   // [B]
-  build_prefix(p, BS, s_pre, s_tmp, s_len);
+  // The lengths' LDS copy is addressed through s_tmp whether or not it is
+  // kept, so every access to it stays an LDS access (a pointer that is LDS
+  // or NULL would be a generic one, read with a flat load whose wait also
+  // covers the wave's outstanding global stores).
+  const bool len_lds = len_lds_entries(p.B) != 0;
+  int32_t* s_len = s_tmp + kAttnBlockThreads;                  // [B] if len_lds
+  build_prefix(p, BS, s_pre, s_tmp, len_lds);
 
   const int Hkv = p.Hkv;
   const int U = Hkv / HG;                  // units per sequence
@@ -629,7 +647,12 @@ void mfma_partition_kernel(const AttnParams p) {
     pc.j0 = __builtin_amdgcn_readfirstlane(pc.j0);
     pc.j1 = __builtin_amdgcn_readfirstlane(pc.j1);
     const int b = pc.b, g0 = pc.u * HG;   // the unit's first kv head
-    const int L_in = s_len != nullptr ? s_len[b] : p.context_lens[b];
+    int L_in;
+    if (len_lds)
+      L_in = s_len[b];
+    else   // (a buffer load: a plain load here would be merged with the LDS read above)
+      L_in = (int)__builtin_amdgcn_raw_buffer_load_b32(
+          tile_rsrc(reinterpret_cast<const unsigned char*>(p.context_lens)), 0, (uint32_t)b * 4, 0);
     const int L = min(max(L_in, 0), p.MBS * BS);
     // a length outside [1, MBS * BS] breaks the contract: no append then
     // (the decode step is one query per sequence: never the GEN instantiation)

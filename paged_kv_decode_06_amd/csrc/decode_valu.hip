@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void valu_partition_kernel(const
 
   extern __shared__ int32_t s_pre[];           // [B + 1] then [blockDim] scratch
   int32_t* s_tmp = s_pre + p.B + 1;
-  build_prefix(p, BS, s_pre, s_tmp, nullptr);
+  build_prefix(p, BS, s_pre, s_tmp, false);
 
   const int Hkv = p.Hkv;
   const int total = Hkv * s_pre[p.B];          // pages over all (b, g)
