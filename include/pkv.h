@@ -365,9 +365,11 @@ int pkv_select_unit_heads(int mode);
  * consecutive pieces of the work, combine their partial results for the
  * runs they share in LDS, so a run inside a workgroup's range is finished
  * there and one crossing its edge leaves one partial row per workgroup
- * instead of one per wave (taken by MFMA calls whose partial rows have at
- * most 8 columns, i.e. kv heads per wave x G x queries per sequence <= 8,
- * and B <= 1024); mode 0: one partial row per wave always.  The result
+ * instead of one per wave (taken by MFMA calls with B <= 1024 whose
+ * partial rows have at most 8 columns, i.e. kv heads per wave x G x queries
+ * per sequence <= 8, or at most 16 with two kv heads per wave where the
+ * larger LDS keeps the grid's size); mode 0: one partial row per wave
+ * always.  The result
  * differs only in floating-point summation order.  Process-wide, read at
  * the start of every attention call and workspace query, like
  * pkv_select_unit_heads.  PKV_SHARE_COMBINE=0 in the environment selects

@@ -441,15 +441,17 @@ __device__ __forceinline__ void rope_rotate(const AttnParams& p, int pos, int la
 // the run).  Each wave leaves at most two shares in LDS: a head share (the
 // piece starts inside a run and finishes it) in its head slot, and an end
 // share (the piece ends inside a run) in its tile buffer, each as o
-// [kWgcMaxCols][D], then m and l [kWgcMaxCols], with a descriptor (segment,
+// [W][D], then m and l [W] (W = p.wgc, the slot's column capacity), with a
+// descriptor (segment,
 // starts at the run's first page, ends at its last).  After the workgroup
 // barrier the shares, in axis order, are grouped by run: a group that starts
 // at the run's first page and ends at its last is the whole run, finished
 // here (bf16 out); any other is merged into one share row of the workgroup,
 // row g + segment, for the merge kernel.  Combining is by the log-sum-exp
 // rule of the merge kernel, in a fixed order, so results stay deterministic.
-template <int D>
-constexpr int kWgcSlot = kWgcMaxCols * (D + 2) * (int)sizeof(float);
+__host__ __device__ constexpr int wgc_slot_bytes(int D, int wcols) {
+  return wcols * (D + 2) * (int)sizeof(float);
+}
 
 template <class S, bool GEN>
 __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* waves_lds,
@@ -474,7 +476,8 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
         waves_lds + (sl / 2) * wave_lds + (sl % 2 == 0 ? 16 * S::PITCH + 32 * NewRows<S>::CH : 0));
   };
   const int t = threadIdx.x;
-  const int c = t / TPR, d4 = (t % TPR) * 4;
+  const int d4 = (t % TPR) * 4;
+  const int W = p.wgc;                          // a slot's column capacity
   int prev = -1;                                // run of the last share seen
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
@@ -483,35 +486,37 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
     prev = seg;
     const int b = seg / U, u = seg % U;
     const int ql = GEN ? seq_queries(p, b) : 1;
-    if (c < UG * ql) {
-      // the run's shares are slots i .. last (consecutive: shares are in axis order)
+    // the run's shares are slots i .. last (consecutive: shares are in axis order)
+    int last = i;
+#pragma unroll
+    for (int k = i + 1; k < NS; ++k)
+      if (sseg[k] == seg) last = k;
+    int lflg = sflg[i];
+#pragma unroll
+    for (int k = i + 1; k < NS; ++k)
+      if (k == last) lflg = sflg[k];
+    const bool whole = (sflg[i] & 1) && (lflg & 2);   // the whole run: out
+    // (kAttnBlockThreads / TPR columns a pass: 8 at D = 128, 16 at D = 64)
+    for (int c = t / TPR; c < UG * ql; c += kAttnBlockThreads / TPR) {
       float M = -FLT_MAX;
-      int last = i;
 #pragma unroll
       for (int k = i; k < NS; ++k)
-        if (sseg[k] == seg) {
-          M = fmaxf(M, share(k)[kWgcMaxCols * D + c]);
-          last = k;
-        }
+        if (sseg[k] == seg) M = fmaxf(M, share(k)[W * D + c]);
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       float den = 0.0f;
 #pragma unroll
       for (int k = i; k < NS; ++k)
         if (sseg[k] == seg) {
           const float* sh = share(k);
-          const float w = fast_exp2(sh[kWgcMaxCols * D + c] - M);
+          const float w = fast_exp2(sh[W * D + c] - M);
           const float4 o = *reinterpret_cast<const float4*>(sh + c * D + d4);
-          den = fmaf(w, sh[kWgcMaxCols * D + kWgcMaxCols + c], den);
+          den = fmaf(w, sh[W * D + W + c], den);
           acc.x = fmaf(w, o.x, acc.x);
           acc.y = fmaf(w, o.y, acc.y);
           acc.z = fmaf(w, o.z, acc.z);
           acc.w = fmaf(w, o.w, acc.w);
         }
-      int lflg = sflg[i];
-#pragma unroll
-      for (int k = i + 1; k < NS; ++k)
-        if (k == last) lflg = sflg[k];
-      if ((sflg[i] & 1) && (lflg & 2)) {      // the whole run: out
+      if (whole) {
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // (0: the query sees no key)
         const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;
         uint16_t* orow = static_cast<uint16_t*>(p.out) +
@@ -593,7 +598,7 @@ void mfma_partition_kernel(const AttnParams p) {
   const size_t pre_bytes = (sizeof(int32_t) * prefix_lds_words(p.B) + 15) & ~size_t(15);
   // per wave: staged tile, the new K and V unit rows (bf16) and, with the
   // workgroup combine, a slot for the share of the run the piece starts in
-  const int wave_lds = 16 * PITCH + 32 * CH + (p.wgc ? kWgcSlot<D> : 0);
+  const int wave_lds = 16 * PITCH + 32 * CH + wgc_slot_bytes(D, p.wgc);
   unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * wave_lds;
   unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
   float* head_slot = reinterpret_cast<float*>(new_rows + 32 * CH);
@@ -1002,8 +1007,8 @@ void mfma_partition_kernel(const AttnParams p) {
             *reinterpret_cast<float4*>(sh + c * D + 16 * nb + 4 * r) =
                 make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
           if (r == 0) {
-            sh[kWgcMaxCols * D + c] = m_run[ct];
-            sh[kWgcMaxCols * D + kWgcMaxCols + c] = l_tot;
+            sh[p.wgc * D + c] = m_run[ct];
+            sh[p.wgc * D + p.wgc + c] = l_tot;
           }
         }
         if (lane == 0) {
@@ -1079,8 +1084,12 @@ bool dispatch_mfma(int D, int BS, int G, int kind, int hg, F&& f) {
 
 int mfma_unit_heads(int G) { return kUnitHeads(G); }
 
-size_t mfma_stage_lds_bytes(int D, int hg, bool wgc) {
-  const size_t slot = wgc ? (size_t)kWgcMaxCols * (D + 2) * sizeof(float) : 0;
+bool mfma_tile_holds_share(int D, int hg, int wgc) {
+  return wgc_slot_bytes(D, wgc) <= 16 * (hg * 2 * D + 32);   // (MfmaShape::PITCH rows)
+}
+
+size_t mfma_stage_lds_bytes(int D, int hg, int wgc) {
+  const size_t slot = (size_t)wgc_slot_bytes(D, wgc);
   return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + 4 * hg * D + slot) +
          (wgc ? 4 * kAttnWavesPerBlock * sizeof(int) : 0);
 }
@@ -1090,7 +1099,7 @@ size_t mfma_stage_lds_bytes(int D, int hg, bool wgc) {
 // (three waves per SIMD measured slower for them: see MfmaShape::WPE).
 constexpr size_t kUnitLdsFloor = 56 * 1024;
 
-static size_t mfma_lds_total(int B, int D, int hg, bool wgc) {
+static size_t mfma_lds_total(int B, int D, int hg, int wgc) {
   const size_t t = ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg, wgc);
   return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
@@ -1106,9 +1115,9 @@ constexpr int blocks_at(int wpe) { return wpe * 4 / kAttnWavesPerBlock; }
 // VGPRs would run 4 per SIMD, measured 13-15% slower than 3), so the grid
 // is capped at the waves per SIMD of the instantiation.
 // col_tiles = 2: the generalised instantiation with two column tiles alone.
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, bool wgc) {
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, int wgc) {
   int blocks = 0, blocks_gen = 0, cap = 0;
-  const size_t lds = mfma_lds_total(B, D, hg, wgc && col_tiles == 1);
+  const size_t lds = mfma_lds_total(B, D, hg, col_tiles == 1 ? wgc : 0);
   if (col_tiles == 2) {
     const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
       using S = decltype(s);
@@ -1139,13 +1148,15 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_ti
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
-  const size_t lds = mfma_lds_total(p.B, D, p.hg, p.wgc != 0);
+  const size_t lds = mfma_lds_total(p.B, D, p.hg, p.wgc);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
   if (gen && p.rope) return hipErrorInvalidValue;
   const int cols = p.hg * G * p.max_q;
   // two column tiles: the generalised call with one kv head per wave only
   if (p.hg < 1 || p.Hkv % p.hg != 0 || cols != p.cols || cols > 32 ||
-      (cols > 16 && (!gen || p.hg != 1)) || (p.wgc && (cols > kWgcMaxCols || kPiecesPerWave != 1)))
+      (cols > 16 && (!gen || p.hg != 1)) ||
+      (p.wgc && (cols > p.wgc || (p.wgc != 8 && p.wgc != 16) || kPiecesPerWave != 1 ||
+                 !mfma_tile_holds_share(D, p.hg, p.wgc))))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

@@ -63,9 +63,9 @@ int cu_count(int dev) {
 // rounded up to a multiple of 1024 so that the cache stays small.  hg: kv
 // heads per wave, col_tiles: 16-column tiles per wave (MFMA only).
 int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg,
-                  int col_tiles = 1, bool wgc = false) {
+                  int col_tiles = 1, int wgc = 0) {
   const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)wgc << 56) |
+  const unsigned long long key = ((unsigned long long)(wgc / 8) << 56) |
                                  ((unsigned long long)col_tiles << 52) |
                                  ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
                                  ((unsigned long long)path << 36) |
@@ -96,7 +96,7 @@ bool supported(int D, int BS, int G, int kv_dtype) {
 
 // Persistent grid: every workgroup that fits at once on every CU.
 int attention_blocks(pkv::AttnPath path, int D, int BS, int G, int kv_dtype, int B, int hg,
-                     int col_tiles = 1, bool wgc = false) {
+                     int col_tiles = 1, int wgc = 0) {
   int dev;
   if (current_device(&dev) != 0) return 0;
   const int ncu = cu_count(dev);
@@ -116,9 +116,7 @@ std::atomic<int>& unit_heads_flag() {
 
 // Workgroup combine of the partition kernel's shares (pkv::AttnParams::wgc):
 // on unless PKV_SHARE_COMBINE=0 is set when the library loads or
-// pkv_select_share_combine(0) switched it off; taken by MFMA calls whose share
-// rows have at most kWgcMaxCols columns and whose batch is at most
-// kWgcMaxBatch.
+// pkv_select_share_combine(0) switched it off; see combine_cols.
 std::atomic<int>& share_combine_flag() {
   static std::atomic<int> flag([] {
     const char* e = std::getenv("PKV_SHARE_COMBINE");
@@ -127,9 +125,25 @@ std::atomic<int>& share_combine_flag() {
   return flag;
 }
 
-bool use_wgc(pkv::AttnPath path, int cols, int B) {
-  return path == pkv::AttnPath::kMfma && share_combine_flag().load(std::memory_order_relaxed) &&
-         cols <= pkv::kWgcMaxCols && B <= pkv::kWgcMaxBatch && pkv::kPiecesPerWave == 1;
+// The column capacity of the combine's share slots for an MFMA call whose
+// share rows have `cols` columns (0: no combine): 8 for up to 8 columns, 16
+// for up to 16 when a wave's tile buffer holds such a share (two kv heads
+// per wave) and the larger slots leave the workgroups per CU as they are.
+// Batches above kWgcMaxBatch take none.
+int combine_cols(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, int cols) {
+  if (path != pkv::AttnPath::kMfma || !share_combine_flag().load(std::memory_order_relaxed) ||
+      cols > pkv::kWgcMaxCols || B > pkv::kWgcMaxBatch || pkv::kPiecesPerWave != 1)
+    return 0;
+  const int w = cols <= 8 ? 8 : 16;
+  if (!pkv::mfma_tile_holds_share(D, hg, w)) return 0;
+  if (w > 8) {
+    int dev;
+    if (current_device(&dev) != 0 ||
+        blocks_per_cu(dev, path, D, BS, G, kind, B, hg, 1, w) <
+            blocks_per_cu(dev, path, D, BS, G, kind, B, hg, 1, 0))
+      return 0;
+  }
+  return w;
 }
 
 // Columns (kv heads per wave * G * max_q) one partition wave serves: the 16
@@ -154,7 +168,8 @@ int unit_heads(pkv::AttnPath path, int D, int BS, int G, int Hkv, int kv_dtype, 
   if (hg <= 1 || Hkv % hg != 0 || hg * G * max_q > kTileCols) return 1;
   int dev;
   if (current_device(&dev) != 0) return 1;
-  return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, 1, use_wgc(path, hg * G * max_q, B)) >= 2
+  return blocks_per_cu(dev, path, D, BS, G, kv_dtype, B, hg, 1,
+                       combine_cols(path, D, BS, G, kv_dtype, B, hg, hg * G * max_q)) >= 2
              ? hg
              : 1;
 }
@@ -237,7 +252,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const bool gen = opts.q_start != nullptr || opts.max_q > 1 || opts.window > 0;
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
   const int cols = hg * G * opts.max_q;
-  const bool wgc = use_wgc(path, cols, B);
+  const int wgc = combine_cols(path, D, BS, G, kv_dtype, B, hg, cols);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
@@ -270,7 +285,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.window = opts.window;
   p.hg = hg;
   p.total_waves = waves;
-  p.wgc = wgc ? 1 : 0;
+  p.wgc = wgc;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
@@ -344,7 +359,8 @@ int pkv_attention_waves(int B, int Hq, int Hkv, int D, int BS, int kv_dtype) {
   if (!supported(D, BS, G, kv_dtype)) return 0;
   const pkv::AttnPath path = path_for(QueryOpts{}, G);
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, false);
-  return attention_blocks(path, D, BS, G, kv_dtype, B, hg, 1, use_wgc(path, hg * G, B)) *
+  return attention_blocks(path, D, BS, G, kv_dtype, B, hg, 1,
+                          combine_cols(path, D, BS, G, kv_dtype, B, hg, hg * G)) *
          pkv::kAttnWavesPerBlock;
 }
 
@@ -408,7 +424,7 @@ size_t workspace_bytes_for(int B, int Hq, int Hkv, int D, int BS, int MBS, int k
     if (gen == 0 && max_q > 1) continue;
     const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen != 0, max_q);
     const int cols = hg * G * max_q;
-    const bool wgc = use_wgc(path, cols, B);
+    const int wgc = combine_cols(path, D, BS, G, kv_dtype, B, hg, cols);
     const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
     if (blocks <= 0) return 0;
     const int waves = blocks * pkv::kAttnWavesPerBlock;

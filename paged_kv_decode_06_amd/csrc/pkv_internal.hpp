@@ -44,6 +44,8 @@ struct AttnParams {
   // of a run in LDS at the end; a run inside the workgroup's range is
   // finished there, and one crossing its edge leaves one share row per
   // workgroup (row g + segment, g the workgroup) instead of one per piece.
+  // Its value is the column capacity of a wave's share slots (8 or 16;
+  // 0: no combine).
   int wgc;
   // workspace (see workspace_layout)
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
@@ -84,16 +86,17 @@ constexpr int kAttnBlockThreads = 256;   // 4 independent waves per workgroup
 constexpr int kAttnWavesPerBlock = kAttnBlockThreads / 64;
 
 // Shares are combined within workgroups (AttnParams::wgc) when a share row
-// has at most this many columns and the batch at most kWgcMaxBatch
-// sequences (the LDS for it then fits beside the rest at the same
-// occupancy).
-constexpr int kWgcMaxCols = 8;
+// has at most this many columns (more than 8 only with two kv heads per
+// wave, whose tile buffer holds a 16-column share) and the batch at most
+// kWgcMaxBatch sequences, and the LDS for it fits beside the rest at the
+// same occupancy.
+constexpr int kWgcMaxCols = 16;
 constexpr int kWgcMaxBatch = 1024;
 
 // `U` = units per sequence (Hkv / hg), `cols` = hg * G * (query tokens per
 // sequence, at most).  With wgc the share rows are per workgroup.
 inline WorkspaceLayout workspace_layout(int B, int U, int cols, int D, int total_waves,
-                                        bool wgc = false) {
+                                        int wgc = 0) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
   w.rows = (wgc ? total_waves / kAttnWavesPerBlock : kPiecesPerWave * total_waves) + B * U;
@@ -137,12 +140,15 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
 // heads per wave reach (0 if there is none: mfma_unit_heads(G) is the one hg
 // above 1 that exists); with col_tiles = 2, that of the generalised
 // instantiation with two 16-column tiles (hg = 1 only).
-// wgc: with the LDS of the workgroup combine.
+// wgc: with the LDS of the workgroup combine for shares of wgc columns.
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1,
-                       bool wgc = false);
+                       int wgc = 0);
 int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
-size_t mfma_stage_lds_bytes(int D, int hg, bool wgc = false);
+size_t mfma_stage_lds_bytes(int D, int hg, int wgc = 0);
+// Whether a wave's tile buffer holds a share of wgc columns (the combine
+// keeps a wave's end share there).
+bool mfma_tile_holds_share(int D, int hg, int wgc);
 
 // Variant used by the attention calls: MFMA unless PKV_ATTN_KERNEL=valu is
 // set when the library loads, or pkv_select_partition_kernel changes it.

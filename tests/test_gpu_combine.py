@@ -2,7 +2,8 @@
 
 The four waves of a partition workgroup stream consecutive pieces of the
 work axis; with the combine on (the default, for calls whose share rows have
-at most 8 columns and B <= 1024) they merge their shares of a run in LDS, so
+at most 8 columns, or 16 with two kv heads per wave, and B <= 1024) they
+merge their shares of a run in LDS, so
 a run inside a workgroup's range is finished by the workgroup and a run
 crossing its edge leaves one share row per workgroup.  Checked: the same
 oracle bar with the combine on and off, results that differ only by
@@ -51,6 +52,8 @@ CASES = [
     (5, 16, 8, 128, 32, (33, 1, 900, 64, 2049), "fp8", "mfma"),          # two heads, G = 2
     (5, 16, 8, 64, 16, (500, 2, 1200, 77, 300), "int8", "mfma"),
     (4, 64, 8, 128, 16, (20, 1000, 2000, 5), "bf16", "mfma1"),           # one head, G = 8
+    (6, 64, 8, 128, 16, (40, 700, 1500, 3, 2600, 17), "bf16", "mfma"),   # two heads, G = 8: 16 columns
+    (5, 32, 4, 64, 32, (33, 1, 900, 64, 2049), "fp8", "mfma"),           # two heads, G = 8, D = 64
     (4, 32, 8, 128, 16, (20, 1000, 2000, 5), "bf16", "mfma1"),           # one head, G = 4
 ]
 
@@ -113,17 +116,21 @@ def test_generalised_call_with_one_query(window):
 
 def test_workspace_follows_the_mode():
     """Share rows are per workgroup with the combine (a quarter as many
-    wave rows) and per wave without it; calls with more than 8 columns or
-    more than 1024 sequences never combine."""
+    wave rows) and per wave without it: 8-column rows (G = 4, two heads)
+    and 16-column rows with two heads (G = 8) combine; one head with 16
+    columns (G = 16: its tile buffer cannot hold such a share) and more than
+    1024 sequences never do."""
     kv = ops.KV_BF16
     on = ops.workspace_bytes(64, 32, 8, 128, 16, 256, kv)
+    on16 = ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv)             # G = 8: 16 columns
     ops.select_share_combine(0)
     off = ops.workspace_bytes(64, 32, 8, 128, 16, 256, kv)
-    wide_off = ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv)        # G = 8: 16 columns
+    off16 = ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv)
+    g16_off = ops.workspace_bytes(64, 128, 8, 128, 16, 256, kv)           # G = 16, one head
     big_off = ops.workspace_bytes(2000, 32, 8, 128, 16, 64, kv)
     ops.select_share_combine(1)
-    assert on < off
-    assert ops.workspace_bytes(256, 64, 8, 128, 16, 1024, kv) == wide_off
+    assert on < off and on16 < off16
+    assert ops.workspace_bytes(64, 128, 8, 128, 16, 256, kv) == g16_off
     assert ops.workspace_bytes(2000, 32, 8, 128, 16, 64, kv) == big_off
     say("workspace bytes, Llama shape: combine", on, "per wave", off)
 
