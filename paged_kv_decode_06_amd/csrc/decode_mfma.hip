@@ -642,6 +642,21 @@ void mfma_partition_kernel(const AttnParams p) {
                       S::Q8 ? p.k_scale_w + pend_sslot : nullptr,
                       S::Q8 ? p.v_scale_w + pend_sslot : nullptr);
   };
+  // Likewise the bf16 output of a run the piece finishes by itself (kernels
+  // with two kv heads per wave and one column tile: the others have no
+  // registers to spare); a lane whose column is past the call's leaves
+  // out_row NULL.
+  constexpr bool DEFER_OUT = NCT == 1 && HG > 1;
+  uint2 out_pend[DEFER_OUT ? NBN : 1];
+  uint16_t* out_row = nullptr;
+  bool out_pending = false;   // (wave-uniform)
+  auto flush_out = [&]() {
+    if (out_row != nullptr) {
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb)
+        *reinterpret_cast<uint2*>(out_row + 16 * nb) = out_pend[DEFER_OUT ? nb : 0];
+    }
+  };
   while (x < x_end) {
     Piece pc = locate_piece(s_pre, p.B, U, x, x_end);
     // (wave-uniform: kept in scalar registers)
@@ -984,16 +999,26 @@ void mfma_partition_kernel(const AttnParams p) {
       l_tot += __shfl_xor(l_tot, 16);
       l_tot += __shfl_xor(l_tot, 32);            // column n's sum, in every row group
       if (pc.j0 == 0 && pc.j1 == pc.n_b) {
+        if constexpr (DEFER_OUT) {
+          if (out_pending) flush_out();
+          out_pending = true;
+          out_row = nullptr;
+        }
         if (c < ncol) {
           // (a query that sees no key gets 0)
           const float inv = !GEN || l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
           uint16_t* orow = static_cast<uint16_t*>(p.out) +
                            ((int64_t)(r0 + col_q[ct]) * p.Hq + col_h[ct]) * D + 4 * r;
 #pragma unroll
-          for (int nb = 0; nb < NBN; ++nb)
-            *reinterpret_cast<uint2*>(orow + 16 * nb) =
-                make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
-                           pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
+          for (int nb = 0; nb < NBN; ++nb) {
+            const uint2 v = make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
+                                       pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
+            if constexpr (DEFER_OUT)
+              out_pend[nb] = v;
+            else
+              *reinterpret_cast<uint2*>(orow + 16 * nb) = v;
+          }
+          if constexpr (DEFER_OUT) out_row = orow;
         }
       } else if (NCT == 1 && p.wgc) {
         // the share goes to LDS for the workgroup combine: a piece ending
@@ -1034,6 +1059,8 @@ void mfma_partition_kernel(const AttnParams p) {
     x = pc.run_start + pc.j1;
   }
   if (pending) flush_pending();
+  if constexpr (DEFER_OUT)
+    if (out_pending) flush_out();
   });
   if constexpr (NCT == 1)
     if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U);
