@@ -163,3 +163,23 @@ def test_balanced_split(mode, kv):
     check_step(wl, f"balanced split {mode} {kv} combine on")
     ops.select_share_combine(0)
     check_step(other, f"balanced split {mode} {kv} combine off")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_sixteen_column_combine_at_the_batch_limit(kv):
+    """B = 1024 sequences at G = 8 with two kv heads per wave: 16-column
+    share slots, the largest batch that combines, whose LDS (prefix sums,
+    lengths, four waves' tiles and slots) still leaves two workgroups per
+    CU.  Lengths 1 .. 300 (runs inside and across workgroup ranges)."""
+    B = 1024
+    L = np.random.default_rng(41).integers(1, 300, B)
+    kvd = GS.KV_KIND[kv]
+    BS = 16 if kv == "bf16" else 32
+    assert ops.decode_unit_heads(B, 64, 8, 128, BS, kvd) == 2
+    on = ops.workspace_bytes(B, 64, 8, 128, BS, 32, kvd)
+    ops.select_share_combine(0)
+    off = ops.workspace_bytes(B, 64, 8, 128, BS, 32, kvd)
+    ops.select_share_combine(1)
+    assert on < off                                   # the combine is taken
+    wl = build(B, 64, 8, 128, BS, L, kv=kv, seed=41)
+    check_step(wl, f"B{B} G8 {kv} 16-column combine")
