@@ -27,8 +27,11 @@ namespace {
 // share's (m, l) and o are loaded together (one wait on memory per batch)
 // and the running max is rescaled when a batch brings a larger m.  The
 // groups then meet in LDS.  With NGRP groups a run of up to NGRP * kBatch
-// shares takes one trip to memory after the prefix sums (a run of 8 columns
-// has two groups: the B64 Llama-shaped step's runs have about 9 shares).
+// shares takes one trip to memory after the prefix sums.  Runs of at most 8
+// columns take two groups when the partition's waves wrote one share row
+// each (the B64 Llama-shaped step's runs then have about 9 shares); with the
+// workgroup combine they have about 3, and one group, without the meeting in
+// LDS, is faster.
 // The run's prefix sums and split are read once for all its columns.
 template <int D, int NGRP>
 __global__ __launch_bounds__(NGRP * 8 * D / 4 > 16 * D / 4 ? NGRP * 8 * D / 4 : 16 * D / 4)
@@ -279,11 +282,12 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
     return hipGetLastError();
   }
   // (a workgroup per run and 16 columns, D / 4 threads a column; runs of at
-  // most 8 columns get two thread groups, which split the shares)
+  // most 8 columns whose shares were not combined in the partition kernel
+  // get two thread groups, which split the shares)
   if (p.cols < 1 || p.cols > 32) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)), (unsigned)((p.cols + 15) / 16));
   const int wcols = p.cols < 16 ? p.cols : 16;
-  const bool two = wcols <= 8;
+  const bool two = wcols <= 8 && p.wgc == 0;
   if (D == 128) {
     if (two)
       hipLaunchKernelGGL((merge_seg_kernel<128, 2>), grid, dim3(2 * wcols * 32), 0, stream, p, G);
