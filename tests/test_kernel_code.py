@@ -14,6 +14,7 @@ The merge kernels are held to the first property too.
 from __future__ import annotations
 
 import os
+import pathlib
 import re
 import shutil
 import subprocess
@@ -27,13 +28,16 @@ OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 
 
 @pytest.fixture(scope="module")
-def disassembly(tmp_path_factory):
+def disassembly():
     lib = ops.library_path()
     if not os.path.exists(lib):
         pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
     if not os.path.exists(OBJDUMP):
         pytest.skip("llvm-objdump is not installed")
-    work = tmp_path_factory.mktemp("code")
+    from paged_kv_decode_06_amd import build as B
+    work = pathlib.Path(B.BUILD) / "code_test"    # (the build folder: not tracked)
+    shutil.rmtree(work, ignore_errors=True)
+    work.mkdir(parents=True)
     copy = work / "libpkv.so"
     shutil.copyfile(lib, copy)
     # (the offload bundles are written next to the input file)
