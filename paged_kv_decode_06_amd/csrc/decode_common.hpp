@@ -76,7 +76,9 @@ __device__ __forceinline__ int seq_pages(const AttnParams& p, int b, int BS) {
 
 // Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]); with
 // keep_len also each sequence's context length as given, in
-// s_tmp[kAttnBlockThreads + b] for b < B.
+// s_tmp[kAttnBlockThreads + b] for b < B, and, where qs_lds_entries(B) is
+// not 0, its first query row (q_start[b], or b without q_start) in
+// s_tmp[kAttnBlockThreads + B + b] for b <= B.
 // Called by every thread of the workgroup.  Each thread sums the pages of a
 // slice of sequences; the slices' sums are scanned within each wave by lane
 // shifts, and the waves' totals are added through LDS (one barrier).
@@ -91,10 +93,13 @@ __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
   const int b0 = tid * per;
   const int b1 = min(B, b0 + per);
   int sum = 0;
+  const bool keep_qs = keep_len && qs_lds_entries(B) != 0;
   for (int b = b0; b < b1; ++b) {
     if (keep_len) s_len[b] = p.context_lens[b];
+    if (keep_qs) s_len[B + b] = p.q_start != nullptr ? p.q_start[b] : b;
     sum += seq_pages(p, b, BS);
   }
+  if (keep_qs && tid == nt - 1) s_len[2 * B] = p.q_start != nullptr ? p.q_start[B] : B;
   int incl = sum;   // inclusive scan of the slice sums within the wave
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {

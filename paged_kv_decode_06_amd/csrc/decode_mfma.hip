@@ -582,7 +582,8 @@ void mfma_partition_kernel(const AttnParams p) {
   // or NULL would be a generic one, read with a flat load whose wait also
   // covers the wave's outstanding global stores).
   const bool len_lds = len_lds_entries(p.B) != 0;
-  int32_t* s_len = s_tmp + kAttnBlockThreads;                  // [B] if len_lds
+  const bool qs_lds = len_lds && qs_lds_entries(p.B) != 0;
+  int32_t* s_len = s_tmp + kAttnBlockThreads;   // [B] if len_lds, then [B + 1] if qs_lds
   build_prefix(p, BS, s_pre, s_tmp, len_lds);
 
   const int Hkv = p.Hkv;
@@ -681,9 +682,17 @@ void mfma_partition_kernel(const AttnParams p) {
     const int64_t head_off = (int64_t)g0 * RB;
     // column n: query token n / UG of the sequence, query head g0 G + n % UG
     // (decode: one query, the unit's UG heads)
-    const int ql = GEN ? seq_queries(p, b) : 1;
+    int ql = 1, r0 = b;   // query count, first q / out row
+    if constexpr (GEN) {
+      if (qs_lds) {
+        r0 = s_len[p.B + b];
+        ql = min(max(s_len[p.B + b + 1] - r0, 0), p.max_q);
+      } else {
+        ql = seq_queries(p, b);
+        r0 = p.q_start != nullptr ? p.q_start[b] : b;
+      }
+    }
     const int ncol = UG * ql;
-    const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;   // first q / out row
     const SeqRange sr = GEN ? seq_range(L, ql, p.sinks, p.window, BS) : SeqRange{0, 0, 0};
     auto table_page = [&](int j) { return !GEN || j < sr.ps ? j : j + sr.gap; };
     // column c = 16 ct + n of tile ct: query c / UG, query head g0 G + c % UG.

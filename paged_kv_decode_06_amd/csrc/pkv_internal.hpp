@@ -115,14 +115,23 @@ constexpr int kMaxBatch = 8192;          // sequence prefix sums live in LDS
 constexpr int kLenLdsMax = 2048;
 __host__ __device__ inline int len_lds_entries(int B) { return B <= kLenLdsMax ? B : 0; }
 
+// Batches up to this size also keep the query-row offsets (q_start, B + 1
+// entries; b for a call without them) there, so that a generalised run's
+// query count and first row come from LDS too: loaded from memory, they
+// put a second round trip before its q and page-table loads.  (Bounded so
+// that the extra LDS moves no occupancy threshold.)
+constexpr int kQsLdsMax = 512;
+__host__ __device__ inline int qs_lds_entries(int B) { return B <= kQsLdsMax ? B + 1 : 0; }
+
 // 32-bit words of LDS the sequence prefix sums take: s_pre [B + 1], the
-// scan's scratch [kAttnBlockThreads], the lengths [len_lds_entries(B)].
+// scan's scratch [kAttnBlockThreads], the lengths [len_lds_entries(B)] and
+// the query-row offsets [qs_lds_entries(B)].
 __host__ __device__ inline size_t prefix_lds_words(int B) {
-  return (size_t)B + 1 + kAttnBlockThreads + len_lds_entries(B);
+  return (size_t)B + 1 + kAttnBlockThreads + len_lds_entries(B) + qs_lds_entries(B);
 }
 
-// LDS of the sequence prefix sums (plus the scan scratch and the cached
-// lengths) for B sequences.
+// LDS of the sequence prefix sums (plus the scan scratch, the cached
+// lengths and query-row offsets) for B sequences.
 inline size_t prefix_lds_bytes(int B) { return sizeof(int32_t) * prefix_lds_words(B); }
 
 // The two partition-kernel variants.  Launchers return hipErrorInvalidValue
