@@ -376,6 +376,19 @@ int pkv_select_unit_heads(int mode);
  * mode 0 when the library loads.  PKV_ERR_UNSUPPORTED for another value. */
 int pkv_select_share_combine(int mode);
 
+/* mode 1 (default): in a generalised call (pkv_paged_attention with
+ * q_start, several queries or a window) whose partition waves serve one kv
+ * head and one 16-column tile without the combine above, a wave keeps the
+ * result of a run that it finishes before its last one in LDS and writes it
+ * out after its last tile, where a store issued at once would hold up the
+ * next run's loads (taken when the LDS slot leaves the workgroups per CU as
+ * they are, so the grid and the workspace do not change).  mode 0 stores
+ * every result when its run ends.  The two give the same bits.
+ * Process-wide, read at the start of every attention call, like
+ * pkv_select_unit_heads.  PKV_RESULT_PARKING=0 in the environment selects
+ * mode 0 when the library loads.  PKV_ERR_UNSUPPORTED for another value. */
+int pkv_select_result_parking(int mode);
+
 /* Partition-kernel variants.  Both compute the same attention; MFMA (the
  * default) puts the GQA group on the matrix cores, VALU uses fp32 vector
  * FMAs.  The choice is process-wide and is read at the start of every

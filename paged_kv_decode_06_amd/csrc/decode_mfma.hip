@@ -453,6 +453,19 @@ __host__ __device__ constexpr int wgc_slot_bytes(int D, int wcols) {
   return wcols * (D + 2) * (int)sizeof(float);
 }
 
+// The parking slot: a 16-column result, o as [D / 16][64 lanes] float4 (each
+// lane its own values) and then (m, l) of the columns.  It overlays the
+// append rows (unused by the generalised instantiations) and extends past
+// them.
+__host__ __device__ constexpr int park_slot_bytes(int D) { return wgc_slot_bytes(D, 16); }
+
+// Bytes a wave keeps after its staged tile: the append rows (or the parking
+// slot over them) and the combine's head slot.
+__host__ __device__ constexpr int wave_rows_bytes(int hg, int D, int wgc, int park) {
+  return (park && park_slot_bytes(D) > 4 * hg * D ? park_slot_bytes(D) : 4 * hg * D) +
+         wgc_slot_bytes(D, wgc);
+}
+
 template <class S, bool GEN>
 __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* waves_lds,
                                             int wave_lds, const int* s_desc, int U) {
@@ -599,7 +612,8 @@ void mfma_partition_kernel(const AttnParams p) {
   const size_t pre_bytes = (sizeof(int32_t) * prefix_lds_words(p.B) + 15) & ~size_t(15);
   // per wave: staged tile, the new K and V unit rows (bf16) and, with the
   // workgroup combine, a slot for the share of the run the piece starts in
-  const int wave_lds = 16 * PITCH + 32 * CH + wgc_slot_bytes(D, p.wgc);
+  static_assert(32 * CH == 4 * HG * D, "append rows: a K and a V unit row of bf16");
+  const int wave_lds = 16 * PITCH + wave_rows_bytes(HG, D, p.wgc, p.park);
   unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * wave_lds;
   unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
   float* head_slot = reinterpret_cast<float*>(new_rows + 32 * CH);
@@ -657,6 +671,47 @@ void mfma_partition_kernel(const AttnParams p) {
       for (int nb = 0; nb < NBN; ++nb)
         *reinterpret_cast<uint2*>(out_row + 16 * nb) = out_pend[DEFER_OUT ? nb : 0];
     }
+  };
+  // Kernels with one kv head and one column tile have no registers to keep
+  // a result in: with p.park, one result that more runs of the piece follow
+  // (its bf16 output, scaled, or its share) waits in the wave's parking slot
+  // instead and goes to memory after the piece's last tile.  Stored at once
+  // it would hold up the next run, whose first waits cover the stores and
+  // whose store acks take longer than a load round trip (skipping such
+  // stores measured 5% of the verify workload, with one of them in a sixth
+  // of the pieces).  Only scalars describe the parked result.
+  constexpr bool PARK = GEN && HG == 1 && NCT == 1;
+  float* const park_slot = reinterpret_cast<float*>(new_rows);   // (see park_slot_bytes)
+  int park_kind = 0;           // 0: empty, 1: output, 2: share (wave-uniform)
+  int64_t park_row = 0;        // share row, or the output's first query row
+  int park_g0 = 0, park_ncol = 0;
+  auto flush_park = [&]() {
+    const int c = n;   // (one tile: column n)
+    if (park_kind == 1) {
+      if (c < park_ncol) {
+        uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                         ((park_row + c / UG) * p.Hq + park_g0 * G + c % UG) * D + 4 * r;
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb) {
+          const float4 v = *reinterpret_cast<const float4*>(park_slot + 4 * (kWave * nb + lane));
+          *reinterpret_cast<uint2*>(orow + 16 * nb) =
+              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+        }
+      }
+    } else {
+      const int C = p.cols;
+      if (c < park_ncol) {
+        float* orow = p.ws_o + (park_row * C + c) * D + 4 * r;
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb)
+          *reinterpret_cast<float4*>(orow + 16 * nb) =
+              *reinterpret_cast<const float4*>(park_slot + 4 * (kWave * nb + lane));
+      }
+      if (lane < park_ncol)
+        *reinterpret_cast<float2*>(p.ws_ml + (park_row * C + lane) * 2) =
+            *reinterpret_cast<const float2*>(park_slot + 4 * kWave * NBN + 2 * lane);
+    }
+    park_kind = 0;
   };
   while (x < x_end) {
     Piece pc = locate_piece(s_pre, p.B, U, x, x_end);
@@ -1001,6 +1056,8 @@ void mfma_partition_kernel(const AttnParams p) {
         for (int i = 0; i < 4; ++i) O[0][nb][i] += __shfl_xor(O[0][nb][i], 8);
     }
     const int seg = b * U + pc.u;
+    // (PARK: one tile, ct = 0; the slot is free and more runs follow)
+    const bool to_park = PARK && p.park && park_kind == 0 && pc.run_start + pc.j1 < x_end;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = 16 * ct + n;
@@ -1013,7 +1070,19 @@ void mfma_partition_kernel(const AttnParams p) {
           out_pending = true;
           out_row = nullptr;
         }
-        if (c < ncol) {
+        if (to_park) {
+          // (a query that sees no key gets 0)
+          const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<float4*>(park_slot + 4 * (kWave * nb + lane)) =
+                make_float4(O[ct][nb][0] * inv, O[ct][nb][1] * inv, O[ct][nb][2] * inv,
+                            O[ct][nb][3] * inv);
+          park_kind = 1;
+          park_row = r0;
+          park_g0 = g0;
+          park_ncol = ncol;
+        } else if (c < ncol) {
           // (a query that sees no key gets 0)
           const float inv = !GEN || l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
           uint16_t* orow = static_cast<uint16_t*>(p.out) +
@@ -1049,6 +1118,18 @@ void mfma_partition_kernel(const AttnParams p) {
           s_desc[4 * wave_in_block + 2 * is_end] = seg;
           s_desc[4 * wave_in_block + 2 * is_end + 1] = (pc.j0 == 0) | (pc.j1 == pc.n_b) << 1;
         }
+      } else if (to_park) {
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb)
+          *reinterpret_cast<float4*>(park_slot + 4 * (kWave * nb + lane)) =
+              make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+        // (lanes 0..15: column `lane`'s max and sum)
+        if (lane < 16)
+          *reinterpret_cast<float2*>(park_slot + 4 * kWave * NBN + 2 * lane) =
+              make_float2(m_run[ct], l_tot);
+        park_kind = 2;
+        park_row = (int64_t)piece + seg;
+        park_ncol = ncol;
       } else {
         const int64_t row = (int64_t)piece + seg;
         const int C = p.cols;
@@ -1070,6 +1151,8 @@ void mfma_partition_kernel(const AttnParams p) {
   if (pending) flush_pending();
   if constexpr (DEFER_OUT)
     if (out_pending) flush_out();
+  if constexpr (PARK)
+    if (park_kind != 0) flush_park();
   });
   if constexpr (NCT == 1)
     if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U);
@@ -1124,19 +1207,21 @@ bool mfma_tile_holds_share(int D, int hg, int wgc) {
   return wgc_slot_bytes(D, wgc) <= 16 * (hg * 2 * D + 32);   // (MfmaShape::PITCH rows)
 }
 
-size_t mfma_stage_lds_bytes(int D, int hg, int wgc) {
-  const size_t slot = (size_t)wgc_slot_bytes(D, wgc);
-  return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + 4 * hg * D + slot) +
+size_t mfma_stage_lds_bytes(int D, int hg, int wgc, int park) {
+  return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + wave_rows_bytes(hg, D, wgc, park)) +
          (wgc ? 4 * kAttnWavesPerBlock * sizeof(int) : 0);
 }
+
+int mfma_park_slot_bytes(int D) { return park_slot_bytes(D); }
 
 // Units of several kv heads run at two workgroups (8 waves) per CU: each
 // workgroup reserves at least this much LDS, so a third one never fits
 // (three waves per SIMD measured slower for them: see MfmaShape::WPE).
 constexpr size_t kUnitLdsFloor = 56 * 1024;
 
-static size_t mfma_lds_total(int B, int D, int hg, int wgc) {
-  const size_t t = ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg, wgc);
+static size_t mfma_lds_total(int B, int D, int hg, int wgc, int park = 0) {
+  const size_t t =
+      ((prefix_lds_bytes(B) + 15) & ~size_t(15)) + mfma_stage_lds_bytes(D, hg, wgc, park);
   return hg > 1 && t < kUnitLdsFloor ? kUnitLdsFloor : t;
 }
 
@@ -1151,9 +1236,10 @@ constexpr int blocks_at(int wpe) { return wpe * 4 / kAttnWavesPerBlock; }
 // VGPRs would run 4 per SIMD, measured 13-15% slower than 3), so the grid
 // is capped at the waves per SIMD of the instantiation.
 // col_tiles = 2: the generalised instantiation with two column tiles alone.
-int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, int wgc) {
+int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, int wgc,
+                       int park) {
   int blocks = 0, blocks_gen = 0, cap = 0;
-  const size_t lds = mfma_lds_total(B, D, hg, col_tiles == 1 ? wgc : 0);
+  const size_t lds = mfma_lds_total(B, D, hg, col_tiles == 1 ? wgc : 0, col_tiles == 1 ? park : 0);
   if (col_tiles == 2) {
     const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
       using S = decltype(s);
@@ -1184,7 +1270,7 @@ int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_ti
 
 hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int kind, int blocks,
                                  hipStream_t stream) {
-  const size_t lds = mfma_lds_total(p.B, D, p.hg, p.wgc);
+  const size_t lds = mfma_lds_total(p.B, D, p.hg, p.wgc, p.park);
   const bool gen = p.q_start != nullptr || p.max_q > 1 || p.window > 0;
   if (gen && p.rope) return hipErrorInvalidValue;
   const int cols = p.hg * G * p.max_q;
@@ -1192,7 +1278,8 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
   if (p.hg < 1 || p.Hkv % p.hg != 0 || cols != p.cols || cols > 32 ||
       (cols > 16 && (!gen || p.hg != 1)) ||
       (p.wgc && (cols > p.wgc || (p.wgc != 8 && p.wgc != 16) || kPiecesPerWave != 1 ||
-                 !mfma_tile_holds_share(D, p.hg, p.wgc))))
+                 !mfma_tile_holds_share(D, p.hg, p.wgc))) ||
+      (p.park && (!gen || p.hg != 1 || cols > 16 || p.wgc)))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

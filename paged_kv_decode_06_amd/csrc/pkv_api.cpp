@@ -60,18 +60,20 @@ int cu_count(int dev) {
 }
 
 // LDS of the partition kernel grows with B; occupancy is looked up for B
-// rounded up to a multiple of 1024 so that the cache stays small.  hg: kv
-// heads per wave, col_tiles: 16-column tiles per wave (MFMA only).
+// rounded up to a multiple of 64 (at most 128 entries per shape; the calls
+// and the workspace queries share the lookup, so they agree on the grid).
+// hg: kv heads per wave, col_tiles: 16-column tiles per wave (MFMA only).
 int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg,
-                  int col_tiles = 1, int wgc = 0) {
-  const int Bq = ((B + 1023) / 1024) * 1024;
-  const unsigned long long key = ((unsigned long long)(wgc / 8) << 56) |
+                  int col_tiles = 1, int wgc = 0, int park = 0) {
+  const int Bq = ((B + 63) / 64) * 64;
+  const unsigned long long key = ((unsigned long long)(park != 0) << 58) |
+                                 ((unsigned long long)(wgc / 8) << 56) |
                                  ((unsigned long long)col_tiles << 52) |
                                  ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
                                  ((unsigned long long)path << 36) |
                                  ((unsigned long long)D << 28) | ((unsigned long long)BS << 20) |
                                  ((unsigned long long)G << 16) | ((unsigned long long)kind << 12) |
-                                 (unsigned long long)(Bq / 1024);
+                                 (unsigned long long)(Bq / 64);
   auto& c = cache();
   {
     std::lock_guard<std::mutex> lk(c.mu);
@@ -79,7 +81,7 @@ int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, i
     if (it != c.blocks.end()) return it->second;
   }
   const int n = path == pkv::AttnPath::kMfma
-                    ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg, col_tiles, wgc)
+                    ? pkv::mfma_blocks_per_cu(D, BS, G, kind, Bq, hg, col_tiles, wgc, park)
                     : pkv::valu_blocks_per_cu(D, BS, G, kind, Bq);
   std::lock_guard<std::mutex> lk(c.mu);
   c.blocks[key] = n;
@@ -144,6 +146,31 @@ int combine_cols(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int 
       return 0;
   }
   return w;
+}
+
+// Parking of mid-piece results (pkv::AttnParams::park): on unless
+// PKV_RESULT_PARKING=0 is set when the library loads or
+// pkv_select_result_parking(0) switched it off; see parking.
+std::atomic<int>& parking_flag() {
+  static std::atomic<int> flag([] {
+    const char* e = std::getenv("PKV_RESULT_PARKING");
+    return (e && std::string(e) == "0") ? 0 : 1;
+  }());
+  return flag;
+}
+
+// Whether a generalised MFMA call parks its mid-piece results: one kv head
+// and one column tile per wave, no combine, and the slot leaves the
+// workgroups per CU (hence the grid and the workspace) as they are.
+int parking(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, int cols, int wgc,
+            bool gen) {
+  if (!gen || path != pkv::AttnPath::kMfma || hg != 1 || cols > 16 || wgc != 0 ||
+      !parking_flag().load(std::memory_order_relaxed))
+    return 0;
+  int dev;
+  if (current_device(&dev) != 0) return 0;
+  const int with = blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 1, 0, 1);
+  return with > 0 && with == blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 1, 0, 0) ? 1 : 0;
 }
 
 // Columns (kv heads per wave * G * max_q) one partition wave serves: the 16
@@ -253,6 +280,8 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const int hg = unit_heads(path, D, BS, G, Hkv, kv_dtype, B, gen, opts.max_q);
   const int cols = hg * G * opts.max_q;
   const int wgc = combine_cols(path, D, BS, G, kv_dtype, B, hg, cols);
+  // (parking keeps the grid: the workspace queries need not know of it)
+  const int park = parking(path, D, BS, G, kv_dtype, B, hg, cols, wgc, gen);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
@@ -286,6 +315,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.hg = hg;
   p.total_waves = waves;
   p.wgc = wgc;
+  p.park = park;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
@@ -397,6 +427,13 @@ int pkv_select_share_combine(int mode) {
   if (mode != 0 && mode != 1)
     return fail(PKV_ERR_UNSUPPORTED, "share-combine mode %d is not 0 or 1", mode);
   share_combine_flag().store(mode, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int pkv_select_result_parking(int mode) {
+  if (mode != 0 && mode != 1)
+    return fail(PKV_ERR_UNSUPPORTED, "result-parking mode %d is not 0 or 1", mode);
+  parking_flag().store(mode, std::memory_order_relaxed);
   return PKV_OK;
 }
 

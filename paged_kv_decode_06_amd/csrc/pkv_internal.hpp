@@ -47,6 +47,10 @@ struct AttnParams {
   // Its value is the column capacity of a wave's share slots (8 or 16;
   // 0: no combine).
   int wgc;
+  // park (generalised calls with one kv head and one column tile per wave,
+  // no combine): a run's result that more runs of the piece follow waits in
+  // an LDS slot of the wave until the piece's end (mfma_park_slot_bytes).
+  int park;
   // workspace (see workspace_layout)
   int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
   float* ws_ml;         // [rows, cols, 2] running max (log2 domain) and sum
@@ -149,12 +153,14 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
 // heads per wave reach (0 if there is none: mfma_unit_heads(G) is the one hg
 // above 1 that exists); with col_tiles = 2, that of the generalised
 // instantiation with two 16-column tiles (hg = 1 only).
-// wgc: with the LDS of the workgroup combine for shares of wgc columns.
+// wgc: with the LDS of the workgroup combine for shares of wgc columns;
+// park: with the parking slot (AttnParams::park).
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1,
-                       int wgc = 0);
+                       int wgc = 0, int park = 0);
 int mfma_unit_heads(int G);
 // LDS a workgroup of the MFMA variant needs on top of the prefix sums.
-size_t mfma_stage_lds_bytes(int D, int hg, int wgc = 0);
+size_t mfma_stage_lds_bytes(int D, int hg, int wgc = 0, int park = 0);
+int mfma_park_slot_bytes(int D);
 // Whether a wave's tile buffer holds a share of wgc columns (the combine
 // keeps a wave's end share there).
 bool mfma_tile_holds_share(int D, int hg, int wgc);

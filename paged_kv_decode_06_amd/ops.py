@@ -96,6 +96,8 @@ def _load():
         lib.pkv_read_probe.restype = I
         lib.pkv_select_share_combine.argtypes = [I]
         lib.pkv_select_share_combine.restype = I
+        lib.pkv_select_result_parking.argtypes = [I]
+        lib.pkv_select_result_parking.restype = I
         lib.pkv_select_unit_heads.argtypes = [I]
         lib.pkv_select_unit_heads.restype = I
         lib.pkv_select_partition_kernel.argtypes = [I]
@@ -266,6 +268,14 @@ def select_share_combine(mode: int) -> None:
     partial results in LDS where the call allows it (default), 0 = one partial
     row per wave (process-wide; resize workspaces afterwards)."""
     _check("pkv_select_share_combine", _load().pkv_select_share_combine(int(mode)))
+
+
+def select_result_parking(mode: int) -> None:
+    """pkv_select_result_parking: 1 = generalised calls with one kv head and
+    one column tile per wave keep a mid-piece result in LDS until the piece
+    ends (default), 0 = store it when its run ends (process-wide; same bits
+    either way)."""
+    _check("pkv_select_result_parking", _load().pkv_select_result_parking(int(mode)))
 
 
 def decode_unit_heads(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:

@@ -1,0 +1,89 @@
+"""Parking of mid-piece results in the generalised partition kernel (GPU).
+
+Calls whose partition waves serve one kv head and one 16-column tile, without
+the workgroup combine (e.g. 4 draft tokens at G = 4), keep the result of a run
+that a wave finishes before its last one in LDS and store it after the wave's
+last tile.  Checked through the C ABI: against the fp64 oracle, and bit for
+bit the same output as storing every result when its run ends
+(pkv_select_result_parking(0)), on batches whose pieces hold complete short
+runs (parked bf16 outputs), runs split across pieces (parked shares) and
+several runs per piece (the slot is taken; later results are stored at
+once).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_decode_06_amd import ops
+from paged_kv_decode_06_amd import workloads as W
+from tests import gpu_support as GS
+from tests.test_gpu_general import build, check
+from tests.test_gpu_parity import DEV, default_kernel
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _restore():
+    yield
+    ops.select_result_parking(1)
+    default_kernel()
+
+
+def rng_lengths(seed, n_short, n_long, long_hi=5000):
+    rng = np.random.default_rng(seed)
+    L = np.concatenate([rng.integers(1, 60, n_short), rng.integers(600, long_hi, n_long)])
+    rng.shuffle(L)
+    return [int(x) for x in L]
+
+
+CASES = [
+    # (B-mix seed, n_short, n_long, Hq, Hkv, D, BS, q_len, kv, sinks, window)
+    (1, 40, 24, 32, 8, 128, 16, 4, "bf16", 0, 0),     # G = 4, 4 queries: 16 columns
+    (2, 60, 8, 16, 8, 128, 32, 8, "bf16", 0, 0),      # G = 2, 8 queries
+    (3, 30, 20, 32, 8, 64, 16, 4, "bf16", 0, 0),      # D = 64
+    (4, 40, 16, 32, 8, 128, 32, 4, "fp8", 0, 0),
+    (5, 40, 16, 32, 8, 128, 32, 3, "int8", 2, 300),   # window with sinks
+    (6, 20, 12, 128, 8, 128, 16, 1, "bf16", 4, 256),  # G = 16, one query, window
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[8]}-D{c[5]}G{c[3]//c[4]}-q{c[7]}-W{c[10]}")
+def test_parking_meets_the_oracle_and_changes_no_bit(case):
+    seed, ns, nl, Hq, Hkv, D, BS, ql, kv, S, Wn = case
+    L = rng_lengths(seed, ns, nl)
+    q_lens = [min(ql, x) for x in L]
+    wl = build(len(L), Hq, Hkv, D, BS, L, q_lens, kv=kv, seed=seed, poison=False, sinks=S,
+               window=Wn)
+    ops.select_result_parking(1)
+    on, _ = check(wl, f"{case} parking on")
+    ops.select_result_parking(0)
+    off = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(on.view(torch.int16), off.view(torch.int16))
+
+
+def test_full_verify_workload_bit_for_bit():
+    """The Llama-shaped verify workload (64 sequences, 4 draft tokens, G = 4):
+    parking on and off give the same bits, and repeated calls too."""
+    wl = W.make_config_workload("llama3_8b_verify4", device=DEV)
+    ops.select_result_parking(1)
+    first = GS.general_step(wl, append=False).clone()
+    again = GS.general_step(wl, append=False).clone()
+    ops.select_result_parking(0)
+    off = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+    assert torch.equal(first.view(torch.int16), off.view(torch.int16))
+
+
+def test_parking_keeps_the_workspace():
+    """Parking never changes the grid, so the workspace queries do not
+    depend on it."""
+    kv = ops.KV_BF16
+    on = ops.attention_workspace_bytes(64, 32, 8, 128, 16, 256, kv, 4)
+    ops.select_result_parking(0)
+    off = ops.attention_workspace_bytes(64, 32, 8, 128, 16, 256, kv, 4)
+    assert on == off
