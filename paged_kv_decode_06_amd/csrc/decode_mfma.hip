@@ -453,10 +453,10 @@ __host__ __device__ constexpr int wgc_slot_bytes(int D, int wcols) {
   return wcols * (D + 2) * (int)sizeof(float);
 }
 
-// The parking slot: a 16-column result, o as [D / 16][64 lanes] float4 (each
-// lane its own values) and then (m, l) of the columns.  It overlays the
-// append rows (unused by the generalised instantiations) and extends past
-// them.
+// The parking slot: a 16-column share, o as [D / 16][64 lanes] float4 (each
+// lane its own values) and then (m, l) of the columns, or a bf16 output of
+// up to 32 columns (as [2][D / 16][64 lanes] uint2).  It overlays the append
+// rows (unused by the generalised instantiations) and extends past them.
 __host__ __device__ constexpr int park_slot_bytes(int D) { return wgc_slot_bytes(D, 16); }
 
 // Bytes a wave keeps after its staged tile: the append rows (or the parking
@@ -672,44 +672,63 @@ void mfma_partition_kernel(const AttnParams p) {
         *reinterpret_cast<uint2*>(out_row + 16 * nb) = out_pend[DEFER_OUT ? nb : 0];
     }
   };
-  // Kernels with one kv head and one column tile have no registers to keep
-  // a result in: with p.park, one result that more runs of the piece follow
-  // (its bf16 output, scaled, or its share) waits in the wave's parking slot
-  // instead and goes to memory after the piece's last tile.  Stored at once
-  // it would hold up the next run, whose first waits cover the stores and
-  // whose store acks take longer than a load round trip (skipping such
-  // stores measured 5% of the verify workload, with one of them in a sixth
-  // of the pieces).  Only scalars describe the parked result.
-  constexpr bool PARK = GEN && HG == 1 && NCT == 1;
-  float* const park_slot = reinterpret_cast<float*>(new_rows);   // (see park_slot_bytes)
+  // Kernels with one kv head per wave have no registers to keep a whole
+  // result in: with p.park, one result that more runs of the piece follow
+  // waits in the wave's parking slot instead (its bf16 output, packed; or its
+  // share, whose first tile stays in registers when there are two) and goes
+  // to memory after the piece's last tile.  Stored at once it would hold up
+  // the next run, whose first waits cover the stores and whose store acks
+  // take longer than a load round trip (skipping such stores measured 5% of
+  // the verify workload, with one of them in a sixth of the pieces, and 15%
+  // of its 70B-shaped mix).  Only scalars describe the parked result.
+  constexpr bool PARK = GEN && HG == 1;
+  constexpr bool PARK_REG = PARK && NCT == 2;   // (the share's tile 0 in registers)
+  unsigned char* const park_slot = new_rows;    // (see park_slot_bytes)
+  float4_t park_o0[PARK_REG ? NBN : 1];
+  float park_m0 = 0.0f, park_l0 = 0.0f;
   int park_kind = 0;           // 0: empty, 1: output, 2: share (wave-uniform)
   int64_t park_row = 0;        // share row, or the output's first query row
   int park_g0 = 0, park_ncol = 0;
+  // slot offsets: output [ct][nb][lane] uint2; share (last tile) [nb][lane]
+  // float4, then (m, l) of its 16 columns
+  auto park_out_at = [&](int ct, int nb) { return 8 * (kWave * (NBN * ct + nb) + lane); };
+  auto park_o_at = [&](int nb) { return 16 * (kWave * nb + lane); };
+  const int park_ml_at = 16 * kWave * NBN;
   auto flush_park = [&]() {
-    const int c = n;   // (one tile: column n)
-    if (park_kind == 1) {
-      if (c < park_ncol) {
-        uint16_t* orow = static_cast<uint16_t*>(p.out) +
-                         ((park_row + c / UG) * p.Hq + park_g0 * G + c % UG) * D + 4 * r;
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb) {
-          const float4 v = *reinterpret_cast<const float4*>(park_slot + 4 * (kWave * nb + lane));
-          *reinterpret_cast<uint2*>(orow + 16 * nb) =
-              make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = 16 * ct + n;   // (no duplicated columns with one head in PARK kernels but
+                                   // the one-tile decode-shaped ones, whose used columns are n)
+      if (park_kind == 1) {
+        if (c < park_ncol) {
+          uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                           ((park_row + c / UG) * p.Hq + park_g0 * G + c % UG) * D + 4 * r;
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<uint2*>(orow + 16 * nb) =
+                *reinterpret_cast<const uint2*>(park_slot + park_out_at(ct, nb));
+        }
+      } else {
+        const int C = p.cols;
+        const bool in_regs = PARK_REG && ct == 0;
+        if (c < park_ncol) {
+          float* orow = p.ws_o + (park_row * C + c) * D + 4 * r;
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb) {
+            float4 v;
+            if (in_regs)
+              v = make_float4(park_o0[nb][0], park_o0[nb][1], park_o0[nb][2], park_o0[nb][3]);
+            else
+              v = *reinterpret_cast<const float4*>(park_slot + park_o_at(nb));
+            *reinterpret_cast<float4*>(orow + 16 * nb) = v;
+          }
+        }
+        if (lane < 16 && 16 * ct + lane < park_ncol) {
+          const float2 ml = in_regs ? make_float2(park_m0, park_l0)
+                                    : *reinterpret_cast<const float2*>(park_slot + park_ml_at + 8 * lane);
+          *reinterpret_cast<float2*>(p.ws_ml + (park_row * C + 16 * ct + lane) * 2) = ml;
         }
       }
-    } else {
-      const int C = p.cols;
-      if (c < park_ncol) {
-        float* orow = p.ws_o + (park_row * C + c) * D + 4 * r;
-#pragma unroll
-        for (int nb = 0; nb < NBN; ++nb)
-          *reinterpret_cast<float4*>(orow + 16 * nb) =
-              *reinterpret_cast<const float4*>(park_slot + 4 * (kWave * nb + lane));
-      }
-      if (lane < park_ncol)
-        *reinterpret_cast<float2*>(p.ws_ml + (park_row * C + lane) * 2) =
-            *reinterpret_cast<const float2*>(park_slot + 4 * kWave * NBN + 2 * lane);
     }
     park_kind = 0;
   };
@@ -1056,7 +1075,7 @@ void mfma_partition_kernel(const AttnParams p) {
         for (int i = 0; i < 4; ++i) O[0][nb][i] += __shfl_xor(O[0][nb][i], 8);
     }
     const int seg = b * U + pc.u;
-    // (PARK: one tile, ct = 0; the slot is free and more runs follow)
+    // (PARK: the slot is free and more runs of the piece follow)
     const bool to_park = PARK && p.park && park_kind == 0 && pc.run_start + pc.j1 < x_end;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -1075,9 +1094,9 @@ void mfma_partition_kernel(const AttnParams p) {
           const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
 #pragma unroll
           for (int nb = 0; nb < NBN; ++nb)
-            *reinterpret_cast<float4*>(park_slot + 4 * (kWave * nb + lane)) =
-                make_float4(O[ct][nb][0] * inv, O[ct][nb][1] * inv, O[ct][nb][2] * inv,
-                            O[ct][nb][3] * inv);
+            *reinterpret_cast<uint2*>(park_slot + park_out_at(ct, nb)) =
+                make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
+                           pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
           park_kind = 1;
           park_row = r0;
           park_g0 = g0;
@@ -1119,14 +1138,21 @@ void mfma_partition_kernel(const AttnParams p) {
           s_desc[4 * wave_in_block + 2 * is_end + 1] = (pc.j0 == 0) | (pc.j1 == pc.n_b) << 1;
         }
       } else if (to_park) {
+        if (PARK_REG && ct == 0) {
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb)
-          *reinterpret_cast<float4*>(park_slot + 4 * (kWave * nb + lane)) =
-              make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
-        // (lanes 0..15: column `lane`'s max and sum)
-        if (lane < 16)
-          *reinterpret_cast<float2*>(park_slot + 4 * kWave * NBN + 2 * lane) =
-              make_float2(m_run[ct], l_tot);
+          for (int nb = 0; nb < NBN; ++nb) park_o0[nb] = O[ct][nb];
+          park_m0 = m_run[ct];
+          park_l0 = l_tot;
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<float4*>(park_slot + park_o_at(nb)) =
+                make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+          // (lanes 0..15: column 16 ct + lane's max and sum)
+          if (lane < 16)
+            *reinterpret_cast<float2*>(park_slot + park_ml_at + 8 * lane) =
+                make_float2(m_run[ct], l_tot);
+        }
         park_kind = 2;
         park_row = (int64_t)piece + seg;
         park_ncol = ncol;
@@ -1239,7 +1265,7 @@ constexpr int blocks_at(int wpe) { return wpe * 4 / kAttnWavesPerBlock; }
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles, int wgc,
                        int park) {
   int blocks = 0, blocks_gen = 0, cap = 0;
-  const size_t lds = mfma_lds_total(B, D, hg, col_tiles == 1 ? wgc : 0, col_tiles == 1 ? park : 0);
+  const size_t lds = mfma_lds_total(B, D, hg, col_tiles == 1 ? wgc : 0, park);
   if (col_tiles == 2) {
     const bool ok = hg == 1 && dispatch_mfma(D, BS, G, kind, 1, [&](auto s) {
       using S = decltype(s);
@@ -1279,7 +1305,7 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
       (cols > 16 && (!gen || p.hg != 1)) ||
       (p.wgc && (cols > p.wgc || (p.wgc != 8 && p.wgc != 16) || kPiecesPerWave != 1 ||
                  !mfma_tile_holds_share(D, p.hg, p.wgc))) ||
-      (p.park && (!gen || p.hg != 1 || cols > 16 || p.wgc)))
+      (p.park && (!gen || p.hg != 1 || p.wgc)))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

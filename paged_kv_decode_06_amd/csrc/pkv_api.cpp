@@ -159,19 +159,6 @@ std::atomic<int>& parking_flag() {
   return flag;
 }
 
-// Whether a generalised MFMA call parks its mid-piece results: one kv head
-// and one column tile per wave, no combine, and the slot leaves the
-// workgroups per CU (hence the grid and the workspace) as they are.
-int parking(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, int cols, int wgc,
-            bool gen) {
-  if (!gen || path != pkv::AttnPath::kMfma || hg != 1 || cols > 16 || wgc != 0 ||
-      !parking_flag().load(std::memory_order_relaxed))
-    return 0;
-  int dev;
-  if (current_device(&dev) != 0) return 0;
-  const int with = blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 1, 0, 1);
-  return with > 0 && with == blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 1, 0, 0) ? 1 : 0;
-}
 
 // Columns (kv heads per wave * G * max_q) one partition wave serves: the 16
 // MFMA columns, or two tiles of them in the generalised call with one kv
@@ -181,6 +168,21 @@ constexpr int kMaxCols = 2 * kTileCols;
 
 // 16-column tiles of a wave serving `cols` columns.
 int col_tiles(int cols) { return (cols + kTileCols - 1) / kTileCols; }
+
+// Whether a generalised MFMA call parks its mid-piece results: one kv head
+// per wave, no combine, and the slot leaves the workgroups per CU (hence the
+// grid and the workspace) as they are.
+int parking(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, int cols, int wgc,
+            bool gen) {
+  if (!gen || path != pkv::AttnPath::kMfma || hg != 1 || wgc != 0 || cols > kMaxCols ||
+      !parking_flag().load(std::memory_order_relaxed))
+    return 0;
+  int dev;
+  if (current_device(&dev) != 0) return 0;
+  const int t = col_tiles(cols);
+  const int with = blocks_per_cu(dev, path, D, BS, G, kind, B, 1, t, 0, 1);
+  return with > 0 && with == blocks_per_cu(dev, path, D, BS, G, kind, B, 1, t, 0, 0) ? 1 : 0;
+}
 
 // A wave of the MFMA kernel serves hg adjacent kv heads when hg divides
 // Hkv, the unit's columns (hg * G per query, max_q queries per sequence)

@@ -1,9 +1,9 @@
 """Parking of mid-piece results in the generalised partition kernel (GPU).
 
-Calls whose partition waves serve one kv head and one 16-column tile, without
-the workgroup combine (e.g. 4 draft tokens at G = 4), keep the result of a run
-that a wave finishes before its last one in LDS and store it after the wave's
-last tile.  Checked through the C ABI: against the fp64 oracle, and bit for
+Calls whose partition waves serve one kv head, without the workgroup combine
+(e.g. 4 draft tokens at G = 4 or G = 8), keep the result of a run that a wave
+finishes before its last one in LDS (with two 16-column tiles, a share's
+first tile in registers) and store it after the wave's last tile.  Checked through the C ABI: against the fp64 oracle, and bit for
 bit the same output as storing every result when its run ends
 (pkv_select_result_parking(0)), on batches whose pieces hold complete short
 runs (parked bf16 outputs), runs split across pieces (parked shares) and
@@ -47,6 +47,11 @@ CASES = [
     (4, 40, 16, 32, 8, 128, 32, 4, "fp8", 0, 0),
     (5, 40, 16, 32, 8, 128, 32, 3, "int8", 2, 300),   # window with sinks
     (6, 20, 12, 128, 8, 128, 16, 1, "bf16", 4, 256),  # G = 16, one query, window
+    # two 16-column tiles: the share's first tile waits in registers
+    (7, 60, 10, 64, 8, 128, 16, 4, "bf16", 0, 0),     # G = 8, 4 queries: 32 columns
+    (8, 40, 10, 32, 8, 128, 16, 6, "bf16", 2, 300),   # G = 4, 6 queries: 24 columns, window
+    (9, 40, 12, 64, 8, 128, 32, 4, "fp8", 0, 0),
+    (10, 30, 10, 64, 8, 64, 16, 3, "int8", 0, 0),     # D = 64, 24 columns
 ]
 
 
@@ -65,10 +70,11 @@ def test_parking_meets_the_oracle_and_changes_no_bit(case):
     assert torch.equal(on.view(torch.int16), off.view(torch.int16))
 
 
-def test_full_verify_workload_bit_for_bit():
-    """The Llama-shaped verify workload (64 sequences, 4 draft tokens, G = 4):
+@pytest.mark.parametrize("name", ["llama3_8b_verify4", "mixed_70b_verify4"])
+def test_full_verify_workload_bit_for_bit(name):
+    """The verify workloads (4 draft tokens; G = 4: one tile, G = 8: two):
     parking on and off give the same bits, and repeated calls too."""
-    wl = W.make_config_workload("llama3_8b_verify4", device=DEV)
+    wl = W.make_config_workload(name, device=DEV)
     ops.select_result_parking(1)
     first = GS.general_step(wl, append=False).clone()
     again = GS.general_step(wl, append=False).clone()
