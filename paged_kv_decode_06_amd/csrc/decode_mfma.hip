@@ -467,8 +467,12 @@ __host__ __device__ constexpr int wave_rows_bytes(int hg, int D, int wgc, int pa
 }
 
 template <class S, bool GEN>
+// s_qs: the query-row offsets in LDS (q_start[0..B]) when qs_lds, which the
+// generalised runs read there rather than from memory, where the load would
+// wait for the wave's last stores too.
 __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* waves_lds,
-                                            int wave_lds, const int* s_desc, int U) {
+                                            int wave_lds, const int* s_desc, int U,
+                                            const int32_t* s_qs, bool qs_lds) {
   constexpr int D = S::D, UG = S::UG, G = S::G, HG = S::HG;
   constexpr int TPR = D / 4;                    // threads per column (4 dims each)
   // Share slots in axis order: wave w's head share is slot 2w, its end share
@@ -498,7 +502,16 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
     if (seg < 0 || seg == prev) continue;       // no share, or not its run's first
     prev = seg;
     const int b = seg / U, u = seg % U;
-    const int ql = GEN ? seq_queries(p, b) : 1;
+    int ql = 1, r0 = b;   // query count, first q / out row
+    if constexpr (GEN) {
+      if (qs_lds) {
+        r0 = s_qs[b];
+        ql = min(max(s_qs[b + 1] - r0, 0), p.max_q);
+      } else {
+        ql = seq_queries(p, b);
+        r0 = p.q_start != nullptr ? p.q_start[b] : b;
+      }
+    }
     // the run's shares are slots i .. last (consecutive: shares are in axis order)
     int last = i;
 #pragma unroll
@@ -531,7 +544,6 @@ __device__ __forceinline__ void wgc_combine(const AttnParams& p, unsigned char* 
         }
       if (whole) {
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // (0: the query sees no key)
-        const int r0 = GEN && p.q_start != nullptr ? p.q_start[b] : b;
         uint16_t* orow = static_cast<uint16_t*>(p.out) +
                          ((int64_t)(r0 + c / UG) * p.Hq + u * HG * G + c % UG) * D + d4;
         *reinterpret_cast<uint2*>(orow) =
@@ -1181,7 +1193,7 @@ void mfma_partition_kernel(const AttnParams p) {
     if (park_kind != 0) flush_park();
   });
   if constexpr (NCT == 1)
-    if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U);
+    if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U, s_len + p.B, qs_lds);
 }
 
 // Calls f(MfmaShape<D, BS, G, kind, hg>{}) for the combination given at run
