@@ -389,6 +389,17 @@ int pkv_select_share_combine(int mode);
  * mode 0 when the library loads.  PKV_ERR_UNSUPPORTED for another value. */
 int pkv_select_result_parking(int mode);
 
+/* The MFMA partition kernel cuts its work (every (sequence, kv-head unit)
+ * run's pages, in order) into equal pieces, one per wave; a wave pays a fixed
+ * cost for each run it starts (the run's q, page-table and first tile
+ * round trips).  The split therefore counts `slots` extra positions ahead
+ * of each non-empty run, so a piece holding several runs gets fewer pages.
+ * 0..8 (default 2; PKV_RUN_COST in the environment sets it when the library
+ * loads); the split, not the result, changes (floating-point summation
+ * order aside).  Process-wide, read at the start of every attention call.
+ * PKV_ERR_UNSUPPORTED for another value. */
+int pkv_select_run_cost(int slots);
+
 /* Partition-kernel variants.  Both compute the same attention; MFMA (the
  * default) puts the GQA group on the matrix cores, VALU uses fp32 vector
  * FMAs.  The choice is process-wide and is read at the start of every

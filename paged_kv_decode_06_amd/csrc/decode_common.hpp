@@ -74,7 +74,16 @@ __device__ __forceinline__ int seq_pages(const AttnParams& p, int b, int BS) {
   return seq_range(seq_length(p, b, BS), seq_queries(p, b), p.sinks, p.window, BS).n;
 }
 
-// Sequence page counts -> exclusive prefix sums in LDS (s_pre[0..B]); with
+// Slots a (sequence, unit) run of sequence b takes on the work axis: its
+// pages plus p.run_cost slots of no pages ahead of them (none for an empty
+// run), so that the split charges each run the fixed cost of starting it.
+__device__ __forceinline__ int seq_slots(const AttnParams& p, int b, int BS) {
+  const int n = seq_pages(p, b, BS);
+  return n > 0 ? n + p.run_cost : 0;
+}
+
+// Sequence slot counts (seq_slots) -> exclusive prefix sums in LDS
+// (s_pre[0..B]); with
 // keep_len also each sequence's context length as given, in
 // s_tmp[kAttnBlockThreads + b] for b < B, and, where qs_lds_entries(B) is
 // not 0, its first query row (q_start[b], or b without q_start) in
@@ -97,7 +106,7 @@ __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
   for (int b = b0; b < b1; ++b) {
     if (keep_len) s_len[b] = p.context_lens[b];
     if (keep_qs) s_len[B + b] = p.q_start != nullptr ? p.q_start[b] : b;
-    sum += seq_pages(p, b, BS);
+    sum += seq_slots(p, b, BS);
   }
   if (keep_qs && tid == nt - 1) s_len[2 * B] = p.q_start != nullptr ? p.q_start[B] : B;
   int incl = sum;   // inclusive scan of the slice sums within the wave
@@ -112,7 +121,7 @@ __device__ inline void build_prefix(const AttnParams& p, int BS, int32_t* s_pre,
   for (int w = 0; w < tid / kWave; ++w) run += s_tmp[w];
   for (int b = b0; b < b1; ++b) {
     s_pre[b] = run;
-    run += seq_pages(p, b, BS);
+    run += seq_slots(p, b, BS);
   }
   if (tid == nt - 1) s_pre[B] = run;
   __syncthreads();
@@ -186,22 +195,26 @@ __device__ __forceinline__ void run_split(const WorkSplit& s, int wave, Body&& b
   }
 }
 
-// One wave's share of a (sequence, unit) run: pages [j0, j1) of run
-// (b, u), whose first page sits at `run_start` on the work axis.
+// One wave's share of a (sequence, unit) run: pages [j0, j1) of run (b, u)
+// of n_b pages (none when j0 == j1: the piece holds only slots ahead of the
+// pages); `next` is the axis position after the piece's part of the run.
+// The run's slots start at run_start, its pages run_cost slots later.
 struct Piece {
-  int b, u, n_b, run_start, j0, j1;
+  int b, u, n_b, run_start, j0, j1, next;
 };
 
-__device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int U, int x,
-                                              int x_end) {
+__device__ __forceinline__ Piece locate_piece(const int32_t* s_pre, int B, int U, int run_cost,
+                                              int x, int x_end) {
   Piece pc;
   pc.b = find_sequence(s_pre, B, U, x);
-  pc.n_b = s_pre[pc.b + 1] - s_pre[pc.b];
+  const int m = s_pre[pc.b + 1] - s_pre[pc.b];   // slots of each of the sequence's runs
   const int seg_start = U * s_pre[pc.b];
-  pc.u = (x - seg_start) / pc.n_b;
-  pc.run_start = seg_start + pc.u * pc.n_b;
-  pc.j0 = x - pc.run_start;
-  pc.j1 = min(pc.n_b, x_end - pc.run_start);
+  pc.u = (x - seg_start) / m;
+  pc.run_start = seg_start + pc.u * m;
+  pc.n_b = m - run_cost;
+  pc.next = pc.run_start + min(m, x_end - pc.run_start);
+  pc.j0 = max(x - pc.run_start - run_cost, 0);
+  pc.j1 = max(pc.next - pc.run_start - run_cost, 0);
   return pc;
 }
 

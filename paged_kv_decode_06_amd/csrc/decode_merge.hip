@@ -68,8 +68,9 @@ void merge_seg_kernel(const AttnParams p, int G) {
   // kAttnWavesPerBlock pieces, are the share rows' owners)
   const WorkSplit split = make_split(U * pre_B, p.total_waves);
   const int owner = p.wgc ? kAttnWavesPerBlock : 1;
+  // (n_b counts the run's slots: its pages start p.run_cost slots in)
   const int start = U * pre_b + u * n_b;
-  const int k0 = piece_of(split, start) / owner;
+  const int k0 = piece_of(split, start + p.run_cost) / owner;
   const int k1 = piece_of(split, start + n_b - 1) / owner;
   if (k0 == k1) return;                        // finished by the partition kernel
   const int P = k1 - k0 + 1;
@@ -180,8 +181,9 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
   }
   const WorkSplit split = make_split(total, p.total_waves);
   const int owner = p.wgc ? kAttnWavesPerBlock : 1;   // (share rows per workgroup: see above)
+  // (n_b counts the run's slots: its pages start p.run_cost slots in)
   const int start = U * pre_b + u * n_b;
-  const int k0 = piece_of(split, start) / owner;
+  const int k0 = piece_of(split, start + p.run_cost) / owner;
   const int k1 = piece_of(split, start + n_b - 1) / owner;
   if (k0 == k1) return;
   const int seg = b * U + u;

@@ -745,7 +745,7 @@ void mfma_partition_kernel(const AttnParams p) {
     park_kind = 0;
   };
   while (x < x_end) {
-    Piece pc = locate_piece(s_pre, p.B, U, x, x_end);
+    Piece pc = locate_piece(s_pre, p.B, U, p.run_cost, x, x_end);
     // (wave-uniform: kept in scalar registers)
     pc.b = __builtin_amdgcn_readfirstlane(pc.b);
     pc.u = __builtin_amdgcn_readfirstlane(pc.u);
@@ -753,6 +753,11 @@ void mfma_partition_kernel(const AttnParams p) {
     pc.run_start = __builtin_amdgcn_readfirstlane(pc.run_start);
     pc.j0 = __builtin_amdgcn_readfirstlane(pc.j0);
     pc.j1 = __builtin_amdgcn_readfirstlane(pc.j1);
+    pc.next = __builtin_amdgcn_readfirstlane(pc.next);
+    if (pc.j0 == pc.j1) {   // only the slots ahead of the run's pages
+      x = pc.next;
+      continue;
+    }
     const int b = pc.b, g0 = pc.u * HG;   // the unit's first kv head
     int L_in;
     if (len_lds)
@@ -1088,7 +1093,7 @@ void mfma_partition_kernel(const AttnParams p) {
     }
     const int seg = b * U + pc.u;
     // (PARK: the slot is free and more runs of the piece follow)
-    const bool to_park = PARK && p.park && park_kind == 0 && pc.run_start + pc.j1 < x_end;
+    const bool to_park = PARK && p.park && park_kind == 0 && pc.next < x_end;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = 16 * ct + n;
@@ -1184,7 +1189,7 @@ void mfma_partition_kernel(const AttnParams p) {
               make_float2(m_run[ct], l_tot);
       }
     }
-    x = pc.run_start + pc.j1;
+    x = pc.next;
   }
   if (pending) flush_pending();
   if constexpr (DEFER_OUT)

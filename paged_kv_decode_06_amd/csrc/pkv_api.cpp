@@ -148,6 +148,23 @@ int combine_cols(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int 
   return w;
 }
 
+// Slots of no pages ahead of each run on the MFMA kernel's work axis
+// (pkv::AttnParams::run_cost): PKV_RUN_COST when the library loads, else
+// kDefaultRunCost; pkv_select_run_cost changes it.
+constexpr int kDefaultRunCost = 2;
+constexpr int kMaxRunCost = 8;
+std::atomic<int>& run_cost_flag() {
+  static std::atomic<int> flag([] {
+    const char* e = std::getenv("PKV_RUN_COST");
+    if (e && *e) {
+      const int v = std::atoi(e);
+      if (v >= 0 && v <= kMaxRunCost) return v;
+    }
+    return kDefaultRunCost;
+  }());
+  return flag;
+}
+
 // Parking of mid-piece results (pkv::AttnParams::park): on unless
 // PKV_RESULT_PARKING=0 is set when the library loads or
 // pkv_select_result_parking(0) switched it off; see parking.
@@ -318,6 +335,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.total_waves = waves;
   p.wgc = wgc;
   p.park = park;
+  p.run_cost = path == pkv::AttnPath::kMfma ? run_cost_flag().load(std::memory_order_relaxed) : 0;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);
   p.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
@@ -429,6 +447,13 @@ int pkv_select_share_combine(int mode) {
   if (mode != 0 && mode != 1)
     return fail(PKV_ERR_UNSUPPORTED, "share-combine mode %d is not 0 or 1", mode);
   share_combine_flag().store(mode, std::memory_order_relaxed);
+  return PKV_OK;
+}
+
+int pkv_select_run_cost(int slots) {
+  if (slots < 0 || slots > kMaxRunCost)
+    return fail(PKV_ERR_UNSUPPORTED, "run cost %d is not in 0..%d", slots, kMaxRunCost);
+  run_cost_flag().store(slots, std::memory_order_relaxed);
   return PKV_OK;
 }
 

@@ -51,8 +51,12 @@ struct AttnParams {
   // no combine): a run's result that more runs of the piece follow waits in
   // an LDS slot of the wave until the piece's end (mfma_park_slot_bytes).
   int park;
+  // run_cost: slots of no pages the work split puts ahead of each non-empty
+  // (sequence, unit) run, so that pieces holding several runs get fewer
+  // pages (0 for the VALU kernel); the prefix sums in ws_pre count slots.
+  int run_cost;
   // workspace (see workspace_layout)
-  int32_t* ws_pre;      // [B + 1] pages-per-sequence prefix sums
+  int32_t* ws_pre;      // [B + 1] slots-per-sequence prefix sums (see run_cost)
   float* ws_ml;         // [rows, cols, 2] running max (log2 domain) and sum
   float* ws_o;          // [rows, cols, D] unnormalised partial outputs
   // Fused append (the decode step): when k_new is non-NULL, the new token of

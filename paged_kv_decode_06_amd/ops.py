@@ -98,6 +98,8 @@ def _load():
         lib.pkv_select_share_combine.restype = I
         lib.pkv_select_result_parking.argtypes = [I]
         lib.pkv_select_result_parking.restype = I
+        lib.pkv_select_run_cost.argtypes = [I]
+        lib.pkv_select_run_cost.restype = I
         lib.pkv_select_unit_heads.argtypes = [I]
         lib.pkv_select_unit_heads.restype = I
         lib.pkv_select_partition_kernel.argtypes = [I]
@@ -276,6 +278,12 @@ def select_result_parking(mode: int) -> None:
     ends (default), 0 = store it when its run ends (process-wide; same bits
     either way)."""
     _check("pkv_select_result_parking", _load().pkv_select_result_parking(int(mode)))
+
+
+def select_run_cost(slots: int) -> None:
+    """pkv_select_run_cost: positions of no pages the MFMA work split counts
+    ahead of each run (0..8, default 2; process-wide)."""
+    _check("pkv_select_run_cost", _load().pkv_select_run_cost(int(slots)))
 
 
 def decode_unit_heads(B: int, Hq: int, Hkv: int, D: int, BS: int, kv_dtype: int) -> int:

@@ -20,7 +20,8 @@ import torch
 from paged_kv_decode_06_amd import ops
 from paged_kv_decode_06_amd import workloads as W
 from tests import gpu_support as GS
-from tests.test_gpu_parity import DEV, build, check_step, default_kernel, say, use_kernel
+from tests.test_gpu_parity import (DEFAULT_RUN_COST, DEV, build, check_step, default_kernel, say,
+                                   use_kernel)
 
 pytestmark = pytest.mark.gpu
 
@@ -157,7 +158,8 @@ def test_balanced_split(mode, kv):
     kvd = GS.KV_KIND[kv]
     waves = ops.attention_waves(wl.B, 32, 8, 128, 16, kvd)
     U = 8 // ops.decode_unit_heads(wl.B, 32, 8, 128, 16, kvd)
-    total = U * sum(-(-L // 16) for L in lengths)
+    # (the split counts each run's pages plus the run cost's positions)
+    total = U * sum(-(-L // 16) + DEFAULT_RUN_COST for L in lengths if L > 0)
     assert balanced_split(total, waves), (total, waves)
     other = twin(wl)
     check_step(wl, f"balanced split {mode} {kv} combine on")

@@ -42,10 +42,15 @@ def use_kernel(name: str) -> None:
     say(f"partition kernel: {name}")
 
 
+DEFAULT_RUN_COST = 2
+
+
 def default_kernel() -> None:
     ops.select_partition_kernel(ops.PARTITION_MFMA)
     ops.select_unit_heads(ops.UNITS_AUTO)
     ops.select_share_combine(1)
+    ops.select_result_parking(1)
+    ops.select_run_cost(DEFAULT_RUN_COST)
 
 
 @pytest.fixture(params=list(KERNELS))

@@ -10,8 +10,9 @@ adds the other heads' products with P = 0 (exact zeros).  So every share is
 the same bits as with one head per wave whenever both split the work into
 the same page ranges, which holds when every piece is one page (the total
 page count does not exceed either grid's waves); the test checks that
-precondition before comparing.  These comparisons run with the workgroup
-combine of the shares switched off: it groups the pieces of four waves, and
+precondition before comparing (with no run cost in the split, whose
+extra positions would depend on the unit size).  These comparisons run with
+the workgroup combine of the shares switched off: it groups the pieces of four waves, and
 the two unit sizes lay out the work axis differently, so they would group
 different pages (tests/test_gpu_combine.py covers the combine).
 """
@@ -38,9 +39,12 @@ def _restore():
 
 @pytest.fixture
 def no_combine():
+    """Combine off, and no run cost in the split: every page its own piece."""
     ops.select_share_combine(0)
+    ops.select_run_cost(0)
     yield
     ops.select_share_combine(1)
+    default_kernel()
 
 
 def unit_heads(wl: W.Workload) -> int:
