@@ -241,3 +241,19 @@ def test_general_one_query_equals_decode_with_units():
     b = GS.general_step(wl, append=False)
     torch.cuda.synchronize()
     assert torch.equal(bits(a), bits(b))
+
+
+def test_small_windowed_call_takes_one_head():
+    """A windowed call whose window bounds its work to a few pages per wave
+    (here at most 130 per sequence and kv head: 4 x 8 x 130 pages for 3072
+    one-head waves) runs one kv head per wave: the same bits as with one head
+    forced; its workspace query covers that unit size."""
+    from tests.test_gpu_general import build as build_general
+    wl = build_general(4, 32, 8, 128, 16, (20000, 30000, 5000, 9000), (1, 1, 1, 1), seed=3,
+                       sinks=16, window=2048, poison=False)
+    GS.append_in_order(wl)
+    a = GS.general_step(wl, append=False).clone()
+    use_kernel("mfma1")
+    b = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(a), bits(b))
