@@ -93,3 +93,39 @@ def test_parking_keeps_the_workspace():
     ops.select_result_parking(0)
     off = ops.attention_workspace_bytes(64, 32, 8, 128, 16, 256, kv, 4)
     assert on == off
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_parking_with_duplicated_columns(window):
+    """At most 8 columns (one query at G = 4, one kv head per wave) normally
+    take the workgroup combine; with it off the results are parked, in the
+    layout where columns 8..15 repeat columns 0..7: bit for bit the stored
+    results, and within the oracle's bar."""
+    L = rng_lengths(41, 50, 12)
+    wl = build(len(L), 32, 8, 128, 16, L, [1] * len(L), seed=41, poison=False,
+               sinks=4 if window else 0, window=window)
+    ops.select_unit_heads(1)
+    ops.select_share_combine(0)
+    ops.select_result_parking(1)
+    on, _ = check(wl, f"dup parking window {window}")
+    ops.select_result_parking(0)
+    off = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(on.view(torch.int16), off.view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [700, 2500])
+def test_parking_with_two_tiles_in_large_batches(B):
+    """Two column tiles park at any batch size: above 512 sequences the
+    query-row offsets, and above 2048 the lengths, come from memory rather
+    than LDS.  Short sequences (many runs per piece), 4 draft tokens at
+    G = 8: within the oracle's bar and bit for bit the stored results."""
+    rng = np.random.default_rng(B)
+    L = [int(x) for x in rng.integers(1, 60, B)]
+    wl = build(B, 64, 8, 64, 16, L, [min(4, x) for x in L], seed=B, poison=False)
+    ops.select_result_parking(1)
+    on, _ = check(wl, f"B{B} two tiles parking on")
+    ops.select_result_parking(0)
+    off = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(on.view(torch.int16), off.view(torch.int16))
