@@ -156,9 +156,10 @@ constexpr int kMaxRunCost = 8;
 std::atomic<int>& run_cost_flag() {
   static std::atomic<int> flag([] {
     const char* e = std::getenv("PKV_RUN_COST");
-    if (e && *e) {
-      const int v = std::atoi(e);
-      if (v >= 0 && v <= kMaxRunCost) return v;
+    if (e && *e) {   // (a value that is not a whole number in range keeps the default)
+      char* end = nullptr;
+      const long v = std::strtol(e, &end, 10);
+      if (end && *end == '\0' && v >= 0 && v <= kMaxRunCost) return (int)v;
     }
     return kDefaultRunCost;
   }());
