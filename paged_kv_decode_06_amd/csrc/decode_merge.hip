@@ -33,10 +33,17 @@ namespace {
 // workgroup combine they have about 3, and one group, without the meeting in
 // LDS, is faster.
 // The run's prefix sums and split are read once for all its columns.
-template <int D, int NGRP>
-__global__ __launch_bounds__(NGRP * 8 * D / 4 > 16 * D / 4 ? NGRP * 8 * D / 4 : 16 * D / 4)
+// DPT: dims per thread, 4 or 8 (one group only).  With 8, a workgroup has
+// half the threads, so twice as many are resident: calls with two column
+// tiles launch two workgroups per run, and their merge runs in fewer rounds
+// of its two trips to memory.  Each output element takes the same operations
+// in the same order either way.
+template <int D, int NGRP, int DPT = 4>
+__global__ __launch_bounds__(NGRP * 8 * D / DPT > 16 * D / DPT ? NGRP * 8 * D / DPT : 16 * D / DPT)
 void merge_seg_kernel(const AttnParams p, int G) {
-  constexpr int TPR = D / 4;                   // threads per column (4 dims each)
+  static_assert(DPT == 4 || (DPT == 8 && NGRP == 1), "8 dims per thread: one group");
+  constexpr int TPR = D / DPT;                 // threads per column (DPT dims each)
+  constexpr int NV = DPT / 4;                  // float4 vectors per thread
   constexpr int kBatch = 8;
   __shared__ float s_acc[NGRP > 1 ? NGRP : 1][NGRP > 1 ? 8 : 1][NGRP > 1 ? D : 1];
   __shared__ float s_den[NGRP > 1 ? NGRP : 1][NGRP > 1 ? 8 : 1];
@@ -49,7 +56,7 @@ void merge_seg_kernel(const AttnParams p, int G) {
   const int b = seg / U, u = seg % U;
   const int cl = t / TPR;                      // column within the workgroup
   const int n = 16 * blockIdx.y + cl;          // column
-  const int d4 = (t % TPR) * 4;
+  const int d4 = (t % TPR) * DPT;
   const int C = p.cols;
   const int UG = p.hg * G;
   const int qi = n / UG;
@@ -61,7 +68,10 @@ void merge_seg_kernel(const AttnParams p, int G) {
   const int r0 = p.q_start != nullptr ? p.q_start[b] : b;
   uint16_t* op = static_cast<uint16_t*>(p.out) + ((int64_t)(r0 + qi) * p.Hq + h) * D + d4;
   if (n_b == 0) {                              // empty history: defined as 0
-    if (live && grp == 0) *reinterpret_cast<uint2*>(op) = make_uint2(0, 0);
+    if (live && grp == 0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) *reinterpret_cast<uint2*>(op + 4 * v) = make_uint2(0, 0);
+    }
     return;                                    // (the whole workgroup)
   }
   // (pieces, or with the workgroup combine the workgroups' ranges of
@@ -79,20 +89,25 @@ void merge_seg_kernel(const AttnParams p, int G) {
   const float* __restrict__ po = p.ws_o;
 
   float M = -FLT_MAX;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 accv[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) accv[v] = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f;
   for (int i0 = grp; i0 < P; i0 += NGRP * kBatch) {
     float2 mlv[kBatch];
-    float4 o[kBatch];
+    float4 o[kBatch][NV];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k * NGRP;
       mlv[k] = make_float2(-FLT_MAX, 0.0f);
-      o[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) o[k][v] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (live && i < P) {
         const int64_t row = (row0 + i) * C + n;
         mlv[k] = *reinterpret_cast<const float2*>(ml + row * 2);
-        o[k] = *reinterpret_cast<const float4*>(po + row * D + d4);
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          o[k][v] = *reinterpret_cast<const float4*>(po + row * D + d4 + 4 * v);
       }
     }
     float mb = M;
@@ -100,22 +115,29 @@ void merge_seg_kernel(const AttnParams p, int G) {
     for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, mlv[k].x);
     const float a = fast_exp2(M - mb);
     den *= a;
-    acc.x *= a;
-    acc.y *= a;
-    acc.z *= a;
-    acc.w *= a;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      accv[v].x *= a;
+      accv[v].y *= a;
+      accv[v].z *= a;
+      accv[v].w *= a;
+    }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const float w = fast_exp2(mlv[k].x - mb);
       den = fmaf(w, mlv[k].y, den);
-      acc.x = fmaf(w, o[k].x, acc.x);
-      acc.y = fmaf(w, o[k].y, acc.y);
-      acc.z = fmaf(w, o[k].z, acc.z);
-      acc.w = fmaf(w, o[k].w, acc.w);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        accv[v].x = fmaf(w, o[k][v].x, accv[v].x);
+        accv[v].y = fmaf(w, o[k][v].y, accv[v].y);
+        accv[v].z = fmaf(w, o[k][v].z, accv[v].z);
+        accv[v].w = fmaf(w, o[k][v].w, accv[v].w);
+      }
     }
     M = mb;
   }
   if constexpr (NGRP > 1) {   // the groups meet in LDS, each brought to the common max
+    float4& acc = accv[0];     // (4 dims per thread)
     *reinterpret_cast<float4*>(&s_acc[grp][cl][d4]) = acc;
     if (d4 == 0) {
       s_den[grp][cl] = den;
@@ -141,8 +163,11 @@ void merge_seg_kernel(const AttnParams p, int G) {
   }
   if (!live) return;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;   // 0: the query sees no key
-  *reinterpret_cast<uint2*>(op) =
-      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+    *reinterpret_cast<uint2*>(op + 4 * v) =
+        make_uint2(pack_bf16x2(accv[v].x * inv, accv[v].y * inv),
+                   pack_bf16x2(accv[v].z * inv, accv[v].w * inv));
 }
 
 // Merge for few rows with many shares each (long contexts): one workgroup
@@ -290,14 +315,19 @@ hipError_t launch_merge(const AttnParams& p, int D, int G, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.B * (p.Hkv / p.hg)), (unsigned)((p.cols + 15) / 16));
   const int wcols = p.cols < 16 ? p.cols : 16;
   const bool two = wcols <= 8 && p.wgc == 0;
+  const bool wide = p.cols > 16;   // (two workgroups per run: 8 dims per thread)
   if (D == 128) {
     if (two)
       hipLaunchKernelGGL((merge_seg_kernel<128, 2>), grid, dim3(2 * wcols * 32), 0, stream, p, G);
+    else if (wide)
+      hipLaunchKernelGGL((merge_seg_kernel<128, 1, 8>), grid, dim3(wcols * 16), 0, stream, p, G);
     else
       hipLaunchKernelGGL((merge_seg_kernel<128, 1>), grid, dim3(wcols * 32), 0, stream, p, G);
   } else if (D == 64) {
     if (two)
       hipLaunchKernelGGL((merge_seg_kernel<64, 2>), grid, dim3(2 * wcols * 16), 0, stream, p, G);
+    else if (wide)
+      hipLaunchKernelGGL((merge_seg_kernel<64, 1, 8>), grid, dim3(wcols * 8), 0, stream, p, G);
     else
       hipLaunchKernelGGL((merge_seg_kernel<64, 1>), grid, dim3(wcols * 16), 0, stream, p, G);
   } else {
