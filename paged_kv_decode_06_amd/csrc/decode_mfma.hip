@@ -709,8 +709,9 @@ void mfma_partition_kernel(const AttnParams p) {
   auto flush_park = [&]() {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const int c = 16 * ct + n;   // (no duplicated columns with one head in PARK kernels but
-                                   // the one-tile decode-shaped ones, whose used columns are n)
+      // (with the repeated columns of a call of at most 8 columns, the used
+      // columns are still the lanes' n < 8)
+      const int c = 16 * ct + n;
       if (park_kind == 1) {
         if (c < park_ncol) {
           uint16_t* orow = static_cast<uint16_t*>(p.out) +
