@@ -5,7 +5,8 @@ sweep draws combinations of them (batch, query group, kv heads, head dim,
 block size, cache kind, lengths with page-boundary and length-1 cases mixed
 in, and for the generalised call query counts, windows and sinks) so that
 interactions none of them picks are checked too.  Every case is a fixed
-seed: a failure names its case and reproduces.
+seed: a failure names its case and reproduces.  The last two sweeps also set
+the process-wide switches (run cost, parking, combine, unit size) at random.
 """
 from __future__ import annotations
 
@@ -90,3 +91,63 @@ def test_random_general_attention_two_tiles(seed):
         f"window={window} sinks={sinks}")
     wl = build_general(B, Hq, Hkv, D, BS, L, q, kv=kv, seed=seed, sinks=sinks, window=window)
     check_general(wl, f"seed {seed}")
+
+
+def draw_switches(rng) -> str:
+    """The process-wide switches at random: the split's run cost, parking of
+    mid-piece results, the workgroup combine and one kv head per wave."""
+    from paged_kv_decode_06_amd import ops
+    rc = int(rng.choice([0, 2, 5, 8]))
+    park, wgc = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    one = int(rng.random() < 0.3)
+    ops.select_run_cost(rc)
+    ops.select_result_parking(park)
+    ops.select_share_combine(wgc)
+    ops.select_unit_heads(one)
+    return f"run cost {rc}, parking {park}, combine {wgc}, one head {one}"
+
+
+def draw_batch(rng, B, BS):
+    """Now and then a batch of 60..400 short sequences (many runs a piece)."""
+    if rng.random() < 0.3:
+        B = int(rng.integers(60, 400))
+        return B, [int(x) for x in rng.integers(1, 80, B)]
+    return B, draw_lengths(rng, B, BS)
+
+
+@pytest.fixture
+def switches_restored():
+    from tests.test_gpu_parity import default_kernel
+    yield
+    default_kernel()
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_decode_step_with_switches(seed, switches_restored):
+    rng = np.random.default_rng(11000 + seed)
+    B, Hq, Hkv, D, BS, kv = draw_shape(rng)
+    B, L = draw_batch(rng, B, BS)
+    sw = draw_switches(rng)
+    say(f"seed {seed}: B={B} Hq={Hq} Hkv={Hkv} D={D} BS={BS} {kv}; {sw}")
+    wl = build(B, Hq, Hkv, D, BS, L, kv=kv, seed=seed)
+    check_step(wl, f"seed {seed}; {sw}")
+    wl = build(B, Hq, Hkv, D, BS, L, kv=kv, seed=seed)
+    assert_same_as_two_calls(wl, f"seed {seed}; {sw}")
+
+
+@pytest.mark.parametrize("seed", range(80))
+def test_random_general_attention_with_switches(seed, switches_restored):
+    rng = np.random.default_rng(13000 + seed)
+    B, Hq, Hkv, D, BS, kv = draw_shape(rng)
+    G = Hq // Hkv
+    qmax = (32 if rng.random() < 0.4 else 16) // G
+    B, L0 = draw_batch(rng, B, BS)
+    q = [int(rng.integers(1, qmax + 1)) for _ in range(B)]
+    L = [max(l, qq) for l, qq in zip(L0, q)]
+    window = int(rng.choice([0, 0, int(rng.integers(1, 600))]))
+    sinks = int(rng.integers(0, 40)) if window > 0 and rng.random() < 0.6 else 0
+    sw = draw_switches(rng)
+    say(f"seed {seed}: B={B} Hq={Hq} Hkv={Hkv} D={D} BS={BS} {kv} q<={qmax} "
+        f"window={window} sinks={sinks}; {sw}")
+    wl = build_general(B, Hq, Hkv, D, BS, L, q, kv=kv, seed=seed, sinks=sinks, window=window)
+    check_general(wl, f"seed {seed}; {sw}")
