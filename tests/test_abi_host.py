@@ -155,3 +155,21 @@ def test_validate_inputs_host_checks(lib):
     assert f(P, P, P, P, P, P, P, 0.125, P, 2, 8, 2, 64, 16, 4, 4, 0, P, 0, P) == -1   # NULL q
     assert f(P, P, P, P, P, P, P, 0.125, P, 2, 8, 2, 96, 16, 4, 4, 0, P, 0, P) == -3   # D = 96
     assert lib.pkv_status_string(-7).decode() == "device-resident input breaks the contract"
+
+
+def test_process_wide_switches_check_their_argument(lib):
+    """The pkv_select_* switches accept their documented values only
+    (PKV_ERR_UNSUPPORTED otherwise; no GPU needed)."""
+    unsupported = -3   # PKV_ERR_UNSUPPORTED
+    assert lib.pkv_select_run_cost(9) == unsupported
+    assert lib.pkv_select_run_cost(-1) == unsupported
+    for v in (0, 8, 2):
+        assert lib.pkv_select_run_cost(v) == 0
+    for f in (lib.pkv_select_result_parking, lib.pkv_select_share_combine,
+              lib.pkv_select_unit_heads):
+        assert f(2) == unsupported and f(-1) == unsupported
+        assert f(0) == 0
+    assert lib.pkv_select_result_parking(1) == 0
+    assert lib.pkv_select_share_combine(1) == 0
+    assert lib.pkv_select_unit_heads(0) == 0
+    assert lib.pkv_select_run_cost(2) == 0
