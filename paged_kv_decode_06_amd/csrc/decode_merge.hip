@@ -76,10 +76,10 @@ void merge_seg_kernel(const AttnParams p, int G) {
     }
     return;                                    // (the whole workgroup)
   }
-  // (pieces, or with the workgroup combine the workgroups' ranges of
-  // kAttnWavesPerBlock pieces, are the share rows' owners)
+  // (pieces, or with the workgroup or chain combine the workgroups' ranges
+  // of kAttnWavesPerBlock pieces, are the share rows' owners)
   const WorkSplit split = make_split(U * pre_B, p.total_waves);
-  const int owner = p.wgc ? kAttnWavesPerBlock : 1;
+  const int owner = p.wgc || p.chain ? kAttnWavesPerBlock : 1;
   // (n_b counts the run's slots: its pages start p.run_cost slots in)
   const int start = U * pre_b + u * n_b;
   const int k0 = piece_of(split, start + p.run_cost) / owner;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kAttnBlockThreads) void merge_wide_kernel(const Att
     return;
   }
   const WorkSplit split = make_split(total, p.total_waves);
-  const int owner = p.wgc ? kAttnWavesPerBlock : 1;   // (share rows per workgroup: see above)
+  const int owner = p.wgc || p.chain ? kAttnWavesPerBlock : 1;   // (share rows per workgroup: see above)
   // (n_b counts the run's slots: its pages start p.run_cost slots in)
   const int start = U * pre_b + u * n_b;
   const int k0 = piece_of(split, start + p.run_cost) / owner;

@@ -629,9 +629,10 @@ void mfma_partition_kernel(const AttnParams p) {
   unsigned char* tile = smem + pre_bytes + (size_t)wave_in_block * wave_lds;
   unsigned char* new_rows = tile + 16 * PITCH;     // [K unit row | V unit row], 16 CH bytes each
   float* head_slot = reinterpret_cast<float*>(new_rows + 32 * CH);
-  // workgroup combine: (segment, flags) of each wave's head and end shares
+  // workgroup combine: (segment, flags) of each wave's head and end shares;
+  // with p.chain, entries 0 and 1 describe the share in the parking slot
   int* s_desc = reinterpret_cast<int*>(smem + pre_bytes + (size_t)kAttnWavesPerBlock * wave_lds);
-  if (p.wgc && lane < 4) s_desc[4 * wave_in_block + lane] = -1;
+  if ((p.wgc || p.chain) && lane < 4) s_desc[4 * wave_in_block + lane] = -1;
 
   const int n = lane & 15;        // column of S^T and O^T (a query head); K row of the A operand
   const int r = lane >> 4;        // 4-token group of S^T rows; 4-dim group of O^T rows
@@ -651,6 +652,32 @@ void mfma_partition_kernel(const AttnParams p) {
   const unsigned char* __restrict__ kc = static_cast<const unsigned char*>(p.k_cache);
   const unsigned char* __restrict__ vc = static_cast<const unsigned char*>(p.v_cache);
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(p.q);
+
+  // O^T, the running max and this lane's share of the sum of the current
+  // run (kept after the piece for the chain combine below)
+  float4_t O[NCT][NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
+  float m_run[NCT];       // running max of column n (exp2 domain)
+  float l_run[NCT];       // this lane's share of column n's sum
+  // parking slot offsets: output [ct][nb][lane] uint2; share (last tile)
+  // [nb][lane] float4, then (m, l) of its 16 columns
+  auto park_out_at = [&](int ct, int nb) { return 8 * (kWave * (NBN * ct + nb) + lane); };
+  auto park_o_at = [&](int nb) { return 16 * (kWave * nb + lane); };
+  const int park_ml_at = 16 * kWave * NBN;
+  // Chain combine (p.chain: one kv head and one column tile per wave).  A
+  // wave whose last run goes on past its piece keeps that share in O (the
+  // walker: its run started in the piece, or it is the workgroup's first
+  // wave); a later wave of the workgroup whose piece starts inside a run
+  // puts its share of it in its parking slot instead of memory.  After the
+  // workgroup's barrier each walker folds in the slots that follow it in
+  // wave order, up to the one ending the run or the workgroup's last wave,
+  // and writes the run's bf16 output (it saw the whole run) or one share
+  // row, g + segment for workgroup g, as the workgroup combine does.
+  constexpr bool CHAIN = GEN && HG == 1 && NCT == 1;
+  int ch_seg = -1;                 // the walker's run (wave-uniform; -1: none)
+  bool ch_first = false;           // its share starts at the run's first page
+  int ch_r0 = 0, ch_g0 = 0, ch_ncol = 0;
+  float ch_l = 0.0f;               // column n's sum over the walker's share
+  const int64_t row_owner = p.chain ? (int64_t)blockIdx.x : 0;   // (+ piece below)
 
   run_split(split, wave, [&](int x, const int x_end, const int piece) {
   // The append's cache stores wait for the end of the piece: a store counts
@@ -698,14 +725,10 @@ void mfma_partition_kernel(const AttnParams p) {
   unsigned char* const park_slot = new_rows;    // (see park_slot_bytes)
   float4_t park_o0[PARK_REG ? NBN : 1];
   float park_m0 = 0.0f, park_l0 = 0.0f;
-  int park_kind = 0;           // 0: empty, 1: output, 2: share (wave-uniform)
+  // (wave-uniform) 0: empty, 1: output, 2: share, 3: share for a walker
+  int park_kind = 0;
   int64_t park_row = 0;        // share row, or the output's first query row
   int park_g0 = 0, park_ncol = 0;
-  // slot offsets: output [ct][nb][lane] uint2; share (last tile) [nb][lane]
-  // float4, then (m, l) of its 16 columns
-  auto park_out_at = [&](int ct, int nb) { return 8 * (kWave * (NBN * ct + nb) + lane); };
-  auto park_o_at = [&](int nb) { return 16 * (kWave * nb + lane); };
-  const int park_ml_at = 16 * kWave * NBN;
   auto flush_park = [&]() {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -844,9 +867,6 @@ void mfma_partition_kernel(const AttnParams p) {
     int64_t new_row = 0, new_sslot = 0;
     bool new_opens = false, parked = false;
 
-    float4_t O[NCT][NBN];   // O^T: lane (n, r) holds dims 16 nb + 4 r + i of column n
-    float m_run[NCT];       // running max of column n (exp2 domain)
-    float l_run[NCT];       // this lane's share of column n's sum
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -1155,6 +1175,31 @@ void mfma_partition_kernel(const AttnParams p) {
           s_desc[4 * wave_in_block + 2 * is_end] = seg;
           s_desc[4 * wave_in_block + 2 * is_end + 1] = (pc.j0 == 0) | (pc.j1 == pc.n_b) << 1;
         }
+      } else if (CHAIN && p.chain && pc.j0 > 0 && wave_in_block > 0) {
+        // a run an earlier wave of the workgroup carries (the piece's first
+        // run, so the slot is free): its share waits in the slot for that
+        // wave, and nothing of it is stored here
+#pragma unroll
+        for (int nb = 0; nb < NBN; ++nb)
+          *reinterpret_cast<float4*>(park_slot + park_o_at(nb)) =
+              make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+        if (lane < 16)
+          *reinterpret_cast<float2*>(park_slot + park_ml_at + 8 * lane) =
+              make_float2(m_run[ct], l_tot);
+        park_kind = 3;
+        if (lane == 0) {
+          s_desc[4 * wave_in_block] = seg;
+          s_desc[4 * wave_in_block + 1] = (pc.j1 == pc.n_b) << 1;
+        }
+      } else if (CHAIN && p.chain && pc.next == x_end && pc.j1 < pc.n_b) {
+        // the run goes on past the piece: this wave walks it (O and m_run
+        // are left as they are; the piece has no more runs)
+        ch_seg = seg;
+        ch_first = pc.j0 == 0;
+        ch_l = l_tot;
+        ch_r0 = r0;
+        ch_g0 = g0;
+        ch_ncol = ncol;
       } else if (to_park) {
         if (PARK_REG && ct == 0) {
 #pragma unroll
@@ -1172,10 +1217,10 @@ void mfma_partition_kernel(const AttnParams p) {
                 make_float2(m_run[ct], l_tot);
         }
         park_kind = 2;
-        park_row = (int64_t)piece + seg;
+        park_row = (p.chain ? row_owner : (int64_t)piece) + seg;
         park_ncol = ncol;
       } else {
-        const int64_t row = (int64_t)piece + seg;
+        const int64_t row = (p.chain ? row_owner : (int64_t)piece) + seg;
         const int C = p.cols;
         if (c < ncol) {
           float* orow = p.ws_o + (row * C + c) * D + 4 * r;
@@ -1196,10 +1241,68 @@ void mfma_partition_kernel(const AttnParams p) {
   if constexpr (DEFER_OUT)
     if (out_pending) flush_out();
   if constexpr (PARK)
-    if (park_kind != 0) flush_park();
+    if (park_kind == 1 || park_kind == 2) flush_park();   // (3: a walker's)
   });
   if constexpr (NCT == 1)
     if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U, s_len + p.B, qs_lds);
+  if constexpr (CHAIN) {
+    if (p.chain) {
+      __syncthreads();   // every wave's slot share and descriptor are in place
+      if (ch_seg >= 0) {
+        // fold in the later waves' shares of the run, in wave order, by the
+        // log-sum-exp rule (column n's max and sum are the same in every
+        // row group of lanes)
+        float M = m_run[0], Ls = ch_l;
+        bool ends = false;
+        for (int j = wave_in_block + 1; j < kAttnWavesPerBlock; ++j) {
+          if (__builtin_amdgcn_readfirstlane(s_desc[4 * j]) != ch_seg) break;
+          const int flg = __builtin_amdgcn_readfirstlane(s_desc[4 * j + 1]);
+          const unsigned char* sl = smem + pre_bytes + (size_t)j * wave_lds + 16 * PITCH;
+          const float2 ml = *reinterpret_cast<const float2*>(sl + park_ml_at + 8 * n);
+          const float Mn = fmaxf(M, ml.x);
+          const float a = fast_exp2(M - Mn), w = fast_exp2(ml.x - Mn);
+          Ls = fmaf(ml.y, w, Ls * a);
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb) {
+            const float4 o = *reinterpret_cast<const float4*>(sl + park_o_at(nb));
+            O[0][nb][0] = fmaf(o.x, w, O[0][nb][0] * a);
+            O[0][nb][1] = fmaf(o.y, w, O[0][nb][1] * a);
+            O[0][nb][2] = fmaf(o.z, w, O[0][nb][2] * a);
+            O[0][nb][3] = fmaf(o.w, w, O[0][nb][3] * a);
+          }
+          M = Mn;
+          if (flg & 2) {
+            ends = true;
+            break;
+          }
+        }
+        if (ch_first && ends) {   // the whole run: bf16 output
+          if (n < ch_ncol) {
+            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;   // (0: the query sees no key)
+            uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                             ((int64_t)(ch_r0 + n / UG) * p.Hq + ch_g0 * G + n % UG) * D + 4 * r;
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb)
+              *reinterpret_cast<uint2*>(orow + 16 * nb) =
+                  make_uint2(pack_bf16x2(O[0][nb][0] * inv, O[0][nb][1] * inv),
+                             pack_bf16x2(O[0][nb][2] * inv, O[0][nb][3] * inv));
+          }
+        } else {                  // the workgroup's share row of the run
+          const int64_t row = row_owner + ch_seg;
+          const int C = p.cols;
+          if (n < ch_ncol) {
+            float* orow = p.ws_o + (row * C + n) * D + 4 * r;
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb)
+              *reinterpret_cast<float4*>(orow + 16 * nb) =
+                  make_float4(O[0][nb][0], O[0][nb][1], O[0][nb][2], O[0][nb][3]);
+          }
+          if (lane < ch_ncol)   // (lanes 0..15: column lane, row group 0)
+            *reinterpret_cast<float2*>(p.ws_ml + (row * C + lane) * 2) = make_float2(M, Ls);
+        }
+      }
+    }
+  }
 }
 
 // Calls f(MfmaShape<D, BS, G, kind, hg>{}) for the combination given at run
@@ -1253,7 +1356,7 @@ bool mfma_tile_holds_share(int D, int hg, int wgc) {
 
 size_t mfma_stage_lds_bytes(int D, int hg, int wgc, int park) {
   return (size_t)kAttnWavesPerBlock * (16 * (hg * 2 * D + 32) + wave_rows_bytes(hg, D, wgc, park)) +
-         (wgc ? 4 * kAttnWavesPerBlock * sizeof(int) : 0);
+         (wgc || park ? 4 * kAttnWavesPerBlock * sizeof(int) : 0);
 }
 
 int mfma_park_slot_bytes(int D) { return park_slot_bytes(D); }
@@ -1323,7 +1426,8 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
       (cols > 16 && (!gen || p.hg != 1)) ||
       (p.wgc && (cols > p.wgc || (p.wgc != 8 && p.wgc != 16) || kPiecesPerWave != 1 ||
                  !mfma_tile_holds_share(D, p.hg, p.wgc))) ||
-      (p.park && (!gen || p.hg != 1 || p.wgc)))
+      (p.park && (!gen || p.hg != 1 || p.wgc)) ||
+      (p.chain && (!p.park || cols <= 8 || cols > 16 || kPiecesPerWave != 1)))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

@@ -116,9 +116,11 @@ std::atomic<int>& unit_heads_flag() {
   return flag;
 }
 
-// Workgroup combine of the partition kernel's shares (pkv::AttnParams::wgc):
-// on unless PKV_SHARE_COMBINE=0 is set when the library loads or
-// pkv_select_share_combine(0) switched it off; see combine_cols.
+// Workgroup combine of the partition kernel's shares (pkv::AttnParams::wgc,
+// and the chain of parked shares, pkv::AttnParams::chain): on unless
+// PKV_SHARE_COMBINE=0 is set when the library loads or
+// pkv_select_share_combine(0) switched it off; see combine_cols and
+// share_chain.
 std::atomic<int>& share_combine_flag() {
   static std::atomic<int> flag([] {
     const char* e = std::getenv("PKV_SHARE_COMBINE");
@@ -200,6 +202,18 @@ int parking(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, i
   const int t = col_tiles(cols);
   const int with = blocks_per_cu(dev, path, D, BS, G, kind, B, 1, t, 0, 1);
   return with > 0 && with == blocks_per_cu(dev, path, D, BS, G, kind, B, 1, t, 0, 0) ? 1 : 0;
+}
+
+// Whether a parking call combines a run's shares across the edges between
+// the waves of a workgroup (pkv::AttnParams::chain): with one column tile
+// of more than 8 columns (8 or fewer take the workgroup combine, whose
+// slots hold both of a wave's shares), under the share-combine switch.
+// It keeps the grid and needs fewer share rows than the workspace holds.
+int share_chain(int park, int cols) {
+  return park && cols > 8 && cols <= kTileCols && pkv::kPiecesPerWave == 1 &&
+                 share_combine_flag().load(std::memory_order_relaxed)
+             ? 1
+             : 0;
 }
 
 // Windowed calls whose work is this small (at most this many pages per
@@ -361,6 +375,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.total_waves = waves;
   p.wgc = wgc;
   p.park = park;
+  p.chain = share_chain(park, cols);
   p.run_cost = path == pkv::AttnPath::kMfma ? run_cost_flag().load(std::memory_order_relaxed) : 0;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);

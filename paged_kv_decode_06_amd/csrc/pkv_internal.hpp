@@ -51,6 +51,13 @@ struct AttnParams {
   // no combine): a run's result that more runs of the piece follow waits in
   // an LDS slot of the wave until the piece's end (mfma_park_slot_bytes).
   int park;
+  // chain (with park, 9 to 16 columns): the shares of a run that crosses
+  // the edge between consecutive waves of a workgroup are combined by the
+  // first of them after the workgroup's barrier (the later ones leave theirs
+  // in their parking slots), so that, as with wgc, a run leaves at most one
+  // share row per workgroup (row g + segment) and one finished inside the
+  // workgroup's range is written as bf16 output there.
+  int chain;
   // run_cost: slots of no pages the work split puts ahead of each non-empty
   // (sequence, unit) run, so that pieces holding several runs get fewer
   // pages (0 for the VALU kernel); the prefix sums in ws_pre count slots.

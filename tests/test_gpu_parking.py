@@ -3,8 +3,10 @@
 Calls whose partition waves serve one kv head, without the workgroup combine
 (e.g. 4 draft tokens at G = 4 or G = 8), keep the result of a run that a wave
 finishes before its last one in LDS (with two 16-column tiles, a share's
-first tile in registers) and store it after the wave's last tile.  Checked through the C ABI: against the fp64 oracle, and bit for
-bit the same output as storing every result when its run ends
+first tile in registers) and store it after the wave's last tile.  Checked
+through the C ABI: against the fp64 oracle, and, with the share combine off
+(so that no shares are chained through the slots: see test_gpu_chain), bit
+for bit the same output as storing every result when its run ends
 (pkv_select_result_parking(0)), on batches whose pieces hold complete short
 runs (parked bf16 outputs), runs split across pieces (parked shares) and
 several runs per piece (the slot is taken; later results are stored at
@@ -62,6 +64,7 @@ def test_parking_meets_the_oracle_and_changes_no_bit(case):
     q_lens = [min(ql, x) for x in L]
     wl = build(len(L), Hq, Hkv, D, BS, L, q_lens, kv=kv, seed=seed, poison=False, sinks=S,
                window=Wn)
+    ops.select_share_combine(0)
     ops.select_result_parking(1)
     on, _ = check(wl, f"{case} parking on")
     ops.select_result_parking(0)
@@ -72,9 +75,11 @@ def test_parking_meets_the_oracle_and_changes_no_bit(case):
 
 @pytest.mark.parametrize("name", ["llama3_8b_verify4", "mixed_70b_verify4"])
 def test_full_verify_workload_bit_for_bit(name):
-    """The verify workloads (4 draft tokens; G = 4: one tile, G = 8: two):
-    parking on and off give the same bits, and repeated calls too."""
+    """The verify workloads (4 draft tokens; G = 4: one tile, G = 8: two),
+    share combine off: parking on and off give the same bits, and repeated
+    calls too."""
     wl = W.make_config_workload(name, device=DEV)
+    ops.select_share_combine(0)
     ops.select_result_parking(1)
     first = GS.general_step(wl, append=False).clone()
     again = GS.general_step(wl, append=False).clone()
@@ -123,6 +128,7 @@ def test_parking_with_two_tiles_in_large_batches(B):
     rng = np.random.default_rng(B)
     L = [int(x) for x in rng.integers(1, 60, B)]
     wl = build(B, 64, 8, 64, 16, L, [min(4, x) for x in L], seed=B, poison=False)
+    ops.select_share_combine(0)
     ops.select_result_parking(1)
     on, _ = check(wl, f"B{B} two tiles parking on")
     ops.select_result_parking(0)
