@@ -369,11 +369,12 @@ int pkv_select_unit_heads(int mode);
  * partial rows have at most 8 columns, i.e. kv heads per wave x G x queries
  * per sequence <= 8, or at most 16 with two kv heads per wave where the
  * larger LDS keeps the grid's size).  Generalised calls with one kv head
- * per wave and 9 to 16 columns, which park mid-piece results (see
- * pkv_select_result_parking), combine instead the shares of a run that
- * crosses the edge between consecutive waves of a workgroup, in the first
- * of those waves after the workgroup's barrier, with the same one row per
- * workgroup.  Mode 0: one partial row per wave always.  The result
+ * per wave and 9 to 32 columns, which park mid-piece results (see
+ * pkv_select_result_parking; with more than 16 columns only where room for
+ * a second share per wave leaves the grid's size), combine instead the
+ * shares of a run that crosses the edge between consecutive waves of a
+ * workgroup, in the first of those waves after the workgroup's barrier,
+ * with the same one row per workgroup.  Mode 0: one partial row per wave always.  The result
  * differs only in floating-point summation order.  Process-wide, read at
  * the start of every attention call and workspace query, like
  * pkv_select_unit_heads.  PKV_SHARE_COMBINE=0 in the environment selects

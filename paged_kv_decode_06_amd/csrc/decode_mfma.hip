@@ -459,10 +459,21 @@ __host__ __device__ constexpr int wgc_slot_bytes(int D, int wcols) {
 // rows (unused by the generalised instantiations) and extends past them.
 __host__ __device__ constexpr int park_slot_bytes(int D) { return wgc_slot_bytes(D, 16); }
 
+// Park mode 2 (the chain combine with two column tiles): the parking slot
+// moves back so that the wave's first park_slot_bytes(D), from its tile
+// buffer on, hold a second 16-column share once the piece's tiles are done;
+// this is how far it moves past the tile buffer.
+__host__ __device__ constexpr int park_share_ext_bytes(int hg, int D) {
+  return park_slot_bytes(D) > 16 * (hg * 2 * D + 32) ? park_slot_bytes(D) - 16 * (hg * 2 * D + 32)
+                                                     : 0;
+}
+
 // Bytes a wave keeps after its staged tile: the append rows (or the parking
-// slot over them) and the combine's head slot.
+// slot over them, in park mode 2 after the extension) and the combine's
+// head slot.
 __host__ __device__ constexpr int wave_rows_bytes(int hg, int D, int wgc, int park) {
-  return (park && park_slot_bytes(D) > 4 * hg * D ? park_slot_bytes(D) : 4 * hg * D) +
+  return (park == 2 ? park_share_ext_bytes(hg, D) : 0) +
+         (park && park_slot_bytes(D) > 4 * hg * D ? park_slot_bytes(D) : 4 * hg * D) +
          wgc_slot_bytes(D, wgc);
 }
 
@@ -672,11 +683,16 @@ void mfma_partition_kernel(const AttnParams p) {
   // wave order, up to the one ending the run or the workgroup's last wave,
   // and writes the run's bf16 output (it saw the whole run) or one share
   // row, g + segment for workgroup g, as the workgroup combine does.
-  constexpr bool CHAIN = GEN && HG == 1 && NCT == 1;
+  // With two column tiles (park mode 2) a follower's share takes both its
+  // slot (tile 1) and the share-sized area from its tile buffer on (tile 0,
+  // written there once its piece's tiles are done).
+  constexpr bool CHAIN = GEN && HG == 1;
   int ch_seg = -1;                 // the walker's run (wave-uniform; -1: none)
   bool ch_first = false;           // its share starts at the run's first page
   int ch_r0 = 0, ch_g0 = 0, ch_ncol = 0;
-  float ch_l = 0.0f;               // column n's sum over the walker's share
+  float ch_l[NCT];                 // column c's sum over the walker's share
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) ch_l[ct] = 0.0f;
   const int64_t row_owner = p.chain ? (int64_t)blockIdx.x : 0;   // (+ piece below)
 
   run_split(split, wave, [&](int x, const int x_end, const int piece) {
@@ -722,8 +738,11 @@ void mfma_partition_kernel(const AttnParams p) {
   // of its 70B-shaped mix).  Only scalars describe the parked result.
   constexpr bool PARK = GEN && HG == 1;
   constexpr bool PARK_REG = PARK && NCT == 2;   // (the share's tile 0 in registers)
-  unsigned char* const park_slot = new_rows;    // (see park_slot_bytes)
+  // (see park_slot_bytes; park mode 2: see park_share_ext_bytes)
+  unsigned char* const park_slot =
+      new_rows + (PARK_REG && p.park == 2 ? park_share_ext_bytes(HG, D) : 0);
   float4_t park_o0[PARK_REG ? NBN : 1];
+  bool h0_regs = false;        // a walker's share waits with its tile 0 in park_o0
   float park_m0 = 0.0f, park_l0 = 0.0f;
   // (wave-uniform) 0: empty, 1: output, 2: share, 3: share for a walker
   int park_kind = 0;
@@ -1178,14 +1197,24 @@ void mfma_partition_kernel(const AttnParams p) {
       } else if (CHAIN && p.chain && pc.j0 > 0 && wave_in_block > 0) {
         // a run an earlier wave of the workgroup carries (the piece's first
         // run, so the slot is free): its share waits in the slot for that
-        // wave, and nothing of it is stored here
+        // wave, and nothing of it is stored here.  With two tiles, tile 0
+        // goes to the area from the tile buffer on, which is free only
+        // after the piece's last tile: until then it waits in park_o0.
+        if (PARK_REG && ct == 0 && pc.next < x_end) {
 #pragma unroll
-        for (int nb = 0; nb < NBN; ++nb)
-          *reinterpret_cast<float4*>(park_slot + park_o_at(nb)) =
-              make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
-        if (lane < 16)
-          *reinterpret_cast<float2*>(park_slot + park_ml_at + 8 * lane) =
-              make_float2(m_run[ct], l_tot);
+          for (int nb = 0; nb < NBN; ++nb) park_o0[nb] = O[ct][nb];
+          park_m0 = m_run[ct];
+          park_l0 = l_tot;
+          h0_regs = true;
+        } else {
+          unsigned char* const dst = PARK_REG && ct == 0 ? tile : park_slot;
+#pragma unroll
+          for (int nb = 0; nb < NBN; ++nb)
+            *reinterpret_cast<float4*>(dst + park_o_at(nb)) =
+                make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+          if (lane < 16)
+            *reinterpret_cast<float2*>(dst + park_ml_at + 8 * lane) = make_float2(m_run[ct], l_tot);
+        }
         park_kind = 3;
         if (lane == 0) {
           s_desc[4 * wave_in_block] = seg;
@@ -1196,7 +1225,7 @@ void mfma_partition_kernel(const AttnParams p) {
         // are left as they are; the piece has no more runs)
         ch_seg = seg;
         ch_first = pc.j0 == 0;
-        ch_l = l_tot;
+        ch_l[ct] = l_tot;
         ch_r0 = r0;
         ch_g0 = g0;
         ch_ncol = ncol;
@@ -1242,6 +1271,16 @@ void mfma_partition_kernel(const AttnParams p) {
     if (out_pending) flush_out();
   if constexpr (PARK)
     if (park_kind == 1 || park_kind == 2) flush_park();   // (3: a walker's)
+  if constexpr (PARK_REG) {
+    if (h0_regs) {   // (wave-uniform; the tile buffer is free now)
+#pragma unroll
+      for (int nb = 0; nb < NBN; ++nb)
+        *reinterpret_cast<float4*>(tile + park_o_at(nb)) =
+            make_float4(park_o0[nb][0], park_o0[nb][1], park_o0[nb][2], park_o0[nb][3]);
+      if (lane < 16)
+        *reinterpret_cast<float2*>(tile + park_ml_at + 8 * lane) = make_float2(park_m0, park_l0);
+    }
+  }
   });
   if constexpr (NCT == 1)
     if (p.wgc) wgc_combine<S, GEN>(p, smem + pre_bytes, wave_lds, s_desc, U, s_len + p.B, qs_lds);
@@ -1250,55 +1289,72 @@ void mfma_partition_kernel(const AttnParams p) {
       __syncthreads();   // every wave's slot share and descriptor are in place
       if (ch_seg >= 0) {
         // fold in the later waves' shares of the run, in wave order, by the
-        // log-sum-exp rule (column n's max and sum are the same in every
+        // log-sum-exp rule (column c's max and sum are the same in every
         // row group of lanes)
-        float M = m_run[0], Ls = ch_l;
+        float M[NCT], Ls[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          M[ct] = m_run[ct];
+          Ls[ct] = ch_l[ct];
+        }
         bool ends = false;
         for (int j = wave_in_block + 1; j < kAttnWavesPerBlock; ++j) {
           if (__builtin_amdgcn_readfirstlane(s_desc[4 * j]) != ch_seg) break;
           const int flg = __builtin_amdgcn_readfirstlane(s_desc[4 * j + 1]);
-          const unsigned char* sl = smem + pre_bytes + (size_t)j * wave_lds + 16 * PITCH;
-          const float2 ml = *reinterpret_cast<const float2*>(sl + park_ml_at + 8 * n);
-          const float Mn = fmaxf(M, ml.x);
-          const float a = fast_exp2(M - Mn), w = fast_exp2(ml.x - Mn);
-          Ls = fmaf(ml.y, w, Ls * a);
+          const unsigned char* wb = smem + pre_bytes + (size_t)j * wave_lds;   // wave j's tile buffer
+          const unsigned char* slot_j =
+              wb + 16 * PITCH + (NCT == 2 && p.park == 2 ? park_share_ext_bytes(HG, D) : 0);
 #pragma unroll
-          for (int nb = 0; nb < NBN; ++nb) {
-            const float4 o = *reinterpret_cast<const float4*>(sl + park_o_at(nb));
-            O[0][nb][0] = fmaf(o.x, w, O[0][nb][0] * a);
-            O[0][nb][1] = fmaf(o.y, w, O[0][nb][1] * a);
-            O[0][nb][2] = fmaf(o.z, w, O[0][nb][2] * a);
-            O[0][nb][3] = fmaf(o.w, w, O[0][nb][3] * a);
+          for (int ct = 0; ct < NCT; ++ct) {
+            const unsigned char* sl = NCT == 2 && ct == 0 ? wb : slot_j;   // (tile 0: see h0_regs)
+            const float2 ml = *reinterpret_cast<const float2*>(sl + park_ml_at + 8 * n);
+            const float Mn = fmaxf(M[ct], ml.x);
+            const float a = fast_exp2(M[ct] - Mn), w = fast_exp2(ml.x - Mn);
+            Ls[ct] = fmaf(ml.y, w, Ls[ct] * a);
+#pragma unroll
+            for (int nb = 0; nb < NBN; ++nb) {
+              const float4 o = *reinterpret_cast<const float4*>(sl + park_o_at(nb));
+              O[ct][nb][0] = fmaf(o.x, w, O[ct][nb][0] * a);
+              O[ct][nb][1] = fmaf(o.y, w, O[ct][nb][1] * a);
+              O[ct][nb][2] = fmaf(o.z, w, O[ct][nb][2] * a);
+              O[ct][nb][3] = fmaf(o.w, w, O[ct][nb][3] * a);
+            }
+            M[ct] = Mn;
           }
-          M = Mn;
           if (flg & 2) {
             ends = true;
             break;
           }
         }
-        if (ch_first && ends) {   // the whole run: bf16 output
-          if (n < ch_ncol) {
-            const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;   // (0: the query sees no key)
-            uint16_t* orow = static_cast<uint16_t*>(p.out) +
-                             ((int64_t)(ch_r0 + n / UG) * p.Hq + ch_g0 * G + n % UG) * D + 4 * r;
+        const bool whole = ch_first && ends;   // (else the workgroup's share row)
+        const int64_t row = row_owner + ch_seg;
+        const int C = p.cols;
 #pragma unroll
-            for (int nb = 0; nb < NBN; ++nb)
-              *reinterpret_cast<uint2*>(orow + 16 * nb) =
-                  make_uint2(pack_bf16x2(O[0][nb][0] * inv, O[0][nb][1] * inv),
-                             pack_bf16x2(O[0][nb][2] * inv, O[0][nb][3] * inv));
-          }
-        } else {                  // the workgroup's share row of the run
-          const int64_t row = row_owner + ch_seg;
-          const int C = p.cols;
-          if (n < ch_ncol) {
-            float* orow = p.ws_o + (row * C + n) * D + 4 * r;
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int c = 16 * ct + n;
+          if (whole) {
+            if (c < ch_ncol) {
+              const float inv = Ls[ct] > 0.0f ? 1.0f / Ls[ct] : 0.0f;   // (0: the query sees no key)
+              uint16_t* orow = static_cast<uint16_t*>(p.out) +
+                               ((int64_t)(ch_r0 + c / UG) * p.Hq + ch_g0 * G + c % UG) * D + 4 * r;
 #pragma unroll
-            for (int nb = 0; nb < NBN; ++nb)
-              *reinterpret_cast<float4*>(orow + 16 * nb) =
-                  make_float4(O[0][nb][0], O[0][nb][1], O[0][nb][2], O[0][nb][3]);
+              for (int nb = 0; nb < NBN; ++nb)
+                *reinterpret_cast<uint2*>(orow + 16 * nb) =
+                    make_uint2(pack_bf16x2(O[ct][nb][0] * inv, O[ct][nb][1] * inv),
+                               pack_bf16x2(O[ct][nb][2] * inv, O[ct][nb][3] * inv));
+            }
+          } else {
+            if (c < ch_ncol) {
+              float* orow = p.ws_o + (row * C + c) * D + 4 * r;
+#pragma unroll
+              for (int nb = 0; nb < NBN; ++nb)
+                *reinterpret_cast<float4*>(orow + 16 * nb) =
+                    make_float4(O[ct][nb][0], O[ct][nb][1], O[ct][nb][2], O[ct][nb][3]);
+            }
+            // (lanes 0..15: column 16 ct + lane, row group 0)
+            if (lane < 16 && c < ch_ncol)
+              *reinterpret_cast<float2*>(p.ws_ml + (row * C + c) * 2) = make_float2(M[ct], Ls[ct]);
           }
-          if (lane < ch_ncol)   // (lanes 0..15: column lane, row group 0)
-            *reinterpret_cast<float2*>(p.ws_ml + (row * C + lane) * 2) = make_float2(M, Ls);
         }
       }
     }
@@ -1427,7 +1483,8 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
       (p.wgc && (cols > p.wgc || (p.wgc != 8 && p.wgc != 16) || kPiecesPerWave != 1 ||
                  !mfma_tile_holds_share(D, p.hg, p.wgc))) ||
       (p.park && (!gen || p.hg != 1 || p.wgc)) ||
-      (p.chain && (!p.park || cols <= 8 || cols > 16 || kPiecesPerWave != 1)))
+      (p.park == 2 && (cols <= 16 || !p.chain)) || p.park < 0 || p.park > 2 ||
+      (p.chain && (!p.park || cols <= 8 || (cols > 16) != (p.park == 2) || kPiecesPerWave != 1)))
     return hipErrorInvalidValue;
   const bool ok = dispatch_mfma(D, BS, G, kind, p.hg, [&](auto s) {
     using S = decltype(s);

@@ -66,7 +66,7 @@ int cu_count(int dev) {
 int blocks_per_cu(int dev, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg,
                   int col_tiles = 1, int wgc = 0, int park = 0) {
   const int Bq = ((B + 63) / 64) * 64;
-  const unsigned long long key = ((unsigned long long)(park != 0) << 58) |
+  const unsigned long long key = ((unsigned long long)park << 58) |
                                  ((unsigned long long)(wgc / 8) << 56) |
                                  ((unsigned long long)col_tiles << 52) |
                                  ((unsigned long long)dev << 44) | ((unsigned long long)hg << 40) |
@@ -205,15 +205,24 @@ int parking(pkv::AttnPath path, int D, int BS, int G, int kind, int B, int hg, i
 }
 
 // Whether a parking call combines a run's shares across the edges between
-// the waves of a workgroup (pkv::AttnParams::chain): with one column tile
-// of more than 8 columns (8 or fewer take the workgroup combine, whose
-// slots hold both of a wave's shares), under the share-combine switch.
-// It keeps the grid and needs fewer share rows than the workspace holds.
-int share_chain(int park, int cols) {
-  return park && cols > 8 && cols <= kTileCols && pkv::kPiecesPerWave == 1 &&
-                 share_combine_flag().load(std::memory_order_relaxed)
-             ? 1
-             : 0;
+// the waves of a workgroup (pkv::AttnParams::chain): with more than 8
+// columns (8 or fewer take the workgroup combine, whose slots hold both of
+// a wave's shares), under the share-combine switch.  Two column tiles need
+// park mode 2 (room for a second share from the tile buffer on), taken only
+// when it leaves the workgroups per CU unchanged; `park` is raised to 2
+// then.  It keeps the grid and needs fewer share rows than the workspace
+// holds.
+int share_chain(int& park, pkv::AttnPath path, int D, int BS, int G, int kind, int B, int cols) {
+  if (!park || cols <= 8 || cols > kMaxCols || pkv::kPiecesPerWave != 1 ||
+      !share_combine_flag().load(std::memory_order_relaxed))
+    return 0;
+  if (cols <= kTileCols) return 1;
+  int dev;
+  if (current_device(&dev) != 0) return 0;
+  const int with = blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 2, 0, 2);
+  if (with <= 0 || with != blocks_per_cu(dev, path, D, BS, G, kind, B, 1, 2, 0, 0)) return 0;
+  park = 2;
+  return 1;
 }
 
 // Windowed calls whose work is this small (at most this many pages per
@@ -340,7 +349,8 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   const int cols = hg * G * opts.max_q;
   const int wgc = combine_cols(path, D, BS, G, kv_dtype, B, hg, cols);
   // (parking keeps the grid: the workspace queries need not know of it)
-  const int park = parking(path, D, BS, G, kv_dtype, B, hg, cols, wgc, gen);
+  int park = parking(path, D, BS, G, kv_dtype, B, hg, cols, wgc, gen);
+  const int chain = share_chain(park, path, D, BS, G, kv_dtype, B, cols);
   const int blocks = attention_blocks(path, D, BS, G, kv_dtype, B, hg, col_tiles(cols), wgc);
   if (blocks <= 0) return fail(PKV_ERR_HIP, "could not size the grid on the current device");
   const int waves = blocks * pkv::kAttnWavesPerBlock;
@@ -375,7 +385,7 @@ int prepare_attention(const void* q, const void* k_cache, const void* v_cache,
   p.total_waves = waves;
   p.wgc = wgc;
   p.park = park;
-  p.chain = share_chain(park, cols);
+  p.chain = chain;
   p.run_cost = path == pkv::AttnPath::kMfma ? run_cost_flag().load(std::memory_order_relaxed) : 0;
   char* ws = static_cast<char*>(workspace);
   p.ws_pre = reinterpret_cast<int32_t*>(ws + lay.pre_off);

@@ -47,11 +47,13 @@ struct AttnParams {
   // Its value is the column capacity of a wave's share slots (8 or 16;
   // 0: no combine).
   int wgc;
-  // park (generalised calls with one kv head and one column tile per wave,
-  // no combine): a run's result that more runs of the piece follow waits in
-  // an LDS slot of the wave until the piece's end (mfma_park_slot_bytes).
+  // park (generalised calls with one kv head per wave, no combine): a run's
+  // result that more runs of the piece follow waits in an LDS slot of the
+  // wave until the piece's end (mfma_park_slot_bytes).  2: the same, with
+  // the slot moved back so that a second share fits from the tile buffer on
+  // (the chain combine with two column tiles).
   int park;
-  // chain (with park, 9 to 16 columns): the shares of a run that crosses
+  // chain (with park, more than 8 columns): the shares of a run that crosses
   // the edge between consecutive waves of a workgroup are combined by the
   // first of them after the workgroup's barrier (the later ones leave theirs
   // in their parking slots), so that, as with wgc, a run leaves at most one
@@ -165,7 +167,7 @@ hipError_t launch_partition_mfma(const AttnParams& p, int D, int BS, int G, int 
 // above 1 that exists); with col_tiles = 2, that of the generalised
 // instantiation with two 16-column tiles (hg = 1 only).
 // wgc: with the LDS of the workgroup combine for shares of wgc columns;
-// park: with the parking slot (AttnParams::park).
+// park: with the parking slot (AttnParams::park: 0, 1 or 2).
 int mfma_blocks_per_cu(int D, int BS, int G, int kind, int B, int hg, int col_tiles = 1,
                        int wgc = 0, int park = 0);
 int mfma_unit_heads(int G);

@@ -1,11 +1,12 @@
 """The chain combine of parked shares in the generalised partition kernel (GPU).
 
-Generalised calls whose waves serve one kv head and 9 to 16 columns (e.g. 4
-draft tokens at G = 4) park mid-piece results in LDS.  With the share
-combine on (the default), a run that crosses the edge between consecutive
-waves of a workgroup is combined after the workgroup's barrier by the first
-of those waves: the later ones leave their shares in their parking slots,
-and the run leaves one share row per workgroup, or its bf16 output when the
+Generalised calls whose waves serve one kv head and 9 to 32 columns (e.g. 4
+draft tokens at G = 4 or G = 8) park mid-piece results in LDS.  With the
+share combine on (the default), a run that crosses the edge between
+consecutive waves of a workgroup is combined after the workgroup's barrier
+by the first of those waves: the later ones leave their shares in their
+parking slots (with two column tiles, tile 0 from the tile buffer on), and
+the run leaves one share row per workgroup, or its bf16 output when the
 workgroup saw all of it.  Checked through the C ABI: against the fp64
 oracle with the chain on and off, outputs within two bf16 steps of each
 other (only the summation order differs) and not all equal (the chain was
@@ -67,7 +68,12 @@ CASES = [
     (4, 40, 16, 32, 8, 128, 32, 4, "fp8", 0, 0),
     (5, 40, 16, 32, 8, 128, 32, 3, "int8", 2, 300),   # 12 columns, window with sinks
     (6, 20, 12, 32, 8, 128, 16, 4, "bf16", 16, 1000),
-    (7, 10, 30, 16, 4, 128, 16, 5, "bf16", 0, 0),     # G = 4, 5 queries (20 > 16: no chain)
+    # two 16-column tiles
+    (7, 10, 30, 16, 4, 128, 16, 5, "bf16", 0, 0),     # G = 4, 5 queries: 20 columns
+    (8, 60, 10, 64, 8, 128, 16, 4, "bf16", 0, 0),     # G = 8, 4 queries: 32 columns
+    (9, 40, 10, 32, 8, 128, 16, 6, "bf16", 2, 300),   # 24 columns, window with sinks
+    (10, 40, 12, 64, 8, 128, 32, 4, "fp8", 0, 0),
+    (11, 30, 10, 64, 8, 64, 16, 3, "int8", 0, 0),     # D = 64, 24 columns
 ]
 
 
@@ -85,10 +91,7 @@ def test_chain_on_and_off_meet_the_oracle_and_agree(case):
     ops.select_share_combine(0)
     off = GS.general_step(wl, append=False)
     torch.cuda.synchronize()
-    if (Hq // Hkv) * ql <= 16:
-        assert_order_only(on, off, str(case))
-    else:   # two column tiles take no chain: the same kernel either way
-        assert torch.equal(bits(on), bits(off))
+    assert_order_only(on, off, str(case))
 
 
 @pytest.mark.parametrize("cost", [0, 8])
@@ -146,18 +149,36 @@ def test_chain_keeps_the_workspace():
     assert on == off
 
 
-def test_verify_workload_chain_on_and_off():
-    """The Llama-shaped verify workload (64 sequences of 512 .. 4096 tokens,
-    4 draft tokens, G = 4): every output within the oracle's bar (also
-    covered by the full-configuration test) and within two bf16 steps of
-    the unchained outputs; repeated calls bit for bit."""
-    wl = W.make_config_workload("llama3_8b_verify4", device=DEV)
+@pytest.mark.parametrize("name", ["llama3_8b_verify4", "mixed_70b_verify4"])
+def test_verify_workload_chain_on_and_off(name):
+    """The verify workloads (4 draft tokens; the Llama shape at G = 4, one
+    column tile; the 70B-shaped mix at G = 8, two): every output within the
+    oracle's bar (covered by the full-configuration test) and within two
+    bf16 steps of the unchained outputs; repeated calls bit for bit."""
+    wl = W.make_config_workload(name, device=DEV)
     first = GS.general_step(wl, append=False).clone()
     again = GS.general_step(wl, append=False).clone()
     ops.select_share_combine(0)
     off = GS.general_step(wl, append=False)
     torch.cuda.synchronize()
     assert torch.equal(bits(first), bits(again))
-    assert_order_only(first, off, "llama3_8b_verify4")
-    say("verify: outputs that differ from the unchained call",
+    assert_order_only(first, off, name)
+    say(f"{name}: outputs that differ from the unchained call",
         int((bits(first) != bits(off)).sum()), "of", first.numel())
+
+
+def test_two_tile_chain_in_large_batches():
+    """Two column tiles (G = 8, 4 queries) at B = 700 and D = 64, where park
+    mode 2 still leaves two workgroups per CU: query-row offsets from
+    memory, many runs per piece, a few runs over many pieces."""
+    rng = np.random.default_rng(70)
+    B = 700
+    L = [int(x) for x in rng.integers(1, 120, B)]
+    for i in rng.choice(B, 6, replace=False):
+        L[i] = int(rng.integers(3000, 8000))
+    wl = build(B, 64, 8, 64, 16, L, [min(4, x) for x in L], seed=70, poison=False)
+    on, _ = check(wl, "B700 two tiles chain on")
+    ops.select_share_combine(0)
+    off = GS.general_step(wl, append=False)
+    torch.cuda.synchronize()
+    assert_order_only(on, off, "B700 two tiles")
