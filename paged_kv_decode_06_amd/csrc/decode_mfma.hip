@@ -674,7 +674,7 @@ void mfma_partition_kernel(const AttnParams p) {
   auto park_out_at = [&](int ct, int nb) { return 8 * (kWave * (NBN * ct + nb) + lane); };
   auto park_o_at = [&](int nb) { return 16 * (kWave * nb + lane); };
   const int park_ml_at = 16 * kWave * NBN;
-  // Chain combine (p.chain: one kv head and one column tile per wave).  A
+  // Chain combine (p.chain: generalised calls, one kv head per wave).  A
   // wave whose last run goes on past its piece keeps that share in O (the
   // walker: its run started in the piece, or it is the workgroup's first
   // wave); a later wave of the workgroup whose piece starts inside a run
@@ -693,7 +693,9 @@ void mfma_partition_kernel(const AttnParams p) {
   float ch_l[NCT];                 // column c's sum over the walker's share
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) ch_l[ct] = 0.0f;
-  const int64_t row_owner = p.chain ? (int64_t)blockIdx.x : 0;   // (+ piece below)
+  // with the chain, workgroup g stores its share rows at g + segment
+  // (without it, a piece's rows are at piece + segment)
+  const int64_t row_owner = p.chain ? (int64_t)blockIdx.x : 0;
 
   run_split(split, wave, [&](int x, const int x_end, const int piece) {
   // The append's cache stores wait for the end of the piece: a store counts
