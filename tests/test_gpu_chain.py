@@ -144,9 +144,11 @@ def test_chain_keeps_the_workspace():
     per-piece rows the workspace holds: the query is the same either way."""
     kv = ops.KV_BF16
     on = ops.attention_workspace_bytes(64, 32, 8, 128, 16, 256, kv, 4)
+    on2 = ops.attention_workspace_bytes(256, 64, 8, 128, 16, 1024, kv, 4)   # two tiles
     ops.select_share_combine(0)
     off = ops.attention_workspace_bytes(64, 32, 8, 128, 16, 256, kv, 4)
-    assert on == off
+    off2 = ops.attention_workspace_bytes(256, 64, 8, 128, 16, 1024, kv, 4)
+    assert on == off and on2 == off2
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_verify4", "mixed_70b_verify4"])
